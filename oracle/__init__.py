@@ -1,0 +1,218 @@
+"""ctypes binding of the fp64 CPU oracle (oracle/fvo.cpp).
+
+TEST INFRASTRUCTURE ONLY: imported by the test suite, the smoke check and the
+benchmark's CPU-baseline leg.  The product package never imports it.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "fvo.cpp")
+_LIB = os.path.join(_HERE, "libfvo.so")
+
+FLAG_E1 = 1          # top-p threshold within 1e-5 of a cumulative-mass step that changes the count
+FLAG_E2 = 2          # near-tie (not exact) between the last kept and first dropped block score
+FLAG_NONFINITE = 4   # row had a non-finite score; repaired to all blocks
+
+
+def build(force: bool = False) -> str:
+    """Compile libfvo.so with g++ (C++17, plain -O2, std::thread)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["g++", "-O2", "-std=c++17", "-fPIC", "-shared", "-pthread", _SRC, "-o", tmp])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+_P = ctypes.c_void_p
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        lib.fvo_num_blocks.restype = ctypes.c_int
+        lib.fvo_num_blocks.argtypes = [_P]
+        lib.fvo_block_table.restype = ctypes.c_int
+        lib.fvo_block_table.argtypes = [_P, _P]
+        lib.fvo_token_block.restype = ctypes.c_int
+        lib.fvo_token_block.argtypes = [_P, _P]
+        lib.fvo_pool.restype = ctypes.c_int
+        lib.fvo_pool.argtypes = [_P, ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int, _P, _P, ctypes.c_int]
+        lib.fvo_scores.restype = ctypes.c_int
+        lib.fvo_scores.argtypes = [_P, _P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _P, ctypes.c_int]
+        lib.fvo_route_scores.restype = ctypes.c_int
+        lib.fvo_route_scores.argtypes = [_P, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_int,
+                                         ctypes.c_double, _P, _P, _P, _P, ctypes.c_int]
+        lib.fvo_route.restype = ctypes.c_int
+        lib.fvo_route.argtypes = [_P, _P, ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int, _P,
+                                  ctypes.c_float, ctypes.c_int, ctypes.c_double, _P, _P, _P, _P, ctypes.c_int]
+        lib.fvo_attn.restype = ctypes.c_int
+        lib.fvo_attn.argtypes = [_P, _P, _P, ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int, _P, _P,
+                                 ctypes.c_double, _P, ctypes.c_int64, _P, ctypes.c_int]
+        lib.fvo_real_pairs.restype = ctypes.c_int64
+        lib.fvo_real_pairs.argtypes = [_P, _P, ctypes.c_int64]
+        lib.fvo_hardware_threads.restype = ctypes.c_int
+        lib.fvo_hardware_threads.argtypes = []
+        _lib = lib
+    return _lib
+
+
+def _threads(n):
+    if n:
+        return n
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _grid6(grid, block):
+    return np.ascontiguousarray(list(grid) + list(block), dtype=np.int32)
+
+
+def _c(x, dtype):
+    a = np.ascontiguousarray(x, dtype=dtype)
+    return a
+
+
+def hardware_threads() -> int:
+    return _load().fvo_hardware_threads()
+
+
+def num_blocks(grid, block) -> int:
+    g = _grid6(grid, block)
+    return _load().fvo_num_blocks(g.ctypes.data)
+
+
+def block_table(grid, block) -> np.ndarray:
+    """[N, 7] int32: t0, y0, x0, et, eh, ew, real count."""
+    g = _grid6(grid, block)
+    n = num_blocks(grid, block)
+    out = np.empty((n, 7), dtype=np.int32)
+    _load().fvo_block_table(g.ctypes.data, out.ctypes.data)
+    return out
+
+
+def token_block(grid, block) -> np.ndarray:
+    g = _grid6(grid, block)
+    T, H, W = grid
+    out = np.full(T * H * W, -1, dtype=np.int32)
+    _load().fvo_token_block(g.ctypes.data, out.ctypes.data)
+    return out
+
+
+def pool(x: np.ndarray, grid, block, nthreads=None) -> np.ndarray:
+    """x bf16 bits [B, L, heads, D] -> fp64 block means [B, heads, N, D]."""
+    x = _c(x, np.uint16)
+    B, L, heads, D = x.shape
+    g = _grid6(grid, block)
+    N = num_blocks(grid, block)
+    out = np.empty((B, heads, N, D), dtype=np.float64)
+    rc = _load().fvo_pool(x.ctypes.data, B, L, heads, D, g.ctypes.data, out.ctypes.data, _threads(nthreads))
+    if rc < 0:
+        raise ValueError("fvo_pool failed (%d)" % rc)
+    return out
+
+
+def scores(qbar: np.ndarray, kbar: np.ndarray, nthreads=None) -> np.ndarray:
+    qbar = _c(qbar, np.float64)
+    kbar = _c(kbar, np.float64)
+    B, heads, N, D = qbar.shape
+    out = np.empty((B, heads, N, N), dtype=np.float64)
+    _load().fvo_scores(qbar.ctypes.data, kbar.ctypes.data, B, heads, N, D, out.ctypes.data, _threads(nthreads))
+    return out
+
+
+MARGIN = 1e-5   # ambiguity margin on the cumulative-mass threshold and on score gaps at the cut
+
+
+def route_scores(s: np.ndarray, top_p: float, k_floor: int, nthreads=None, margin: float = MARGIN):
+    """Rows of scores [..., N] -> (mask [..., ceil(N/32)] u32, cnt [...] i32, flags [...] u8, status)."""
+    s = _c(s, np.float64)
+    N = s.shape[-1]
+    lead = s.shape[:-1]
+    R = int(np.prod(lead)) if lead else 1
+    words = (N + 31) // 32
+    mask = np.zeros(lead + (words,), dtype=np.uint32)
+    cnt = np.zeros(lead, dtype=np.int32)
+    flags = np.zeros(lead, dtype=np.uint8)
+    status = np.zeros(1, dtype=np.uint32)
+    rc = _load().fvo_route_scores(s.ctypes.data, R, N, float(top_p), int(k_floor), float(margin), mask.ctypes.data,
+                                  cnt.ctypes.data, flags.ctypes.data, status.ctypes.data, _threads(nthreads))
+    if rc < 0:
+        raise ValueError("fvo_route_scores rejected its arguments")
+    return mask, cnt, flags, int(status[0])
+
+
+def route(q: np.ndarray, k: np.ndarray, grid, block, top_p: float, k_floor: int, nthreads=None,
+          margin: float = MARGIN):
+    """bf16 Q, K [B, L, heads, D] -> (mask [B, heads, N, W] u32, cnt [B, heads, N], flags, status)."""
+    q = _c(q, np.uint16)
+    k = _c(k, np.uint16)
+    B, L, heads, D = q.shape
+    g = _grid6(grid, block)
+    N = num_blocks(grid, block)
+    words = (N + 31) // 32
+    mask = np.zeros((B, heads, N, words), dtype=np.uint32)
+    cnt = np.zeros((B, heads, N), dtype=np.int32)
+    flags = np.zeros((B, heads, N), dtype=np.uint8)
+    status = np.zeros(1, dtype=np.uint32)
+    rc = _load().fvo_route(q.ctypes.data, k.ctypes.data, B, L, heads, D, g.ctypes.data, float(top_p),
+                           int(k_floor), float(margin), mask.ctypes.data, cnt.ctypes.data, flags.ctypes.data,
+                           status.ctypes.data, _threads(nthreads))
+    if rc < 0:
+        raise ValueError("fvo_route rejected its arguments (%d)" % rc)
+    return mask, cnt, flags, int(status[0])
+
+
+def attn(q, k, v, grid, block, mask, scale, items=None, nthreads=None, out=None) -> np.ndarray:
+    """Block-sparse attention in fp64 -> [B, L, heads, D] (NaN where not computed).
+
+    items: optional 1-D array of item ids (b*heads + h)*N + i."""
+    q = _c(q, np.uint16)
+    k = _c(k, np.uint16)
+    v = _c(v, np.uint16)
+    mask = _c(mask, np.uint32)
+    B, L, heads, D = q.shape
+    g = _grid6(grid, block)
+    if out is None:
+        out = np.full((B, L, heads, D), np.nan, dtype=np.float64)
+    if items is None:
+        ip, n = None, 0
+    else:
+        items = _c(items, np.int64)
+        ip, n = items.ctypes.data, items.size
+    rc = _load().fvo_attn(q.ctypes.data, k.ctypes.data, v.ctypes.data, B, L, heads, D, g.ctypes.data,
+                          mask.ctypes.data, float(scale), ip, n, out.ctypes.data, _threads(nthreads))
+    if rc < 0:
+        raise ValueError("fvo_attn rejected its arguments (%d)" % rc)
+    return out
+
+
+def real_pairs(grid, block, mask) -> int:
+    """Real (query, key) token pairs the mask asks for; attention FLOPs = 4*D*pairs."""
+    mask = _c(mask, np.uint32)
+    N = num_blocks(grid, block)
+    rows = mask.size // (((N + 31) // 32) * N)
+    g = _grid6(grid, block)
+    return int(_load().fvo_real_pairs(g.ctypes.data, mask.ctypes.data, rows))
+
+
+def dense_mask(B, heads, N) -> np.ndarray:
+    words = (N + 31) // 32
+    m = np.zeros((B, heads, N, words), dtype=np.uint32)
+    for j in range(N):
+        m[..., j >> 5] |= np.uint32(1 << (j & 31))
+    return m
+
+
+def mask_to_bool(mask: np.ndarray, N: int) -> np.ndarray:
+    """u32 words [..., W] -> bool [..., N]."""
+    bits = (mask[..., :, None] >> np.arange(32, dtype=np.uint32)) & 1
+    return bits.reshape(mask.shape[:-1] + (-1,))[..., :N].astype(bool)
