@@ -1,0 +1,215 @@
+"""Routed block-sparse attention for video DiTs on MI355X -- Python binding.
+
+Thin ctypes marshalling over libfva.so (include/fva.h).  Every step of the
+path runs in the library's HIP kernels; torch provides device memory and the
+current stream only.  There is no CPU or eager fallback: if the library is not
+built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfva.so")
+
+FVA_OK = 0
+STATUS_NAMES = ["FVA_OK", "FVA_ERR_INVALID_ARG", "FVA_ERR_SHAPE", "FVA_ERR_TOPK", "FVA_ERR_SCALE",
+                "FVA_ERR_WORKSPACE", "FVA_ERR_UNSUPPORTED", "FVA_ERR_DEVICE"]
+SCHED_LPT = 0
+SCHED_NAIVE = 1
+
+# every symbol include/fva.h declares
+EXPORTS = ["fva_num_blocks", "fva_route_workspace_bytes", "fva_attn_workspace_bytes", "fva_attn_workgroups",
+           "fva_route", "fva_sparse_attn", "fva_dense_attn_ref", "fva_trace_imbalance", "fva_last_error",
+           "fva_status_name"]
+
+
+class FvaError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        self.name = STATUS_NAMES[status] if 0 <= status < len(STATUS_NAMES) else str(status)
+        super().__init__("%s: %s" % (self.name, detail))
+
+
+class Grid(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("W", ctypes.c_int32),
+                ("bt", ctypes.c_int32), ("bh", ctypes.c_int32), ("bw", ctypes.c_int32)]
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("L", ctypes.c_int32), ("heads", ctypes.c_int32), ("D", ctypes.c_int32)]
+
+
+class RouteCfg(ctypes.Structure):
+    _fields_ = [("top_p", ctypes.c_float), ("k_floor", ctypes.c_int32)]
+
+
+_lib = None
+_P = ctypes.c_void_p
+
+
+def load():
+    """Load libfva.so (built in-tree by __graft_entry__.build() or build.py)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libfva.so is not built: run `python adaptive_block_sparse_tile_amd/build.py`")
+    lib = ctypes.CDLL(LIB_PATH)
+    G, D, C = ctypes.POINTER(Grid), ctypes.POINTER(Desc), ctypes.POINTER(RouteCfg)
+    lib.fva_num_blocks.restype = ctypes.c_int32
+    lib.fva_num_blocks.argtypes = [G]
+    lib.fva_route_workspace_bytes.restype = ctypes.c_size_t
+    lib.fva_route_workspace_bytes.argtypes = [D, G]
+    lib.fva_attn_workspace_bytes.restype = ctypes.c_size_t
+    lib.fva_attn_workspace_bytes.argtypes = [D, G]
+    lib.fva_attn_workgroups.restype = ctypes.c_int32
+    lib.fva_attn_workgroups.argtypes = [D, G]
+    lib.fva_route.restype = ctypes.c_int
+    lib.fva_route.argtypes = [_P, _P, D, G, C, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.fva_sparse_attn.restype = ctypes.c_int
+    lib.fva_sparse_attn.argtypes = [_P, _P, _P, _P, D, G, _P, ctypes.c_float, ctypes.c_int32, _P, _P,
+                                    ctypes.c_size_t, _P]
+    lib.fva_dense_attn_ref.restype = ctypes.c_int
+    lib.fva_dense_attn_ref.argtypes = [_P, _P, _P, _P, D, ctypes.c_float, _P]
+    lib.fva_trace_imbalance.restype = ctypes.c_int
+    lib.fva_trace_imbalance.argtypes = [_P, ctypes.c_int32, ctypes.POINTER(ctypes.c_double),
+                                        ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32)]
+    lib.fva_last_error.restype = ctypes.c_char_p
+    lib.fva_last_error.argtypes = []
+    lib.fva_status_name.restype = ctypes.c_char_p
+    lib.fva_status_name.argtypes = [ctypes.c_int32]
+    _lib = lib
+    return lib
+
+
+def _check(rc: int):
+    if rc != FVA_OK:
+        raise FvaError(rc, load().fva_last_error().decode())
+
+
+def make_grid(grid, block) -> Grid:
+    return Grid(*[int(x) for x in tuple(grid) + tuple(block)])
+
+
+def make_desc(B, L, heads, D) -> Desc:
+    return Desc(int(B), int(L), int(heads), int(D))
+
+
+def num_blocks(grid, block) -> int:
+    return load().fva_num_blocks(ctypes.byref(make_grid(grid, block)))
+
+
+def route_workspace_bytes(shape, grid, block) -> int:
+    return load().fva_route_workspace_bytes(ctypes.byref(make_desc(*shape)), ctypes.byref(make_grid(grid, block)))
+
+
+def attn_workspace_bytes(shape, grid, block) -> int:
+    return load().fva_attn_workspace_bytes(ctypes.byref(make_desc(*shape)), ctypes.byref(make_grid(grid, block)))
+
+
+def attn_workgroups(shape, grid, block) -> int:
+    n = load().fva_attn_workgroups(ctypes.byref(make_desc(*shape)), ctypes.byref(make_grid(grid, block)))
+    if n < 0:
+        raise FvaError(1, "fva_attn_workgroups failed")
+    return n
+
+
+# ----------------------------------------------------------------------- torch-facing calls
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_ptr(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check_qkv(*ts):
+    torch = _torch()
+    shape = ts[0].shape
+    for t in ts:
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous() or t.dim() != 4 or t.shape != shape:
+            raise ValueError("q, k, v must be contiguous bf16 device tensors of one shape [B, L, heads, D]")
+    return tuple(int(x) for x in shape)
+
+
+def workspace(nbytes: int, device):
+    """Caller-owned device workspace (256-byte aligned by the torch allocator)."""
+    torch = _torch()
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def route(q, k, grid, block, top_p: float, k_floor: int, ws=None, out=None, stream=None):
+    """Block router on the GPU -> (mask u32 [B, heads, N, W] as int32 bits, kv_cnt int32 [B, heads, N],
+    status int32 [1])."""
+    torch = _torch()
+    shape = _check_qkv(q, k)
+    B, L, heads, D = shape
+    N = num_blocks(grid, block)
+    words = (N + 31) // 32
+    if out is None:
+        mask = torch.empty((B, heads, N, words), dtype=torch.int32, device=q.device)
+        cnt = torch.empty((B, heads, N), dtype=torch.int32, device=q.device)
+        status = torch.empty((1,), dtype=torch.int32, device=q.device)
+    else:
+        mask, cnt, status = out
+    need = route_workspace_bytes(shape, grid, block)
+    if ws is None:
+        ws = workspace(need, q.device)
+    _check(load().fva_route(q.data_ptr(), k.data_ptr(), ctypes.byref(make_desc(*shape)),
+                            ctypes.byref(make_grid(grid, block)), ctypes.byref(RouteCfg(float(top_p), int(k_floor))),
+                            mask.data_ptr(), cnt.data_ptr(), status.data_ptr(), ws.data_ptr(), ws.numel(),
+                            _stream_ptr(stream)))
+    return mask, cnt, status
+
+
+def sparse_attn(q, k, v, grid, block, mask, scale=None, sched: str = "lpt", trace=None, ws=None, out=None,
+                stream=None):
+    """Block-sparse attention on the GPU -> O bf16 [B, L, heads, D].
+
+    trace: optional uint64-sized device tensor (int64) of attn_workgroups()*4 entries."""
+    torch = _torch()
+    shape = _check_qkv(q, k, v)
+    B, L, heads, D = shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = torch.empty_like(q) if out is None else out
+    need = attn_workspace_bytes(shape, grid, block)
+    if ws is None:
+        ws = workspace(need, q.device)
+    sch = {"lpt": SCHED_LPT, "naive": SCHED_NAIVE}[sched]
+    tp = trace.data_ptr() if trace is not None else None
+    _check(load().fva_sparse_attn(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                  ctypes.byref(make_desc(*shape)), ctypes.byref(make_grid(grid, block)),
+                                  mask.data_ptr(), float(scale), sch, tp, ws.data_ptr(), ws.numel(),
+                                  _stream_ptr(stream)))
+    return o
+
+
+def dense_attn_ref(q, k, v, scale=None, out=None, stream=None):
+    """Dense attention over all tokens on the GPU (same core and numerics)."""
+    torch = _torch()
+    shape = _check_qkv(q, k, v)
+    D = shape[3]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = torch.empty_like(q) if out is None else out
+    _check(load().fva_dense_attn_ref(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                     ctypes.byref(make_desc(*shape)), float(scale), _stream_ptr(stream)))
+    return o
+
+
+def trace_imbalance(trace_host: np.ndarray):
+    """(busy max/mean, finish max/mean, CUs used) from a host copy of the trace."""
+    t = np.ascontiguousarray(trace_host).view(np.uint64).reshape(-1)
+    n_wg = t.size // 4
+    b, f, n = ctypes.c_double(), ctypes.c_double(), ctypes.c_int32()
+    _check(load().fva_trace_imbalance(t.ctypes.data, n_wg, ctypes.byref(b), ctypes.byref(f), ctypes.byref(n)))
+    return b.value, f.value, n.value

@@ -1,0 +1,293 @@
+// fva_api.cpp -- the C ABI of libfva: host-side validation, workspace layout
+// and kernel launches.  Every check runs before anything is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "../../include/fva.h"
+#include "fva_kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+fva_status fail(fva_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+fva_status ok() {
+  g_last_error.clear();
+  return FVA_OK;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool make_geo(const fva_grid* g, fva::Geo* out) {
+  if (!g || g->T < 1 || g->H < 1 || g->W < 1 || g->bt < 1 || g->bh < 1 || g->bw < 1) return false;
+  fva::Geo geo;
+  geo.T = g->T; geo.H = g->H; geo.W = g->W;
+  geo.bt = g->bt; geo.bh = g->bh; geo.bw = g->bw;
+  geo.nT = (g->T + g->bt - 1) / g->bt;
+  geo.nH = (g->H + g->bh - 1) / g->bh;
+  geo.nW = (g->W + g->bw - 1) / g->bw;
+  const int64_t n = (int64_t)geo.nT * geo.nH * geo.nW;
+  if (n > (1 << 30)) return false;
+  geo.N = (int)n;
+  *out = geo;
+  return true;
+}
+
+constexpr int kMaxBlocks = 8192;  // largest row the router sorts in one workgroup's LDS
+constexpr int64_t kMaxTokens = 1 << 24;
+
+fva_status check_desc(const fva_desc* d) {
+  if (!d) return fail(FVA_ERR_INVALID_ARG, "desc is null");
+  if (d->B < 1 || d->L < 1 || d->heads < 1 || d->D < 1)
+    return fail(FVA_ERR_INVALID_ARG, "desc sizes must be positive (B %d, L %d, heads %d, D %d)", d->B, d->L,
+                d->heads, d->D);
+  if (d->D != 64 && d->D != 128) return fail(FVA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", d->D);
+  if ((int64_t)d->L >= kMaxTokens) return fail(FVA_ERR_UNSUPPORTED, "L %d >= 2^24 not supported", d->L);
+  const int64_t elems = (int64_t)d->B * d->L * d->heads * d->D;
+  if (elems >= ((int64_t)1 << 40)) return fail(FVA_ERR_UNSUPPORTED, "tensor too large");
+  return FVA_OK;
+}
+
+fva_status check_grid(const fva_desc* d, const fva_grid* g, fva::Geo* geo) {
+  if (!g) return fail(FVA_ERR_INVALID_ARG, "grid is null");
+  if (!make_geo(g, geo))
+    return fail(FVA_ERR_INVALID_ARG, "grid and block dims must be positive (T %d H %d W %d, block %d %d %d)", g->T,
+                g->H, g->W, g->bt, g->bh, g->bw);
+  const int64_t thw = (int64_t)g->T * g->H * g->W;
+  if (thw != d->L)
+    return fail(FVA_ERR_SHAPE, "grid T*H*W = %lld does not equal sequence length %d", (long long)thw, d->L);
+  const int64_t vol = (int64_t)g->bt * g->bh * g->bw;
+  if (vol > 256) return fail(FVA_ERR_UNSUPPORTED, "block volume %lld > 256 not supported", (long long)vol);
+  return FVA_OK;
+}
+
+fva_status check_scale(int D, float scale) {
+  const double want = 1.0 / std::sqrt((double)D);
+  if (!(std::fabs((double)scale - want) <= 1e-6))
+    return fail(FVA_ERR_SCALE, "scale %.9g is not head_dim^-0.5 = %.9g within 1e-6", (double)scale, want);
+  return FVA_OK;
+}
+
+struct RouteWs {
+  size_t qbar, kbar, s, total;
+};
+
+RouteWs route_ws_layout(const fva_desc* d, const fva::Geo& g) {
+  RouteWs w;
+  const size_t rows = (size_t)d->B * d->heads * g.N;
+  size_t off = 0;
+  w.qbar = off; off += align_up(rows * d->D * sizeof(double));
+  w.kbar = off; off += align_up(rows * d->D * sizeof(double));
+  w.s = off; off += align_up(rows * (size_t)g.N * sizeof(double));
+  w.total = off;
+  return w;
+}
+
+struct AttnWs {
+  size_t tok, cnt, keys, rank, order, queue, total;
+};
+
+AttnWs attn_ws_layout(const fva_desc* d, const fva::Geo& g) {
+  AttnWs w;
+  const size_t items = (size_t)d->B * d->heads * g.N;
+  size_t off = 0;
+  w.tok = off; off += align_up((size_t)d->L * sizeof(int32_t));
+  w.cnt = off; off += align_up((size_t)g.N * sizeof(int32_t));
+  w.keys = off; off += align_up(items * sizeof(uint64_t));
+  w.rank = off; off += align_up(items * sizeof(uint32_t));
+  w.order = off; off += align_up(items * sizeof(int32_t));
+  w.queue = off; off += align_up(sizeof(uint32_t));
+  w.total = off;
+  return w;
+}
+
+fva_status check_ws(const void* ws, size_t have, size_t need) {
+  if (!ws) return fail(FVA_ERR_WORKSPACE, "workspace is null (%zu bytes needed)", need);
+  if (((uintptr_t)ws) % kAlign) return fail(FVA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  if (have < need) return fail(FVA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", have, need);
+  return FVA_OK;
+}
+
+fva_status device_error(hipError_t e, const char* what) {
+  return fail(FVA_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t fva_num_blocks(const fva_grid* grid) {
+  fva::Geo g;
+  if (!make_geo(grid, &g)) return -1;
+  return g.N;
+}
+
+size_t fva_route_workspace_bytes(const fva_desc* desc, const fva_grid* grid) {
+  fva::Geo g;
+  if (check_desc(desc) != FVA_OK || check_grid(desc, grid, &g) != FVA_OK) return 0;
+  return route_ws_layout(desc, g).total;
+}
+
+size_t fva_attn_workspace_bytes(const fva_desc* desc, const fva_grid* grid) {
+  fva::Geo g;
+  if (check_desc(desc) != FVA_OK || check_grid(desc, grid, &g) != FVA_OK) return 0;
+  return attn_ws_layout(desc, g).total;
+}
+
+int32_t fva_attn_workgroups(const fva_desc* desc, const fva_grid* grid) {
+  fva::Geo g;
+  if (check_desc(desc) != FVA_OK || check_grid(desc, grid, &g) != FVA_OK) return -1;
+  int err = 0;
+  const int n = fva::attn_persistent_workgroups(desc->D, fva::attn_waves_for_block(g.bt * g.bh * g.bw), &err);
+  return err ? -1 : n;
+}
+
+fva_status fva_route(const void* q, const void* k, const fva_desc* desc, const fva_grid* grid,
+                     const fva_route_cfg* cfg, uint32_t* mask, int32_t* kv_cnt, uint32_t* status, void* ws,
+                     size_t ws_bytes, void* stream) {
+  if (!q || !k || !mask || !cfg) return fail(FVA_ERR_INVALID_ARG, "q, k, mask and cfg must not be null");
+  fva_status st = check_desc(desc);
+  if (st != FVA_OK) return st;
+  fva::Geo g;
+  if ((st = check_grid(desc, grid, &g)) != FVA_OK) return st;
+  if (std::isnan(cfg->top_p)) return fail(FVA_ERR_INVALID_ARG, "top_p is NaN");
+  if (cfg->k_floor < 1) return fail(FVA_ERR_TOPK, "k_floor %d must be a positive integer", cfg->k_floor);
+  if (cfg->k_floor > g.N) return fail(FVA_ERR_TOPK, "k_floor %d > num_blocks %d", cfg->k_floor, g.N);
+  if (g.N > kMaxBlocks) return fail(FVA_ERR_UNSUPPORTED, "num_blocks %d > %d not supported", g.N, kMaxBlocks);
+  const RouteWs lay = route_ws_layout(desc, g);
+  if ((st = check_ws(ws, ws_bytes, lay.total)) != FVA_OK) return st;
+
+  hipStream_t s = (hipStream_t)stream;
+  char* w = (char*)ws;
+  double* qbar = (double*)(w + lay.qbar);
+  double* kbar = (double*)(w + lay.kbar);
+  double* S = (double*)(w + lay.s);
+  hipError_t e = fva::launch_pool(q, k, g, desc->B, desc->L, desc->heads, desc->D, qbar, kbar, status, s);
+  if (e != hipSuccess) return device_error(e, "pool kernel launch");
+  e = fva::launch_scores(qbar, kbar, desc->B * desc->heads, g.N, desc->D, S, s);
+  if (e != hipSuccess) return device_error(e, "scores kernel launch");
+  e = fva::launch_route_rows(S, (int64_t)desc->B * desc->heads * g.N, g.N, cfg->top_p, cfg->k_floor, mask, kv_cnt,
+                             status, s);
+  if (e != hipSuccess) return device_error(e, "route kernel launch");
+  return ok();
+}
+
+fva_status fva_sparse_attn(const void* q, const void* k, const void* v, void* o, const fva_desc* desc,
+                           const fva_grid* grid, const uint32_t* mask, float scale, int32_t sched, uint64_t* trace,
+                           void* ws, size_t ws_bytes, void* stream) {
+  if (!q || !k || !v || !o || !mask) return fail(FVA_ERR_INVALID_ARG, "q, k, v, o and mask must not be null");
+  fva_status st = check_desc(desc);
+  if (st != FVA_OK) return st;
+  fva::Geo g;
+  if ((st = check_grid(desc, grid, &g)) != FVA_OK) return st;
+  if ((st = check_scale(desc->D, scale)) != FVA_OK) return st;
+  if (sched != FVA_SCHED_LPT && sched != FVA_SCHED_NAIVE) return fail(FVA_ERR_INVALID_ARG, "unknown schedule %d", sched);
+  const int64_t items = (int64_t)desc->B * desc->heads * g.N;
+  if (items >= ((int64_t)1 << 31)) return fail(FVA_ERR_UNSUPPORTED, "too many work items");
+  const AttnWs lay = attn_ws_layout(desc, g);
+  if ((st = check_ws(ws, ws_bytes, lay.total)) != FVA_OK) return st;
+
+  char* w = (char*)ws;
+  fva::AttnLaunch a;
+  a.q = q; a.k = k; a.v = v; a.o = o;
+  a.B = desc->B; a.L = desc->L; a.heads = desc->heads; a.D = desc->D;
+  a.g = g;
+  a.mask = mask;
+  a.scale = scale;
+  a.trace = trace;
+  a.tok = (int32_t*)(w + lay.tok);
+  a.blk_cnt = (int32_t*)(w + lay.cnt);
+  a.keys = (uint64_t*)(w + lay.keys);
+  a.rank = (uint32_t*)(w + lay.rank);
+  a.order = (int32_t*)(w + lay.order);
+  a.queue = (uint32_t*)(w + lay.queue);
+  hipError_t e = fva::launch_sparse_attn(a, sched == FVA_SCHED_LPT, (hipStream_t)stream);
+  if (e != hipSuccess) return device_error(e, "sparse attention launch");
+  return ok();
+}
+
+fva_status fva_dense_attn_ref(const void* q, const void* k, const void* v, void* o, const fva_desc* desc, float scale,
+                              void* stream) {
+  if (!q || !k || !v || !o) return fail(FVA_ERR_INVALID_ARG, "q, k, v and o must not be null");
+  fva_status st = check_desc(desc);
+  if (st != FVA_OK) return st;
+  if ((st = check_scale(desc->D, scale)) != FVA_OK) return st;
+  hipError_t e = fva::launch_dense_attn(q, k, v, o, desc->B, desc->L, desc->heads, desc->D, scale, (hipStream_t)stream);
+  if (e != hipSuccess) return device_error(e, "dense attention launch");
+  return ok();
+}
+
+fva_status fva_trace_imbalance(const uint64_t* t, int32_t n_wg, double* busy_ratio, double* finish_ratio,
+                               int32_t* n_cu) {
+  if (!t || n_wg < 1 || !busy_ratio || !finish_ratio) return fail(FVA_ERR_INVALID_ARG, "bad trace arguments");
+  // CU identity: XCC id plus the HW_ID fields se_id [15:13], sh_id [12], cu_id [11:8]
+  std::map<uint64_t, std::pair<double, uint64_t>> cu;  // key -> (busy, last end)
+  uint64_t t0 = ~0ull;
+  for (int i = 0; i < n_wg; ++i) {
+    const uint64_t* r = t + (size_t)i * 4;
+    const uint64_t items = r[3] >> 40;
+    if (!items) continue;
+    if (r[0] < t0) t0 = r[0];
+  }
+  if (t0 == ~0ull) return fail(FVA_ERR_INVALID_ARG, "trace holds no work");
+  for (int i = 0; i < n_wg; ++i) {
+    const uint64_t* r = t + (size_t)i * 4;
+    const uint64_t items = r[3] >> 40;
+    if (!items) continue;
+    const uint32_t hw = (uint32_t)r[3];
+    const uint64_t xcc = (r[3] >> 32) & 0xff;
+    const uint64_t key = (xcc << 16) | (((hw >> 13) & 7u) << 5) | (((hw >> 12) & 1u) << 4) | ((hw >> 8) & 15u);
+    auto& e = cu[key];
+    e.first += (double)r[2];
+    if (r[1] > e.second) e.second = r[1];
+  }
+  double bmax = 0, bsum = 0, fmax_ = 0, fsum = 0;
+  for (auto& kv : cu) {
+    const double b = kv.second.first, f = (double)(kv.second.second - t0);
+    bmax = std::max(bmax, b);
+    bsum += b;
+    fmax_ = std::max(fmax_, f);
+    fsum += f;
+  }
+  const double n = (double)cu.size();
+  *busy_ratio = bsum > 0 ? bmax / (bsum / n) : 0.0;
+  *finish_ratio = fsum > 0 ? fmax_ / (fsum / n) : 0.0;
+  if (n_cu) *n_cu = (int32_t)cu.size();
+  return ok();
+}
+
+const char* fva_last_error(void) { return g_last_error.c_str(); }
+
+const char* fva_status_name(int32_t s) {
+  switch (s) {
+    case FVA_OK: return "FVA_OK";
+    case FVA_ERR_INVALID_ARG: return "FVA_ERR_INVALID_ARG";
+    case FVA_ERR_SHAPE: return "FVA_ERR_SHAPE";
+    case FVA_ERR_TOPK: return "FVA_ERR_TOPK";
+    case FVA_ERR_SCALE: return "FVA_ERR_SCALE";
+    case FVA_ERR_WORKSPACE: return "FVA_ERR_WORKSPACE";
+    case FVA_ERR_UNSUPPORTED: return "FVA_ERR_UNSUPPORTED";
+    case FVA_ERR_DEVICE: return "FVA_ERR_DEVICE";
+    default: return "unknown";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,367 @@
+// fva_route.hip -- block router kernels for gfx950.
+//
+// FVAttn abstract: the sparse-routing frontend is Top-p routing with a Top-k
+// safety floor over video-aware blocks, and the materialised mask is repaired
+// at runtime.  The block score of a (query block, key block) pair is the dot
+// product of the block-mean pooled Q and K rows scaled by head_dim^-0.5
+// (scale rule: VSA guide, section 5).
+//
+// Three kernels, all taking their integer decisions in fp64 (MI355X runs fp64
+// FMA at the fp32 rate, so the router costs little and decides as an fp64
+// reference would):
+//   pool_kernel        HBM stream of Q and K -> fp64 block means [B,h,N,D]
+//   scores_kernel      per (b,h): S = Qbar Kbar^T / sqrt(D), 64x64 tiles
+//   route_rows_kernel  one workgroup per row: softmax, bitonic sort on
+//                      (score desc, index asc), scan, Top-p count, floor,
+//                      mask words and kept count
+#include "fva_dev.h"
+#include "fva_kernels.h"
+
+namespace fva {
+
+// ---------------------------------------------------------------------------
+// Block-mean pooling.  grid = (N * chunks, 2, B), 256 threads.  A chunk covers
+// 64 vectors of 8 channels (512 of the heads*D channels of a token row), one
+// vector per lane; the 4 waves split the block's (t, y) rows and their partial
+// sums are added in a fixed order.  Every token row is read as contiguous
+// 16-byte loads across the lanes of a wave.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void pool_kernel(const bf16_bits* __restrict__ q, const bf16_bits* __restrict__ k,
+                                                   Geo g, int L, int heads, int D, int chunks,
+                                                   double* __restrict__ qbar, double* __restrict__ kbar,
+                                                   uint32_t* __restrict__ status) {
+  const int n = blockIdx.x / chunks;
+  const int chunk = blockIdx.x % chunks;
+  const int which = blockIdx.y;
+  const int b = blockIdx.z;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  if (status && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) *status = 0u;
+
+  const bf16_bits* x = which == 0 ? q : k;
+  double* out = which == 0 ? qbar : kbar;
+  const int nvec = heads * D / 8;
+  const int vec = chunk * 64 + lane;
+  const bool active = vec < nvec;
+  const Box bx = block_box(g, n);
+  const int64_t row_stride = (int64_t)heads * D;
+  const bf16_bits* base = x + (int64_t)b * L * row_stride + (int64_t)vec * 8;
+
+  double acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.0;
+
+  const int rows = bx.et * bx.eh;
+  for (int r = wave; r < rows; r += 4) {
+    const int dt = r / bx.eh, dy = r % bx.eh;
+    const int64_t tok0 = ((int64_t)(bx.t0 + dt) * g.H + (bx.y0 + dy)) * g.W + bx.x0;
+    if (active) {
+      int dx = 0;
+      for (; dx + 4 <= bx.ew; dx += 4) {
+        u32x4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = *(const u32x4*)(base + (tok0 + dx + u) * row_stride);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[2 * e] += (double)__uint_as_float(v[u][e] << 16);
+            acc[2 * e + 1] += (double)__uint_as_float(v[u][e] & 0xffff0000u);
+          }
+      }
+      for (; dx < bx.ew; ++dx) {
+        u32x4 v = *(const u32x4*)(base + (tok0 + dx) * row_stride);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] += (double)__uint_as_float(v[e] << 16);
+          acc[2 * e + 1] += (double)__uint_as_float(v[e] & 0xffff0000u);
+        }
+      }
+    }
+  }
+
+  __shared__ double part[4][64][9];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) part[wave][lane][e] = acc[e];
+  __syncthreads();
+  if (wave == 0 && active) {
+    const double inv_cnt = (double)bx.count;
+    const int c0 = vec * 8;
+    const int h = c0 / D, d0 = c0 % D;
+    double* o = out + (((int64_t)b * heads + h) * g.N + n) * D + d0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      double s = part[0][lane][e];
+      s += part[1][lane][e];
+      s += part[2][lane][e];
+      s += part[3][lane][e];
+      o[e] = s / inv_cnt;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Block scores.  grid = (ceil(N/64), ceil(N/64), B*heads), 256 threads, each
+// thread a 4x4 set of outputs i = i0 + ty + 16a, j = j0 + tx + 16c.  The dot
+// product runs over d in increasing order for every (i, j), so equal key
+// blocks get bit-equal scores (exact ties stay exact).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void scores_kernel(const double* __restrict__ qbar, const double* __restrict__ kbar,
+                                                     int N, int D, double* __restrict__ S) {
+  __shared__ double As[64][33];
+  __shared__ double Bs[64][33];
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
+  const int64_t bh = blockIdx.z;
+  const double* qa = qbar + bh * N * D;
+  const double* kb = kbar + bh * N * D;
+  double acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[a][c] = 0.0;
+
+  for (int d0 = 0; d0 < D; d0 += 32) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = threadIdx.x + u * 256;  // 0..2047
+      const int r = e >> 5, c = e & 31;
+      As[r][c] = (i0 + r < N) ? qa[(int64_t)(i0 + r) * D + d0 + c] : 0.0;
+      Bs[r][c] = (j0 + r < N) ? kb[(int64_t)(j0 + r) * D + d0 + c] : 0.0;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int kk = 0; kk < 32; ++kk) {
+      double av[4], bv[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) av[a] = As[ty + 16 * a][kk];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) bv[c] = Bs[tx + 16 * c][kk];
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[a][c] = fma(av[a], bv[c], acc[a][c]);
+    }
+    __syncthreads();
+  }
+  const double rs = sqrt((double)D);
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const int i = i0 + ty + 16 * a;
+    if (i >= N) continue;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int j = j0 + tx + 16 * c;
+      if (j < N) S[(bh * N + i) * N + j] = acc[a][c] / rs;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Row routing.  One workgroup per (b, h, i) row; SLOTS = next power of two of
+// N.  Keys live in LDS as (score, index) pairs; padding slots hold -inf and
+// an index >= N so they sort last.
+// ---------------------------------------------------------------------------
+template <int THREADS>
+__device__ inline double block_sum(double v, double* red) {
+  // fixed-order tree: xor butterfly inside each wave, then waves in order
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  double s = red[0];
+#pragma unroll
+  for (int w = 1; w < THREADS / 64; ++w) s += red[w];
+  __syncthreads();
+  return s;
+}
+
+template <int THREADS>
+__device__ inline double block_max(double v, double* red) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmax(v, __shfl_xor(v, off));
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  double s = red[0];
+#pragma unroll
+  for (int w = 1; w < THREADS / 64; ++w) s = fmax(s, red[w]);
+  __syncthreads();
+  return s;
+}
+
+template <int SLOTS, int THREADS>
+__global__ __launch_bounds__(THREADS) void route_rows_kernel(const double* __restrict__ S, int N, int words,
+                                                             float top_p, int k_floor, uint32_t* __restrict__ mask,
+                                                             int32_t* __restrict__ kv_cnt,
+                                                             uint32_t* __restrict__ status) {
+  constexpr int E = SLOTS / THREADS;
+  __shared__ double key[SLOTS];
+  __shared__ uint16_t idx[SLOTS];
+  __shared__ uint32_t mw[SLOTS / 32];
+  __shared__ double red[THREADS / 64];
+  __shared__ double wtot[THREADS / 64];
+  __shared__ int nstar_s;
+
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const double* s = S + row * N;
+
+  bool bad = false;
+  double lmax = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = e * THREADS + tid;
+    double v = -INFINITY;
+    if (j < N) {
+      v = s[j];
+      if (!isfinite(v)) bad = true;
+      lmax = fmax(lmax, v);
+    }
+    key[j] = v;
+    idx[j] = (uint16_t)j;
+  }
+  for (int w = tid; w < SLOTS / 32; w += THREADS) mw[w] = 0u;
+  if (tid == 0) nstar_s = N;
+  const bool row_bad = __syncthreads_or(bad);
+
+  if (row_bad) {
+    // repair: a row whose scores cannot be ranked keeps every block
+    for (int w = tid; w < words; w += THREADS) {
+      const int lo = w * 32;
+      const int nb = min(32, N - lo);
+      mask[row * words + w] = nb == 32 ? 0xffffffffu : ((1u << nb) - 1u);
+    }
+    if (tid == 0) {
+      if (kv_cnt) kv_cnt[row] = N;
+      if (status) atomicOr(status, 1u);
+    }
+    return;
+  }
+
+  // softmax normaliser over all N blocks (max subtracted)
+  const double M = block_max<THREADS>(lmax, red);
+  double lz = 0.0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = e * THREADS + tid;
+    if (j < N) lz += exp(key[j] - M);
+  }
+  const double Z = block_sum<THREADS>(lz, red);
+
+  // bitonic sort into (score desc, index asc)
+  for (int kk = 2; kk <= SLOTS; kk <<= 1) {
+    for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+      for (int t = tid; t < SLOTS / 2; t += THREADS) {
+        const int i = 2 * t - (t & (jj - 1));
+        const int p = i + jj;
+        const double ki = key[i], kp = key[p];
+        const uint16_t xi = idx[i], xp = idx[p];
+        const bool i_first = (ki > kp) || (ki == kp && xi < xp);
+        const bool want_i_first = (i & kk) == 0;
+        if (i_first != want_i_first) {
+          key[i] = kp; key[p] = ki;
+          idx[i] = xp; idx[p] = xi;
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  // cumulative mass in sorted order: each thread owns E consecutive slots
+  const double p = (double)top_p;
+  double pm[E];
+  double run = 0.0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int m = tid * E + e;
+    pm[e] = (m < N) ? exp(key[m] - M) / Z : 0.0;
+    run += pm[e];
+  }
+  // exclusive prefix of the per-thread totals: inclusive scan in each wave,
+  // then wave totals in order
+  double incl = run;
+  const int lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const double o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) wtot[wave] = incl;
+  __syncthreads();
+  double base = incl - run;
+  for (int w = 0; w < wave; ++w) base += wtot[w];
+
+  int nstar;
+  if (p >= 1.0) {
+    nstar = N;
+  } else if (p <= 0.0) {
+    nstar = 0;
+  } else {
+    double c = base;
+    int first = N;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int m = tid * E + e;
+      c += pm[e];
+      if (m < N && c >= p && first == N) first = m + 1;
+    }
+    if (first < N) atomicMin(&nstar_s, first);
+    __syncthreads();
+    nstar = nstar_s;
+  }
+  const int keep = min(N, max(k_floor, nstar));
+
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int m = tid * E + e;
+    if (m < keep) atomicOr(&mw[idx[m] >> 5], 1u << (idx[m] & 31));
+  }
+  __syncthreads();
+  for (int w = tid; w < words; w += THREADS) mask[row * words + w] = mw[w];
+  if (tid == 0 && kv_cnt) kv_cnt[row] = keep;
+}
+
+// ---------------------------------------------------------------------------
+// launches
+// ---------------------------------------------------------------------------
+hipError_t launch_pool(const void* q, const void* k, const Geo& g, int B, int L, int heads, int D, double* qbar,
+                       double* kbar, uint32_t* status, hipStream_t st) {
+  const int nvec = heads * D / 8;
+  const int chunks = (nvec + 63) / 64;
+  dim3 grid(g.N * chunks, 2, B);
+  hipLaunchKernelGGL(pool_kernel, grid, dim3(256), 0, st, (const bf16_bits*)q, (const bf16_bits*)k, g, L, heads, D,
+                     chunks, qbar, kbar, status);
+  return hipGetLastError();
+}
+
+hipError_t launch_scores(const double* qbar, const double* kbar, int BH, int N, int D, double* S, hipStream_t st) {
+  dim3 grid((N + 63) / 64, (N + 63) / 64, BH);
+  hipLaunchKernelGGL(scores_kernel, grid, dim3(256), 0, st, qbar, kbar, N, D, S);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_rows(const double* S, int64_t rows, int N, float top_p, int k_floor, uint32_t* mask,
+                             int32_t* kv_cnt, uint32_t* status, hipStream_t st) {
+  const int words = (N + 31) / 32;
+  dim3 grid((unsigned)rows);
+#define FVA_ROUTE_CASE(SL, TH)                                                                                 \
+  if (N <= SL) {                                                                                               \
+    hipLaunchKernelGGL((route_rows_kernel<SL, TH>), grid, dim3(TH), 0, st, S, N, words, top_p, k_floor, mask, \
+                       kv_cnt, status);                                                                        \
+    return hipGetLastError();                                                                                  \
+  }
+  FVA_ROUTE_CASE(64, 64)
+  FVA_ROUTE_CASE(128, 64)
+  FVA_ROUTE_CASE(256, 64)
+  FVA_ROUTE_CASE(512, 64)
+  FVA_ROUTE_CASE(1024, 128)
+  FVA_ROUTE_CASE(2048, 256)
+  FVA_ROUTE_CASE(4096, 512)
+  FVA_ROUTE_CASE(8192, 1024)
+#undef FVA_ROUTE_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fva

@@ -1,0 +1,246 @@
+"""Benchmark: one routed block-sparse attention layer per step on one MI355X.
+
+A step is the whole hot path on one layer's Q/K/V already resident in HBM:
+fva_route (block-mean pooling, pooled scores, softmax, sort, cumulative Top-p
+count, Top-k floor, mask) followed by fva_sparse_attn (work costs, LPT order,
+persistent block-sparse flash attention).  Prints one JSON line.
+
+Inputs are seeded synthetic Q/K/V shaped like a Wan2.2 14B-like attention
+layer (27280 = 31x22x40 tokens, 40 heads, head_dim 128, (4,8,8) blocks); no
+model weights or real activations are used.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6    # MI355X dense bf16 MFMA (no sparsity)
+PEAK_HBM_GBS = 8000.0
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="wan14b")
+    ap.add_argument("--sched", default="lpt", choices=["lpt", "naive"])
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--oracle-items", type=int, default=48, help="work items in the CPU oracle sample")
+    ap.add_argument("--no-dense", action="store_true", help="skip timing the dense reference")
+    ap.add_argument("--traffic", default=None, help="JSON file with rocprofv3 FETCH/WRITE per attention launch")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the path has no multi-GPU part in this build "
+              "(it would shard by head; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import adaptive_block_sparse_tile_amd as fva
+    import fvgen
+
+    wl = fvgen.WORKLOADS[args.workload]
+    t0 = time.time()
+    host = fvgen.generate_qkv(wl, seed=args.seed)
+    gen_s = time.time() - t0
+    dev = [torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda() for a in host]
+    q, k, v = dev
+    shape = tuple(q.shape)
+    B, L, heads, D = shape
+    N = fva.num_blocks(wl.grid, wl.block)
+    words = (N + 31) // 32
+    mask = torch.empty((B, heads, N, words), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((B, heads, N), dtype=torch.int32, device="cuda")
+    status = torch.empty((1,), dtype=torch.int32, device="cuda")
+    o = torch.empty_like(q)
+    ws_r = fva.workspace(fva.route_workspace_bytes(shape, wl.grid, wl.block), q.device)
+    ws_a = fva.workspace(fva.attn_workspace_bytes(shape, wl.grid, wl.block), q.device)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        fva.route(q, k, wl.grid, wl.block, wl.top_p, wl.k_floor, ws=ws_r, out=(mask, cnt, status), stream=stream)
+        fva.sparse_attn(q, k, v, wl.grid, wl.block, mask, sched=args.sched, ws=ws_a, out=o, stream=stream)
+
+    print("[bench] workload %s: generated inputs in %.1fs; warmup %d" % (wl.name, gen_s, args.warmup),
+          file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K whole steps, plus per-call events on the same stream
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for s in range(args.steps):
+        ev[s][0].record(stream)
+        fva.route(q, k, wl.grid, wl.block, wl.top_p, wl.k_floor, ws=ws_r, out=(mask, cnt, status), stream=stream)
+        ev[s][1].record(stream)
+        fva.sparse_attn(q, k, v, wl.grid, wl.block, mask, sched=args.sched, ws=ws_a, out=o, stream=stream)
+        ev[s][2].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_step = total_ms / args.steps
+    route_ms = float(np.median([e[0].elapsed_time(e[1]) for e in ev]))
+    attn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    print("[bench] timed %d steps: %.3f ms/step (route %.3f ms, attention call %.3f ms)"
+          % (args.steps, ms_step, route_ms, attn_ms), file=sys.stderr, flush=True)
+
+    # algorithmic work of the routed mask (real token pairs)
+    mask_h = mask.cpu().numpy().view(np.uint32)
+    cnt_h = cnt.cpu().numpy()
+    counts = _block_counts(wl)
+    kept = ((mask_h[..., :, None] >> np.arange(32, dtype=np.uint32)) & 1).reshape(B, heads, N, -1)[..., :N]
+    kv_tok = (kept * counts[None, None, None, :]).sum(-1)
+    pairs = int((kv_tok * counts[None, None, :]).sum())
+    eff_flop = 4.0 * D * pairs
+    dense_flop = 4.0 * D * float(L) * L * heads * B
+    eff_tflops = eff_flop / (ms_step * 1e-3) / 1e12
+    attn_tflops = eff_flop / (attn_ms * 1e-3) / 1e12
+    frac_per_head = cnt_h.mean(axis=(0, 2)) / N
+
+    # route stage bytes: Q and K read once by the pooling kernel
+    route_bytes = 2.0 * B * L * heads * D * 2
+
+    # dense reference (same MFMA core over all tokens), for the speedup
+    dense_ms = None
+    if not args.no_dense:
+        od = torch.empty_like(q)
+        for _ in range(2):
+            fva.dense_attn_ref(q, k, v, out=od, stream=stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        nd = max(3, args.steps // 4)
+        e0.record(stream)
+        for _ in range(nd):
+            fva.dense_attn_ref(q, k, v, out=od, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dense_ms = e0.elapsed_time(e1) / nd
+
+    # CU imbalance of the persistent kernel (separate, untimed run with a trace)
+    nwg = fva.attn_workgroups(shape, wl.grid, wl.block)
+    imb = {}
+    for sched in ("lpt", "naive"):
+        tr = torch.zeros(nwg * 4, dtype=torch.int64, device="cuda")
+        fva.sparse_attn(q, k, v, wl.grid, wl.block, mask, sched=sched, trace=tr, ws=ws_a, out=o, stream=stream)
+        torch.cuda.synchronize()
+        busy, finish, ncu = fva.trace_imbalance(tr.cpu().numpy())
+        imb[sched] = {"busy_max_over_mean": round(busy, 4), "finish_max_over_mean": round(finish, 4), "cus": ncu}
+
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            traffic = json.load(f).get("bytes_per_launch")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = _cpu_baseline(wl, host, mask_h, counts, args.oracle_items)
+
+    res = {
+        "metric": "effective TFLOP/s of routed sparse attention per layer (Wan 27280-token, 40-head layer)",
+        "value": round(eff_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded smooth-field + noise Q/K/V; no model weights)",
+        "config": {
+            "workload": "%s: B=%d, heads=%d, head_dim=%d, grid=%s=%d tokens, block=%s -> %d blocks, "
+                        "top_p=%g, k_floor=%d, sched=%s" % (wl.name, B, heads, D, list(wl.grid), L, list(wl.block),
+                                                             N, wl.top_p, wl.k_floor, args.sched),
+        },
+        "ms_per_layer": round(ms_step, 4),
+        "route_ms": round(route_ms, 4),
+        "route_gbs": round(route_bytes / (route_ms * 1e-3) / 1e9, 1),
+        "attn_call_ms": round(attn_ms, 4),
+        "effective_flop": eff_flop,
+        "dense_equiv_tflops": round(dense_flop / (ms_step * 1e-3) / 1e12, 2),
+        "kept_fraction_per_head": {"min": round(float(frac_per_head.min()), 4),
+                                   "mean": round(float(frac_per_head.mean()), 4),
+                                   "max": round(float(frac_per_head.max()), 4)},
+        "dense_ref_ms": None if dense_ms is None else round(dense_ms, 4),
+        "dense_ref_tflops": None if dense_ms is None else round(dense_flop / (dense_ms * 1e-3) / 1e12, 2),
+        "speedup_vs_dense_ref": None if dense_ms is None else round(dense_ms / ms_step, 3),
+        "cu_imbalance": imb,
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(attn_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def _block_counts(wl):
+    """Real tokens per block (harness arithmetic on the grid, for FLOP counting)."""
+    T, H, W = wl.grid
+    bt, bh, bw = wl.block
+    et = [min(bt, T - i * bt) for i in range(-(-T // bt))]
+    eh = [min(bh, H - i * bh) for i in range(-(-H // bh))]
+    ew = [min(bw, W - i * bw) for i in range(-(-W // bw))]
+    return np.array([a * b * c for a in et for b in eh for c in ew], dtype=np.int64)
+
+
+def _cpu_baseline(wl, host, mask_h, counts, n_items):
+    """The fp64 oracle, as it stands, on the host cores: the full router, plus
+    attention on a seeded sample of work items (including the heaviest and the
+    lightest).  Reported as effective TFLOP/s on that sample."""
+    import oracle
+    q, k, v = host
+    N = len(counts)
+    B, heads = mask_h.shape[0], mask_h.shape[1]
+    threads = max(1, min(16, os.cpu_count() or 1))
+    print("[bench] cpu baseline: oracle router + %d attention items on %d threads" % (n_items, threads),
+          file=sys.stderr, flush=True)
+    t0 = time.time()
+    oracle.route(q, k, wl.grid, wl.block, wl.top_p, wl.k_floor, nthreads=threads)
+    route_s = time.time() - t0
+    kept = ((mask_h[..., :, None] >> np.arange(32, dtype=np.uint32)) & 1).reshape(B * heads * N, -1)[:, :N]
+    cost = counts[np.arange(B * heads * N) % N] * (kept * counts[None, :]).sum(1)
+    rng = np.random.default_rng(1)
+    pick = {int(np.argmax(cost)), int(np.argmin(cost))}
+    while len(pick) < min(n_items, cost.size):
+        pick.add(int(rng.integers(cost.size)))
+    items = np.array(sorted(pick))
+    t0 = time.time()
+    oracle.attn(q, k, v, wl.grid, wl.block, mask_h, 1.0 / math.sqrt(wl.head_dim), items=items, nthreads=threads)
+    attn_s = time.time() - t0
+    flop = 4.0 * wl.head_dim * float(cost[items].sum())
+    total_flop = 4.0 * wl.head_dim * float(cost.sum())
+    return {
+        "value": round(flop / attn_s / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": "%d of %d work items (heaviest, lightest, seeded random), %.2f%% of the layer's effective FLOPs; "
+                  "attention %.1fs, full router %.2fs; whole layer extrapolated %.0fs"
+                  % (len(items), cost.size, 100 * flop / total_flop, attn_s, route_s,
+                     route_s + attn_s * total_flop / flop),
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,164 @@
+/*
+ * fva.h -- C ABI of libfva: routed block-sparse attention for video DiTs on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The library computes, on the GPU, the data-parallel hot path of
+ * training-free adaptive sparse attention as the FVAttn abstract describes
+ * its sparse-routing frontend (Top-p routing, a Top-k safety floor,
+ * video-aware block organisation, a mask repaired at runtime) followed by
+ * attention restricted to the routed blocks:
+ *   1. the (T,H,W) latent token grid is tiled into (bt,bh,bw) blocks; the
+ *      number of blocks is prod ceil(dim/block) and the blocks on the far
+ *      edges are ragged (vLLM-Omni FastVideo VSA guide, sections 1, 3, 6);
+ *   2. fva_route: per (batch, head, query block), block-mean pooled Q and K,
+ *      scores scaled by 1/sqrt(D), row softmax over all blocks, a descending
+ *      order, the smallest prefix whose cumulative probability reaches top_p,
+ *      at least k_floor blocks, materialised as a bit mask;
+ *   3. fva_sparse_attn: exact softmax attention of every real query token
+ *      over the real tokens of the kept key blocks only, scheduled across the
+ *      compute units longest-item-first from the routed per-row work (the
+ *      one-GPU share of the FVAttn abstract's runtime load balancing).
+ *
+ * Conventions shared by every entry point
+ *   - Tensors Q, K, V, O are bf16, contiguous BSHD: element (b, l, h, d) at
+ *     ((b*L + l)*heads + h)*D + d.  Token l = (t*H + y)*W + x.
+ *   - Every tensor, mask and workspace pointer is a DEVICE pointer owned by
+ *     the caller.  The library never allocates, frees or caches device memory
+ *     and keeps no state between calls.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls enqueue their kernels on it and return without synchronising.
+ *   - Arguments are validated on the host before anything is enqueued; on a
+ *     validation error nothing is launched, the status says which rule failed
+ *     and fva_last_error() gives the detail.  There is no fallback path: the
+ *     library never silently runs something else.
+ *   - FVA_ERR_DEVICE means a HIP call failed while enqueueing; the HIP
+ *     context may be unusable and the caller must not continue on it.
+ *   - Calls that share a workspace buffer must not overlap in time.
+ */
+#ifndef FVA_H
+#define FVA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FVA_OK = 0,
+  FVA_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, NaN top_p, unknown schedule */
+  FVA_ERR_SHAPE = 2,       /* T*H*W != L */
+  FVA_ERR_TOPK = 3,        /* k_floor < 1 or k_floor > num_blocks */
+  FVA_ERR_SCALE = 4,       /* |scale - 1/sqrt(D)| > 1e-6 */
+  FVA_ERR_WORKSPACE = 5,   /* workspace null, smaller than required or not 256-byte aligned */
+  FVA_ERR_UNSUPPORTED = 6, /* D not in {64,128}; block volume > 256; num_blocks > 8192 */
+  FVA_ERR_DEVICE = 7       /* a HIP runtime call failed */
+} fva_status;
+
+/* Latent token grid (T, H, W) and block shape (bt, bh, bw), all >= 1. */
+typedef struct {
+  int32_t T, H, W;
+  int32_t bt, bh, bw;
+} fva_grid;
+
+/* Shape of the contiguous BSHD bf16 tensors Q, K, V and O. */
+typedef struct {
+  int32_t B, L, heads, D;
+} fva_desc;
+
+/* Routing knobs.  0 < top_p < 1: Top-p with a floor of k_floor blocks;
+ * top_p >= 1: every block is kept; top_p <= 0: Top-p is off and exactly
+ * k_floor blocks are kept (fixed top-k, as the VSA backend does).
+ * 1 <= k_floor <= num_blocks; k_floor == num_blocks gives dense rows. */
+typedef struct {
+  float top_p;
+  int32_t k_floor;
+} fva_route_cfg;
+
+/* Schedules of the persistent attention kernel. */
+#define FVA_SCHED_LPT 0   /* work items in descending order of real token pairs */
+#define FVA_SCHED_NAIVE 1 /* work items in (batch, head, query block) order */
+
+/* Number of blocks prod ceil(dim/block) (VSA guide, section 3), or -1 when a
+ * dimension is not positive.  Host only. */
+int32_t fva_num_blocks(const fva_grid* grid);
+
+/* Device workspace fva_route needs (pooled Q and K and the block scores,
+ * fp64), or 0 for invalid arguments.  Host only. */
+size_t fva_route_workspace_bytes(const fva_desc* desc, const fva_grid* grid);
+
+/* Device workspace fva_sparse_attn needs (block-ordered token table, work
+ * item costs, ranks, order and queue counter), or 0 for invalid arguments. */
+size_t fva_attn_workspace_bytes(const fva_desc* desc, const fva_grid* grid);
+
+/* Number of persistent workgroups fva_sparse_attn launches on the current
+ * device for this shape; the trace buffer holds 4 uint64 per workgroup.
+ * Returns -1 on invalid arguments or a HIP error. */
+int32_t fva_attn_workgroups(const fva_desc* desc, const fva_grid* grid);
+
+/* Block router (FVAttn abstract: Top-p routing, Top-k safety floor,
+ * video-aware blocks, runtime mask repair; VSA guide section 5: scores use
+ * head_dim^-0.5).  Pooling, scores, softmax, order, cumulative mass and the
+ * count are taken in fp64; ties in score go to the lower block index.
+ *   q, k     bf16 [B, L, heads, D] (device)
+ *   mask     out, uint32 [B, heads, N, ceil(N/32)]: bit (j % 32) of word
+ *            j / 32 of row (b, h, i) is set iff key block j is kept for
+ *            query block i.  Rows are written whole.
+ *   kv_cnt   out, int32 [B, heads, N]: kept blocks per row (nullable).
+ *   status   out, uint32 [1]: bit 0 set if some row had a non-finite score
+ *            and was repaired to keep every block (nullable).
+ *   ws       device workspace of at least fva_route_workspace_bytes(),
+ *            256-byte aligned; contents on entry are ignored.
+ * Errors: INVALID_ARG, SHAPE, TOPK ("k_floor K > num_blocks N"),
+ * UNSUPPORTED, WORKSPACE, DEVICE. */
+fva_status fva_route(const void* q, const void* k, const fva_desc* desc, const fva_grid* grid,
+                     const fva_route_cfg* cfg, uint32_t* mask, int32_t* kv_cnt, uint32_t* status, void* ws,
+                     size_t ws_bytes, void* stream);
+
+/* Block-sparse attention (VSA guide sections 1 and 6: each query block
+ * attends only to its selected key/value blocks; ragged edge blocks run on
+ * their real prefix and padding never acts as a key).  For every real token
+ * l of query block i of (b, h):
+ *   O[b,l,h,:] = sum_{l' in kept(i)} softmax_l'(scale * Q[b,l,h,:].K[b,l',h,:]) V[b,l',h,:]
+ * with bf16 MFMA products, fp32 accumulation and online softmax, and the
+ * result rounded to bf16.  Every token of the grid is written.
+ *   q, k, v  bf16 [B, L, heads, D] (device); o out, same shape
+ *   mask     uint32 [B, heads, N, ceil(N/32)] as fva_route writes it; a row
+ *            with no bit set is an error the caller must avoid (its O rows
+ *            are written as zeros)
+ *   scale    softmax scale; must be within 1e-6 of 1/sqrt(D)
+ *   sched    FVA_SCHED_LPT or FVA_SCHED_NAIVE; both give bitwise equal O
+ *   trace    nullable device uint64 [fva_attn_workgroups()][4]: per
+ *            workgroup first-item start, last-item end, summed item time
+ *            (100 MHz ticks) and (items << 40 | xcc_id << 32 | hw_id)
+ *   ws       device workspace of at least fva_attn_workspace_bytes()
+ * Errors: INVALID_ARG, SHAPE, SCALE, UNSUPPORTED, WORKSPACE, DEVICE. */
+fva_status fva_sparse_attn(const void* q, const void* k, const void* v, void* o, const fva_desc* desc,
+                           const fva_grid* grid, const uint32_t* mask, float scale, int32_t sched, uint64_t* trace,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/* Dense softmax attention over all L tokens (the FlashAttention baseline the
+ * FVAttn abstract measures against), same numerics as fva_sparse_attn and
+ * no workspace.  Errors: INVALID_ARG, SCALE, UNSUPPORTED, DEVICE. */
+fva_status fva_dense_attn_ref(const void* q, const void* k, const void* v, void* o, const fva_desc* desc, float scale,
+                              void* stream);
+
+/* Host helper: CU imbalance from a trace copied to host memory.  Groups the
+ * workgroups by compute unit (xcc, shader engine, CU) and returns max/mean of
+ * summed busy time and of finish time (last end - earliest start) over the
+ * CUs that ran work.  Returns INVALID_ARG for null pointers or n_wg < 1. */
+fva_status fva_trace_imbalance(const uint64_t* host_trace, int32_t n_wg, double* busy_max_over_mean,
+                               double* finish_max_over_mean, int32_t* n_cu);
+
+/* Detail of the last error on the calling thread ("" if none). */
+const char* fva_last_error(void);
+
+/* Short name of a status code. */
+const char* fva_status_name(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FVA_H */

@@ -1,0 +1,116 @@
+"""The C-ABI boundary on the CPU: the library loads, exports every symbol the
+header declares, and rejects invalid arguments on the host before touching
+the GPU (no compute calls here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import adaptive_block_sparse_tile_amd as fva
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fva.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(fva.LIB_PATH), reason="libfva.so not built")
+
+FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: every call below fails validation first
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fva_[a-z_]+)\s*\(", src)))
+
+
+def test_header_and_binding_agree():
+    assert _declared() == sorted(fva.EXPORTS)
+
+
+def test_exports_every_declared_symbol():
+    lib = fva.load()
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_num_blocks():
+    assert fva.num_blocks((31, 22, 40), (4, 8, 8)) == 120
+    assert fva.num_blocks((21, 45, 80), (4, 8, 8)) == 360
+    assert fva.num_blocks((96, 64, 64), (4, 4, 4)) == 6144
+    assert fva.num_blocks((8, 16, 16), (4, 8, 8)) == 8
+    assert fva.num_blocks((0, 16, 16), (4, 8, 8)) == -1
+
+
+def test_workspace_sizes():
+    shape = (1, 27280, 40, 128)
+    r = fva.route_workspace_bytes(shape, (31, 22, 40), (4, 8, 8))
+    rows = 40 * 120
+    assert r >= 2 * rows * 128 * 8 + rows * 120 * 8
+    a = fva.attn_workspace_bytes(shape, (31, 22, 40), (4, 8, 8))
+    assert a >= 27280 * 4 + rows * (8 + 4 + 4)
+    assert fva.route_workspace_bytes((1, 27281, 40, 128), (31, 22, 40), (4, 8, 8)) == 0   # T*H*W != L
+
+
+def _route(desc, grid, cfg, ws_bytes=1 << 30, ws=FAKE, mask=FAKE):
+    lib = fva.load()
+    return lib.fva_route(FAKE, FAKE, ctypes.byref(desc), ctypes.byref(grid), ctypes.byref(cfg), mask, None, None,
+                         ws, ws_bytes, None)
+
+
+def _err():
+    return fva.load().fva_last_error().decode()
+
+
+def test_route_validation_errors():
+    desc = fva.make_desc(1, 27280, 40, 128)
+    grid = fva.make_grid((31, 22, 40), (4, 8, 8))
+    assert _route(desc, grid, fva.RouteCfg(0.9, 130)) == 3
+    assert _err() == "k_floor 130 > num_blocks 120"
+    assert _route(desc, grid, fva.RouteCfg(0.9, 0)) == 3
+    assert _route(desc, grid, fva.RouteCfg(float("nan"), 8)) == 1
+    assert _route(fva.make_desc(1, 27281, 40, 128), grid, fva.RouteCfg(0.9, 8)) == 2
+    assert _route(fva.make_desc(1, 27280, 40, 96), grid, fva.RouteCfg(0.9, 8)) == 6
+    assert _route(desc, fva.make_grid((31, 22, 40), (4, 8, 16)), fva.RouteCfg(0.9, 8)) == 6
+    assert _route(desc, grid, fva.RouteCfg(0.9, 8), ws_bytes=16) == 5
+    assert _route(desc, grid, fva.RouteCfg(0.9, 8), ws=ctypes.c_void_p(0x10010)) == 5   # misaligned
+    assert _route(desc, grid, fva.RouteCfg(0.9, 8), ws=None) == 5
+    assert _route(desc, grid, fva.RouteCfg(0.9, 8), mask=None) == 1
+    # long video with 2x2x2 blocks: 48*32*32 = 49152 blocks > 8192
+    assert _route(fva.make_desc(1, 393216, 5, 128), fva.make_grid((96, 64, 64), (2, 2, 2)),
+                  fva.RouteCfg(0.9, 8)) == 6
+
+
+def test_attn_validation_errors():
+    lib = fva.load()
+    desc = fva.make_desc(1, 27280, 40, 128)
+    grid = fva.make_grid((31, 22, 40), (4, 8, 8))
+
+    def call(scale=128 ** -0.5, sched=0, ws_bytes=1 << 30, desc=desc):
+        return lib.fva_sparse_attn(FAKE, FAKE, FAKE, FAKE, ctypes.byref(desc), ctypes.byref(grid), FAKE, scale,
+                                   sched, None, FAKE, ws_bytes, None)
+
+    assert call(scale=0.088) == 4
+    assert "head_dim^-0.5" in _err()
+    assert call(sched=7) == 1
+    assert call(ws_bytes=100) == 5
+    assert call(desc=fva.make_desc(1, 100, 40, 128)) == 2
+    assert lib.fva_dense_attn_ref(FAKE, FAKE, FAKE, FAKE, ctypes.byref(desc), ctypes.c_float(0.1), None) == 4
+    assert lib.fva_dense_attn_ref(FAKE, FAKE, FAKE, None, ctypes.byref(desc), ctypes.c_float(128 ** -0.5),
+                                  None) == 1
+
+
+def test_status_names():
+    lib = fva.load()
+    for i, n in enumerate(fva.STATUS_NAMES):
+        assert lib.fva_status_name(i).decode() == n
+
+
+def test_trace_imbalance_host_helper():
+    import numpy as np
+    # 4 workgroups on 2 CUs (cu_id 0 and 1): busy 10+10 and 20+0 -> max/mean = 20/20 = 1
+    def rec(t0, t1, busy, cu, items=1):
+        return [t0, t1, busy, (items << 40) | (cu << 8)]
+    t = np.array([rec(0, 10, 10, 0), rec(0, 10, 10, 0), rec(0, 20, 20, 1), rec(0, 0, 0, 1, items=0)],
+                 dtype=np.uint64)
+    b, f, n = fva.trace_imbalance(t)
+    assert n == 2 and abs(b - 1.0) < 1e-12 and abs(f - 20 / 15) < 1e-12
