@@ -53,6 +53,7 @@ bool make_geo(const fva_grid* g, fva::Geo* out) {
 
 constexpr int kMaxBlocks = 8192;  // largest row the router sorts in one workgroup's LDS
 constexpr int64_t kMaxTokens = 1 << 24;
+constexpr int kMaxHeads = 4096;  // B*heads planned by one workgroup's LDS
 
 fva_status check_desc(const fva_desc* d) {
   if (!d) return fail(FVA_ERR_INVALID_ARG, "desc is null");
@@ -102,19 +103,24 @@ RouteWs route_ws_layout(const fva_desc* d, const fva::Geo& g) {
 }
 
 struct AttnWs {
-  size_t tok, cnt, keys, rank, order, queue, total;
+  size_t tok, cnt, tiles, keys, rank, order, head_pos, qoff, qctr, total;
 };
 
 AttnWs attn_ws_layout(const fva_desc* d, const fva::Geo& g) {
   AttnWs w;
-  const size_t items = (size_t)d->B * d->heads * g.N;
+  const size_t bh = (size_t)d->B * d->heads;
+  const size_t items = bh * g.N;
+  const int cpb = fva::attn_chunks_per_block(g.bt * g.bh * g.bw);
   size_t off = 0;
   w.tok = off; off += align_up((size_t)d->L * sizeof(int32_t));
   w.cnt = off; off += align_up((size_t)g.N * sizeof(int32_t));
+  w.tiles = off; off += align_up(fva::attn_tile_bytes(d->D, (int64_t)items * cpb));
   w.keys = off; off += align_up(items * sizeof(uint64_t));
   w.rank = off; off += align_up(items * sizeof(uint32_t));
   w.order = off; off += align_up(items * sizeof(int32_t));
-  w.queue = off; off += align_up(sizeof(uint32_t));
+  w.head_pos = off; off += align_up(bh * sizeof(int32_t));
+  w.qoff = off; off += align_up(16 * sizeof(int32_t));
+  w.qctr = off; off += align_up(16 * sizeof(uint32_t));
   w.total = off;
   return w;
 }
@@ -201,7 +207,10 @@ fva_status fva_sparse_attn(const void* q, const void* k, const void* v, void* o,
   if ((st = check_scale(desc->D, scale)) != FVA_OK) return st;
   if (sched != FVA_SCHED_LPT && sched != FVA_SCHED_NAIVE) return fail(FVA_ERR_INVALID_ARG, "unknown schedule %d", sched);
   const int64_t items = (int64_t)desc->B * desc->heads * g.N;
-  if (items >= ((int64_t)1 << 31)) return fail(FVA_ERR_UNSUPPORTED, "too many work items");
+  const int64_t slots = items * fva::attn_chunks_per_block(g.bt * g.bh * g.bw);
+  if (slots >= ((int64_t)1 << 31)) return fail(FVA_ERR_UNSUPPORTED, "too many work items");
+  if ((int64_t)desc->B * desc->heads > kMaxHeads)
+    return fail(FVA_ERR_UNSUPPORTED, "B*heads = %lld > %d not supported", (long long)desc->B * desc->heads, kMaxHeads);
   const AttnWs lay = attn_ws_layout(desc, g);
   if ((st = check_ws(ws, ws_bytes, lay.total)) != FVA_OK) return st;
 
@@ -215,10 +224,13 @@ fva_status fva_sparse_attn(const void* q, const void* k, const void* v, void* o,
   a.trace = trace;
   a.tok = (int32_t*)(w + lay.tok);
   a.blk_cnt = (int32_t*)(w + lay.cnt);
+  a.tiles = (uint16_t*)(w + lay.tiles);
   a.keys = (uint64_t*)(w + lay.keys);
   a.rank = (uint32_t*)(w + lay.rank);
   a.order = (int32_t*)(w + lay.order);
-  a.queue = (uint32_t*)(w + lay.queue);
+  a.head_pos = (int32_t*)(w + lay.head_pos);
+  a.qoff = (int32_t*)(w + lay.qoff);
+  a.qctr = (uint32_t*)(w + lay.qctr);
   hipError_t e = fva::launch_sparse_attn(a, sched == FVA_SCHED_LPT, (hipStream_t)stream);
   if (e != hipSuccess) return device_error(e, "sparse attention launch");
   return ok();

@@ -2,30 +2,56 @@
 //
 // VSA guide (sections 1 and 6): each query block attends only to its selected
 // key/value blocks; the far-edge blocks are ragged and run on their real
-// prefix, and padding never acts as a key.  FVAttn abstract: per-head work is
-// uneven after Top-p routing and is balanced at runtime from the current
-// routing; on one GPU this becomes longest-item-first list scheduling of
-// (batch, head, query block) items over the compute units.
+// prefix, and padding never acts as a key.  The guide's backend reorders the
+// sequence into a block-ordered tiled layout before its kernel; here the keys
+// and values are likewise re-tiled once per call, directly into the byte
+// image each 64-key chunk has in LDS.
 //
-// Kernel shape (one work item = the real rows of one query block):
-//   - WAVES wavefronts, each owning 32 query rows held in registers as the
-//     B operand of v_mfma_f32_32x32x16_bf16;
-//   - key/value rows stream through LDS in chunks of 64 keys, double
-//     buffered: K row-major [key][d], V transposed [d][key] so both MFMA A
-//     operands are single 16-byte LDS reads;
-//   - S^T = K Q^T puts one query per lane column, so the online softmax row
-//     statistics need only one cross-lane exchange (lane ^ 32) per chunk, and
-//     the probabilities feed O^T += V^T P^T straight from registers;
+// FVAttn abstract: Top-p routing leaves uneven per-head work, which runtime
+// load balancing moves between ranks by whole heads, from the current
+// routing.  The one-GPU share: heads are assigned longest-first to the eight
+// XCDs (each XCD has its own L2, so the keys and values of a head stay in one
+// cache), each XCD's queue runs its heads' (query block) items longest-first,
+// and a workgroup whose queue is empty takes items from the other XCDs.
+//
+// Attention kernel (one work item = the real rows of one query block):
+//   - WAVES wavefronts, each owning 32 query rows held in registers as the B
+//     operand of v_mfma_f32_32x32x16_bf16;
+//   - chunks of 64 keys stream through a 3-stage LDS ring; a chunk's image is
+//     K [64][D] followed by V^T [D][64], 16-byte pieces XOR-swizzled by row so
+//     the MFMA operand reads of 32 rows hit distinct banks;
+//   - S^T = K Q^T gives each lane one query column, so the softmax row
+//     statistics need one cross-half lane swap per chunk, and the bf16
+//     probabilities feed O^T += V^T P^T from registers;
+//   - Q K^T of chunk c+1 is issued before the softmax of chunk c so the
+//     matrix cores and the vector ALUs work at the same time;
 //   - the running max is raised lazily (only when it grows by more than 8 in
 //     log2 units), which skips most rescales of the O accumulators.
-// A persistent grid pops items from a queue in the schedule's order; the
-// dense reference runs the same core over consecutive 32*WAVES-token tiles.
 #include "fva_dev.h"
 #include "fva_kernels.h"
 
 namespace fva {
 
-constexpr int KCH = 64;  // keys per chunk
+constexpr int KCH = 64;     // keys per chunk
+constexpr int STAGES = 3;   // LDS ring depth
+constexpr int NXCD = 8;     // XCDs of an MI355X
+
+// Byte image of one chunk in LDS and in the tiled copy.
+template <int D>
+struct Img {
+  static constexpr int KELEMS = KCH * D;
+  static constexpr int ELEMS = 2 * KCH * D;
+  static constexpr int KSW = (D / 8 >= 16) ? 15 : (D / 8 - 1);
+  // K element (row, 8*piece + e)
+  __host__ __device__ static int k_off(int row, int piece) { return row * D + ((piece ^ (row & KSW)) << 3); }
+  // V^T element (d, 8*piece + e), position-ordered keys
+  __host__ __device__ static int v_off(int d, int piece) { return KELEMS + d * KCH + ((piece ^ (d & 7)) << 3); }
+};
+
+// Key k of a chunk sits at V^T position pi(k): inside each group of 16 keys,
+// bits 2 and 3 of the index trade places, so the eight keys a lane feeds one
+// 16-key MFMA step are contiguous.  pi is its own inverse.
+__host__ __device__ inline int pi_key(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
 
 struct AttnParams {
   const bf16_bits* q;
@@ -34,54 +60,42 @@ struct AttnParams {
   bf16_bits* o;
   int B, L, heads;
   Geo g;
-  int words;
+  int words, cpb;          // mask words per row; chunk slots per block
   const uint32_t* mask;
-  const int32_t* tok;    // block-ordered token ids (sparse)
-  const int32_t* order;  // item order (sparse)
-  uint32_t* queue;       // work counter (sparse)
+  const int32_t* tok;      // block-ordered token ids (sparse)
+  const bf16_bits* tiles;  // chunk images (sparse)
+  const int32_t* order;    // item order (sparse)
+  const int32_t* qoff;     // [NXCD + 1] queue segments in order (sparse)
+  uint32_t* qctr;          // [NXCD] pop counters (sparse)
   int n_items;
   int q_tiles;  // dense: query tiles per (b, h)
   float scale_log2;
   uint64_t* trace;
 };
 
-// Walks the key positions of one work item chunk by chunk: the set bits of
-// the item's mask row in ascending block order (sparse) or the whole
-// sequence (dense).  All threads of the workgroup hold the same state.
+// One chunk of a work item's key sequence.
+struct Chunk {
+  int slot;   // sparse: chunk image index; dense: first token
+  int valid;  // real keys in the chunk (1..64)
+};
+
+// Walks the chunks of one work item: the set bits of the item's mask row in
+// ascending block order (sparse) or the whole sequence (dense).  Every thread
+// of the workgroup holds the same state.
 struct KvIter {
   const uint32_t* mrow;
-  int words;
-  int w;
+  int w, words, c, nch, count, slot0;
   uint32_t bits;
-  int start, count, c, nch;
   bool done;
 
-  template <bool DENSE>
-  __device__ void first(const Geo& g, const uint32_t* row, int nwords, int L) {
-    c = 0;
-    done = false;
-    if (DENSE) {
-      start = 0;
-      count = L;
-      nch = (L + KCH - 1) / KCH;
-      return;
-    }
-    mrow = row;
-    words = nwords;
-    w = 0;
-    bits = load_word(g, 0);
-    next_block(g);
-  }
-
-  // mask word w with the bits of blocks >= N cleared
   __device__ uint32_t load_word(const Geo& g, int wi) const {
     uint32_t x = mrow[wi];
     const int rem = g.N - wi * 32;
-    if (rem < 32) x &= (1u << rem) - 1u;
+    if (rem < 32) x &= (1u << rem) - 1u;  // bits of blocks >= N are not blocks
     return x;
   }
 
-  __device__ void next_block(const Geo& g) {
+  __device__ void next_block(const Geo& g, int bh, int cpb) {
     while (bits == 0u) {
       if (++w >= words) {
         done = true;
@@ -89,17 +103,33 @@ struct KvIter {
       }
       bits = load_word(g, w);
     }
-    const int bit = __builtin_ctz(bits);
+    const int j = w * 32 + __builtin_ctz(bits);
     bits &= bits - 1u;
-    const Box bx = block_box(g, w * 32 + bit);
-    start = bx.start;
-    count = bx.count;
+    count = block_box(g, j).count;
     nch = (count + KCH - 1) / KCH;
+    slot0 = (bh * g.N + j) * cpb;
     c = 0;
   }
 
   template <bool DENSE>
-  __device__ void advance(const Geo& g) {
+  __device__ void first(const Geo& g, const uint32_t* row, int nwords, int L, int bh, int cpb) {
+    done = false;
+    c = 0;
+    if (DENSE) {
+      count = L;
+      nch = (L + KCH - 1) / KCH;
+      slot0 = 0;
+      return;
+    }
+    mrow = row;
+    words = nwords;
+    w = 0;
+    bits = load_word(g, 0);
+    next_block(g, bh, cpb);
+  }
+
+  template <bool DENSE>
+  __device__ void advance(const Geo& g, int bh, int cpb) {
     if (c + 1 < nch) {
       ++c;
       return;
@@ -108,21 +138,117 @@ struct KvIter {
       done = true;
       return;
     }
-    next_block(g);
+    next_block(g, bh, cpb);
   }
 
-  __device__ int base() const { return start + c * KCH; }
-  __device__ int valid() const { return min(KCH, count - c * KCH); }
+  template <bool DENSE>
+  __device__ Chunk chunk() const {
+    Chunk ck;
+    ck.slot = DENSE ? c * KCH : slot0 + c;
+    ck.valid = min(KCH, count - c * KCH);
+    return ck;
+  }
 };
 
+// Register staging of one chunk between its global load and its LDS store.
+template <int D, int THREADS, bool DENSE>
+struct Stager;
+
+// Sparse: the chunk image is contiguous; a linear copy.
 template <int D, int THREADS>
-struct Prefetch {
-  static constexpr int KSLOTS = 4 * D;  // (row, 16-element piece) pairs of a 64-key K chunk
-  static constexpr int KREG = (KSLOTS + THREADS - 1) / THREADS;
-  static constexpr int VSLOTS = 4 * D;  // (d pair, 8-key group) pairs of a 64-key V chunk
-  static constexpr int VREG = (VSLOTS + THREADS - 1) / THREADS;
-  u32x4 kv[KREG][2];
-  uint32_t vv[VREG][8];
+struct Stager<D, THREADS, false> {
+  static constexpr int N16 = Img<D>::ELEMS * 2 / 16;  // 16-byte pieces per image
+  static constexpr int PER = (N16 + THREADS - 1) / THREADS;
+  u32x4 r[PER];
+
+  __device__ void load(const AttnParams& p, int64_t, int64_t, Chunk ck) {
+    const u32x4* src = (const u32x4*)(p.tiles + (int64_t)ck.slot * Img<D>::ELEMS);
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int s = threadIdx.x + u * THREADS;
+      if (N16 % THREADS == 0 || s < N16) r[u] = src[s];
+    }
+  }
+  __device__ void store(bf16_bits* img) const {
+    u32x4* dst = (u32x4*)img;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int s = threadIdx.x + u * THREADS;
+      if (N16 % THREADS == 0 || s < N16) dst[s] = r[u];
+    }
+  }
+};
+
+// Dense: 64 consecutive tokens of BSHD K and V; V is transposed on the way.
+template <int D, int THREADS>
+struct Stager<D, THREADS, true> {
+  static constexpr int KP = KCH * D / 8;  // (row, piece) pairs of K
+  static constexpr int KPER = (KP + THREADS - 1) / THREADS;
+  static constexpr int VP = (D / 2) * 8;  // (d pair, 8-key group) pairs of V
+  static constexpr int VPER = (VP + THREADS - 1) / THREADS;
+  u32x4 kr[KPER];
+  uint32_t vr[VPER][8];
+
+  __device__ void load(const AttnParams& p, int64_t head_off, int64_t rs, Chunk ck) {
+    const bf16_bits* kb = p.k + head_off + (int64_t)ck.slot * rs;
+    const bf16_bits* vb = p.v + head_off + (int64_t)ck.slot * rs;
+    const bool full = ck.valid == KCH;
+#pragma unroll
+    for (int u = 0; u < KPER; ++u) {
+      const int s = threadIdx.x + u * THREADS;
+      const int row = s / (D / 8), piece = s % (D / 8);
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if ((KP % THREADS == 0 || s < KP) && (full || row < ck.valid)) x = *(const u32x4*)(kb + row * rs + piece * 8);
+      kr[u] = x;
+    }
+#pragma unroll
+    for (int u = 0; u < VPER; ++u) {
+      const int s = threadIdx.x + u * THREADS;
+      const int dp = s % (D / 2), kg = s / (D / 2);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int row = kg * 8 + e;
+        uint32_t x = 0u;
+        if ((VP % THREADS == 0 || s < VP) && (full || row < ck.valid)) x = *(const uint32_t*)(vb + row * rs + dp * 2);
+        vr[u][e] = x;
+      }
+    }
+  }
+  __device__ void store(bf16_bits* img) const {
+#pragma unroll
+    for (int u = 0; u < KPER; ++u) {
+      const int s = threadIdx.x + u * THREADS;
+      if (KP % THREADS == 0 || s < KP) {
+        const int row = s / (D / 8), piece = s % (D / 8);
+        *(u32x4*)(img + Img<D>::k_off(row, piece)) = kr[u];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < VPER; ++u) {
+      const int s = threadIdx.x + u * THREADS;
+      if (VP % THREADS == 0 || s < VP) {
+        const int dp = s % (D / 2), kg = s / (D / 2);
+        const uint32_t* w = vr[u];
+        // keys 8kg+0..3 -> positions p0+0..3, keys 8kg+4..7 -> p0+8..11
+        const int p0 = 16 * (kg >> 1) + 4 * (kg & 1);
+        u32x2 lo0, lo1, hi0, hi1;
+        lo0[0] = (w[0] & 0xffffu) | (w[1] << 16);
+        lo0[1] = (w[2] & 0xffffu) | (w[3] << 16);
+        lo1[0] = (w[4] & 0xffffu) | (w[5] << 16);
+        lo1[1] = (w[6] & 0xffffu) | (w[7] << 16);
+        hi0[0] = (w[0] >> 16) | (w[1] & 0xffff0000u);
+        hi0[1] = (w[2] >> 16) | (w[3] & 0xffff0000u);
+        hi1[0] = (w[4] >> 16) | (w[5] & 0xffff0000u);
+        hi1[1] = (w[6] >> 16) | (w[7] & 0xffff0000u);
+        const int d0 = 2 * dp, d1 = 2 * dp + 1;
+        const int pc0 = p0 >> 3, pc1 = (p0 + 8) >> 3, sub = p0 & 7;
+        *(u32x2*)(img + Img<D>::v_off(d0, pc0) + sub) = lo0;
+        *(u32x2*)(img + Img<D>::v_off(d0, pc1) + sub) = lo1;
+        *(u32x2*)(img + Img<D>::v_off(d1, pc0) + sub) = hi0;
+        *(u32x2*)(img + Img<D>::v_off(d1, pc1) + sub) = hi1;
+      }
+    }
+  }
 };
 
 template <bool DENSE>
@@ -130,96 +256,30 @@ __device__ inline int pos_to_token(const AttnParams& p, int pos) {
   return DENSE ? pos : p.tok[pos];
 }
 
-template <int D, int THREADS, bool DENSE>
-__device__ inline void load_chunk(const AttnParams& p, int64_t head_off, int base, int valid,
-                                  Prefetch<D, THREADS>& pf) {
-  using PF = Prefetch<D, THREADS>;
-  const int tid = threadIdx.x;
-  const int64_t rs = (int64_t)p.heads * D;  // token row stride (elements)
-#pragma unroll
-  for (int u = 0; u < PF::KREG; ++u) {
-    const int s = tid + u * THREADS;
-    const int r = s / (D / 16), piece = s % (D / 16);
-    u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-    if (s < PF::KSLOTS && r < valid) {
-      const int64_t tok = pos_to_token<DENSE>(p, base + r);
-      const u32x4* src = (const u32x4*)(p.k + head_off + tok * rs + piece * 16);
-      a = src[0];
-      b = src[1];
-    }
-    pf.kv[u][0] = a;
-    pf.kv[u][1] = b;
-  }
-#pragma unroll
-  for (int u = 0; u < PF::VREG; ++u) {
-    const int s = tid + u * THREADS;
-    const int dp = s % (D / 2), kg = s / (D / 2);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int r = kg * 8 + e;
-      uint32_t x = 0u;
-      if (s < PF::VSLOTS && r < valid) {
-        const int64_t tok = pos_to_token<DENSE>(p, base + r);
-        x = *(const uint32_t*)(p.v + head_off + tok * rs + dp * 2);
-      }
-      pf.vv[u][e] = x;
-    }
-  }
-}
-
-// LDS row strides (elements): 16 bytes of padding per row keeps the 16-byte
-// operand reads of 32 consecutive rows on distinct bank groups.
-template <int D>
-struct alignas(16) Lds {
-  static constexpr int KST = D + 8;
-  static constexpr int VST = KCH + 8;
-  bf16_bits k[2][KCH][KST];
-  bf16_bits vt[2][D][VST];
-};
-
-// Key k of a chunk is stored in V^T at position pi(k): inside each group of
-// 16 keys, bits 2 and 3 of the key index trade places, so the eight keys one
-// lane contributes to a 16-key MFMA step are contiguous.
-template <int D, int THREADS>
-__device__ inline void store_chunk(Lds<D>& lds, int buf, const Prefetch<D, THREADS>& pf) {
-  using PF = Prefetch<D, THREADS>;
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int u = 0; u < PF::KREG; ++u) {
-    const int s = tid + u * THREADS;
-    if (s < PF::KSLOTS) {
-      const int r = s / (D / 16), piece = s % (D / 16);
-      u32x4* dst = (u32x4*)&lds.k[buf][r][piece * 16];
-      dst[0] = pf.kv[u][0];
-      dst[1] = pf.kv[u][1];
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < PF::VREG; ++u) {
-    const int s = tid + u * THREADS;
-    if (s < PF::VSLOTS) {
-      const int dp = s % (D / 2), kg = s / (D / 2);
-      const uint32_t* w = pf.vv[u];
-      // keys 8kg+0..3 -> positions 16(kg/2) + 4(kg%2) + 0..3 ; keys 8kg+4..7 -> +8
-      const int p0 = 16 * (kg >> 1) + 4 * (kg & 1);
-      u32x2 lo0, lo1, hi0, hi1;
-      lo0[0] = (w[0] & 0xffffu) | (w[1] << 16);
-      lo0[1] = (w[2] & 0xffffu) | (w[3] << 16);
-      lo1[0] = (w[4] & 0xffffu) | (w[5] << 16);
-      lo1[1] = (w[6] & 0xffffu) | (w[7] << 16);
-      hi0[0] = (w[0] >> 16) | (w[1] & 0xffff0000u);
-      hi0[1] = (w[2] >> 16) | (w[3] & 0xffff0000u);
-      hi1[0] = (w[4] >> 16) | (w[5] & 0xffff0000u);
-      hi1[1] = (w[6] >> 16) | (w[7] & 0xffff0000u);
-      *(u32x2*)&lds.vt[buf][2 * dp][p0] = lo0;
-      *(u32x2*)&lds.vt[buf][2 * dp][p0 + 8] = lo1;
-      *(u32x2*)&lds.vt[buf][2 * dp + 1][p0] = hi0;
-      *(u32x2*)&lds.vt[buf][2 * dp + 1][p0 + 8] = hi1;
-    }
-  }
-}
-
 __device__ inline uint64_t wall_ticks() { return __builtin_amdgcn_s_memrealtime(); }
+
+// value of lane l ^ 32
+__device__ inline float swap_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
+// S^T (64 keys x 32 queries) of one chunk.
+template <int D>
+__device__ inline void qk_chunk(const bf16_bits* img, const bf16x8* qf, int lr, int hi, f32x16* s) {
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
+#pragma unroll
+  for (int ds = 0; ds < D / 16; ++ds) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const bf16x8 a = *(const bf16x8*)(img + Img<D>::k_off(32 * kt + lr, 2 * ds + hi));
+      s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ds], s[kt], 0, 0, 0);
+    }
+  }
+}
 
 template <int D, int WAVES, bool DENSE>
 __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
@@ -227,27 +287,38 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
   constexpr int QROWS = WAVES * 32;
   constexpr int DS = D / 16;  // 16-wide d steps of Q K^T
   constexpr int DT = D / 32;  // 32-row d tiles of O^T
-  __shared__ Lds<D> lds;
+  constexpr int IMG = Img<D>::ELEMS;
+  __shared__ __attribute__((aligned(16))) bf16_bits ring[STAGES][IMG];
   __shared__ int item_s;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 31, hi = lane >> 5;
+  const float cl2 = p.scale_log2;
 
   uint64_t t_first = 0, t_last = 0, busy = 0, nitems = 0;
+  int my_xcd = 0;
+  if (!DENSE) my_xcd = (int)(__builtin_amdgcn_s_getreg((15 << 11) | 20) & 7);  // HW_REG_XCC_ID
 
   for (int iter = 0;; ++iter) {
     // ---- fetch a work item
     int item;
     if (DENSE) {
       if (iter > 0) break;
-      const int per = (p.n_items + 7) / 8;  // consecutive items share an XCD (blockIdx % 8)
-      item = (blockIdx.x % 8) * per + blockIdx.x / 8;
+      const int per = (p.n_items + NXCD - 1) / NXCD;  // consecutive tiles share an XCD (blockIdx % 8)
+      item = (blockIdx.x % NXCD) * per + blockIdx.x / NXCD;
       if (item >= p.n_items) break;
     } else {
       if (tid == 0) {
-        const uint32_t slot = atomicAdd(p.queue, 1u);
-        item_s = slot < (uint32_t)p.n_items ? p.order[slot] : -1;
+        int got = -1;
+        for (int t = 0; t < NXCD && got < 0; ++t) {
+          const int x = (my_xcd + t) % NXCD;
+          const int n = p.qoff[x + 1] - p.qoff[x];
+          if (n <= 0 || __atomic_load_n(&p.qctr[x], __ATOMIC_RELAXED) >= (uint32_t)n) continue;
+          const uint32_t s = atomicAdd(&p.qctr[x], 1u);
+          if (s < (uint32_t)n) got = p.order[p.qoff[x] + s];
+        }
+        item_s = got;
       }
       __syncthreads();
       item = item_s;
@@ -255,35 +326,33 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
     }
     const uint64_t t_start = wall_ticks();
 
-    int b, h, qbase, qcount;
+    int b, h, bh, qbase, qcount;
     const uint32_t* mrow = nullptr;
     if (DENSE) {
       const int tile = item % p.q_tiles;
-      const int bh = item / p.q_tiles;
-      h = bh % p.heads;
-      b = bh / p.heads;
+      bh = item / p.q_tiles;
       qbase = tile * QROWS;
       qcount = min(QROWS, p.L - qbase);
     } else {
       const int i = item % p.g.N;
-      const int bh = item / p.g.N;
-      h = bh % p.heads;
-      b = bh / p.heads;
+      bh = item / p.g.N;
       const Box bx = block_box(p.g, i);
       qbase = bx.start;
       qcount = bx.count;
       mrow = p.mask + (int64_t)item * p.words;
     }
-    const int64_t head_off = (int64_t)b * p.L * p.heads * D + (int64_t)h * D;
+    h = bh % p.heads;
+    b = bh / p.heads;
     const int64_t rs = (int64_t)p.heads * D;
+    const int64_t head_off = (int64_t)b * p.L * rs + (int64_t)h * D;
 
     // ---- Q fragment: row 32*wave + lr, d = 16s + 8hi .. +7
     const int qrow = wave * 32 + lr;
     const bool wave_active = wave * 32 < qcount;
     bf16x8 qf[DS];
     {
-      int64_t qtok = 0;
       const bool ok = qrow < qcount;
+      int64_t qtok = 0;
       if (ok) qtok = pos_to_token<DENSE>(p, qbase + qrow);
 #pragma unroll
       for (int s = 0; s < DS; ++s) {
@@ -298,109 +367,144 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
     for (int t = 0; t < DT; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
-    float m_used = -INFINITY, lsum = 0.f;
+    float m_run = -INFINITY, lsum = 0.f;
 
+    // ---- pipeline: `it` is the next chunk to load; the ring holds `ready`
+    //      loaded chunks starting at stage `cur`, with real key counts v0, v1
     KvIter it;
-    it.template first<DENSE>(p.g, mrow, p.words, p.L);
-    Prefetch<D, THREADS> pf;
-    int buf = 0;
+    it.template first<DENSE>(p.g, mrow, p.words, p.L, bh, p.cpb);
+    Stager<D, THREADS, DENSE> st;
+    int ready = 0, v0 = 0, v1 = 0;
     if (!it.done) {
-      load_chunk<D, THREADS, DENSE>(p, head_off, it.base(), it.valid(), pf);
-      store_chunk<D, THREADS>(lds, 0, pf);
+      const Chunk ck = it.template chunk<DENSE>();
+      st.load(p, head_off, rs, ck);
+      st.store(ring[0]);
+      v0 = ck.valid;
+      ++ready;
+      it.template advance<DENSE>(p.g, bh, p.cpb);
+    }
+    if (!it.done) {
+      const Chunk ck = it.template chunk<DENSE>();
+      st.load(p, head_off, rs, ck);
+      st.store(ring[1]);
+      v1 = ck.valid;
+      ++ready;
+      it.template advance<DENSE>(p.g, bh, p.cpb);
     }
     __syncthreads();
 
-    while (!it.done) {
-      const int valid = it.valid();
-      KvIter nx = it;
-      nx.template advance<DENSE>(p.g);
-      if (!nx.done) load_chunk<D, THREADS, DENSE>(p, head_off, nx.base(), nx.valid(), pf);
+    f32x16 s_cur[2];
+    if (wave_active && ready > 0) qk_chunk<D>(ring[0], qf, lr, hi, s_cur);
+
+    int cur = 0;  // stage of the chunk being finished
+    while (ready > 0) {
+      const int valid = v0;
+      const bool has1 = ready >= 2, has2 = !it.done;
+      const int st1 = cur == STAGES - 1 ? 0 : cur + 1;
+      const int st2 = st1 == STAGES - 1 ? 0 : st1 + 1;
+      int v2 = 0;
+      if (has2) {
+        const Chunk ck = it.template chunk<DENSE>();
+        v2 = ck.valid;
+        st.load(p, head_off, rs, ck);
+      }
 
       if (wave_active) {
-        // S^T (keys x queries) for 64 keys: two 32x32 tiles
-        f32x16 s[2];
+        // Q K^T of the next chunk, independent of this chunk's softmax
+        f32x16 s_nxt[2];
+        if (has1) qk_chunk<D>(ring[st1], qf, lr, hi, s_nxt);
+
+        // ---- online softmax of this chunk (log2 units); lane holds keys
+        //      32kt + 8(r/4) + 4hi + r%4 of query lr
+        if (valid < KCH) {
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+          for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
-#pragma unroll
-        for (int ds = 0; ds < DS; ++ds) {
-#pragma unroll
-          for (int kt = 0; kt < 2; ++kt) {
-            const bf16x8 a = *(const bf16x8*)&lds.k[buf][32 * kt + lr][16 * ds + 8 * hi];
-            s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ds], s[kt], 0, 0, 0);
-          }
-        }
-        // online softmax in log2 units; lane holds keys 32kt + 8(r/4) + 4hi + r%4
-        float mloc = -INFINITY;
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float x = s[kt][r] * p.scale_log2;
-            if (valid < KCH) {
+            for (int r = 0; r < 16; ++r) {
               const int key = 32 * kt + 8 * (r >> 2) + 4 * hi + (r & 3);
-              if (key >= valid) x = -INFINITY;
+              if (key >= valid) s_cur[kt][r] = -INFINITY;
             }
-            s[kt][r] = x;
-            mloc = fmaxf(mloc, x);
-          }
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-        const float m_new = fmaxf(m_used, mloc);
-        if (__any(m_new > m_used + 8.0f)) {
-          const float alpha = __builtin_amdgcn_exp2f(m_used - m_new);
+        }
+        float mx = s_cur[0][0];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[kt][r]);
+        mx = fmaxf(mx, swap_halves(mx)) * cl2;
+        if (__any(mx > m_run + 8.0f)) {
+          const float m_new = fmaxf(m_run, mx);
+          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
           for (int t = 0; t < DT; ++t)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[t][r] *= alpha;
           lsum *= alpha;
-          m_used = m_new;
+          m_run = m_new;
         }
+        const float nm = -m_run;
         bf16x8 pb[2][2];
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-          for (int qh = 0; qh < 2; ++qh)
+          for (int qh = 0; qh < 2; ++qh) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const float pe = __builtin_amdgcn_exp2f(s[kt][8 * qh + e] - m_used);
-              lsum += pe;
-              pb[kt][qh][e] = (__bf16)pe;
+            for (int e = 0; e < 8; ++e)
+              pb[kt][qh][e] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[kt][8 * qh + e], cl2, nm));
+            typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+            const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+              const bf16x2_t pr = {pb[kt][qh][e], pb[kt][qh][e + 1]};
+              lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, one, lsum, false);
             }
-        // O^T (d x queries) += V^T P^T
+          }
+        // ---- O^T (d x queries) += V^T P^T
+        const bf16_bits* img = ring[cur];
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
           for (int qh = 0; qh < 2; ++qh)
 #pragma unroll
             for (int t = 0; t < DT; ++t) {
-              const bf16x8 a = *(const bf16x8*)&lds.vt[buf][32 * t + lr][32 * kt + 16 * qh + 8 * hi];
+              const bf16x8 a = *(const bf16x8*)(img + Img<D>::v_off(32 * t + lr, 4 * kt + 2 * qh + hi));
               acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kt][qh], acc[t], 0, 0, 0);
             }
+        if (has1) {
+          s_cur[0] = s_nxt[0];
+          s_cur[1] = s_nxt[1];
+        }
       }
 
-      if (!nx.done) store_chunk<D, THREADS>(lds, buf ^ 1, pf);
+      if (has2) {
+        st.store(ring[st2]);
+        ++ready;
+        it.template advance<DENSE>(p.g, bh, p.cpb);
+      }
       __syncthreads();
-      buf ^= 1;
-      it = nx;
+      --ready;
+      cur = st1;
+      v0 = v1;
+      v1 = v2;
     }
 
     // ---- normalise and store the real rows (lane and lane ^ 32 share a row)
-    float lt = 0.f;
-    if (wave_active) lt = lsum + __shfl_xor(lsum, 32);
-    if (wave_active && qrow < qcount) {
-      const float inv = lt > 0.f ? 1.f / lt : 0.f;
-      const int64_t otok = pos_to_token<DENSE>(p, qbase + qrow);
-      bf16_bits* dst = p.o + head_off + otok * rs;
+    if (wave_active) {
+      const float lt = lsum + swap_halves(lsum);
+      if (qrow < qcount) {
+        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        const int64_t otok = pos_to_token<DENSE>(p, qbase + qrow);
+        bf16_bits* dst = p.o + head_off + otok * rs;
 #pragma unroll
-      for (int t = 0; t < DT; ++t)
+        for (int t = 0; t < DT; ++t)
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          u32x2 w;
-          w[0] = (uint32_t)f32_to_bf16(acc[t][4 * g4 + 0] * inv) | ((uint32_t)f32_to_bf16(acc[t][4 * g4 + 1] * inv) << 16);
-          w[1] = (uint32_t)f32_to_bf16(acc[t][4 * g4 + 2] * inv) | ((uint32_t)f32_to_bf16(acc[t][4 * g4 + 3] * inv) << 16);
-          *(u32x2*)(dst + 32 * t + 8 * g4 + 4 * hi) = w;
-        }
+          for (int g4 = 0; g4 < 4; ++g4) {
+            typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+            bf16x4_t w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = (__bf16)(acc[t][4 * g4 + e] * inv);
+            *(bf16x4_t*)(dst + 32 * t + 8 * g4 + 4 * hi) = w;
+          }
+      }
     }
     const uint64_t t_end = wall_ticks();
     if (nitems == 0) t_first = t_start;
@@ -422,7 +526,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Schedule kernels
+// Per-call preparation kernels
 // ---------------------------------------------------------------------------
 
 // Block-ordered token table and real counts: one workgroup per block.
@@ -438,27 +542,66 @@ __global__ __launch_bounds__(256) void layout_kernel(Geo g, int32_t* __restrict_
   }
 }
 
-// Work of every item (real query-key token pairs) and its sort key; resets
-// the queue.  cost < 2^32 because a block holds at most 256 tokens and
-// L < 2^24.  key = cost << 32 | (~item): descending keys give descending cost,
-// ties to the lower item id.
-__global__ __launch_bounds__(256) void cost_kernel(const uint32_t* __restrict__ mask, const int32_t* __restrict__ cnt,
-                                                   int N, int words, int n_items, bool lpt,
-                                                   uint64_t* __restrict__ keys, uint32_t* __restrict__ rank,
-                                                   int32_t* __restrict__ order, uint32_t* __restrict__ queue) {
-  const int item = blockIdx.x * blockDim.x + threadIdx.x;
-  if (item == 0) *queue = 0u;
-  if (item >= n_items) return;
-  if (!lpt) {
-    order[item] = item;
-    return;
+// Chunk images of K and V: one workgroup per (b, h, block, chunk) slot.
+// Rows past the block's real count are zero.
+template <int D>
+__global__ __launch_bounds__(256) void tile_kernel(const bf16_bits* __restrict__ k, const bf16_bits* __restrict__ v,
+                                                   const int32_t* __restrict__ tok, Geo g, int L, int heads, int cpb,
+                                                   bf16_bits* __restrict__ tiles) {
+  __shared__ __attribute__((aligned(16))) bf16_bits vs[KCH][D + 8];
+  const int cs = blockIdx.x;
+  const int c = cs % cpb;
+  const int n = (cs / cpb) % g.N;
+  const int bh = cs / (cpb * g.N);
+  const int h = bh % heads, b = bh / heads;
+  const Box bx = block_box(g, n);
+  const int valid = bx.count - c * KCH;
+  if (valid <= 0) return;  // slot past the block's chunks: never read
+  const int64_t rs = (int64_t)heads * D;
+  const int64_t head_off = (int64_t)b * L * rs + (int64_t)h * D;
+  bf16_bits* img = tiles + (int64_t)cs * Img<D>::ELEMS;
+  constexpr int PIECES = KCH * D / 8;
+  for (int s = threadIdx.x; s < PIECES; s += 256) {
+    const int row = s / (D / 8), piece = s % (D / 8);
+    u32x4 kx = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
+    if (row < valid) {
+      const int64_t t = tok[bx.start + c * KCH + row];
+      kx = *(const u32x4*)(k + head_off + t * rs + piece * 8);
+      vx = *(const u32x4*)(v + head_off + t * rs + piece * 8);
+    }
+    *(u32x4*)(img + Img<D>::k_off(row, piece)) = kx;
+    *(u32x4*)&vs[row][piece * 8] = vx;
   }
+  __syncthreads();
+  for (int s = threadIdx.x; s < D * 8; s += 256) {
+    const int d = s / 8, piece = s % 8;
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int k0 = pi_key(piece * 8 + 2 * e), k1 = pi_key(piece * 8 + 2 * e + 1);
+      w[e] = (uint32_t)vs[k0][d] | ((uint32_t)vs[k1][d] << 16);
+    }
+    u32x4 x = {w[0], w[1], w[2], w[3]};
+    *(u32x4*)(img + Img<D>::v_off(d, piece)) = x;
+  }
+}
+
+// Work of every item (real query-key token pairs), its LPT sort key, and the
+// reset of the queue counters.  cost < 2^32: a block holds at most 256 tokens
+// and L < 2^24.  key = cost << 32 | ~item: descending keys give descending
+// cost, ties to the lower item id.
+__global__ __launch_bounds__(256) void cost_kernel(const uint32_t* __restrict__ mask, const int32_t* __restrict__ cnt,
+                                                   int N, int words, int n_items, uint64_t* __restrict__ keys,
+                                                   uint32_t* __restrict__ rank, uint32_t* __restrict__ qctr) {
+  const int item = blockIdx.x * blockDim.x + threadIdx.x;
+  if (item < NXCD) qctr[item] = 0u;
+  if (item >= n_items) return;
   const uint32_t* row = mask + (int64_t)item * words;
   uint32_t kv = 0;
   for (int w = 0; w < words; ++w) {
     uint32_t bits = row[w];
     const int rem = N - w * 32;
-    if (rem < 32) bits &= (1u << rem) - 1u;  // ignore bits of blocks >= N
+    if (rem < 32) bits &= (1u << rem) - 1u;
     while (bits) {
       const int j = w * 32 + __builtin_ctz(bits);
       bits &= bits - 1u;
@@ -470,8 +613,62 @@ __global__ __launch_bounds__(256) void cost_kernel(const uint32_t* __restrict__ 
   rank[item] = 0u;
 }
 
-// rank[a] += #{b in this tile : key[b] > key[a]}  (keys are distinct)
-__global__ __launch_bounds__(256) void rank_kernel(const uint64_t* __restrict__ keys, int n_items,
+// Heads to XCDs, longest first (single workgroup).  Head cost = sum of its
+// items' costs; heads are taken in descending cost (ties: lower head) and
+// each goes to the XCD with the least assigned cost (ties: lower XCD).
+// Writes each head's first position in the order array and the queue
+// segments qoff[0..NXCD].  NAIVE puts every head on queue 0 in head order.
+__global__ __launch_bounds__(256) void head_plan_kernel(const uint64_t* __restrict__ keys, int N, int BH, bool lpt,
+                                                        int32_t* __restrict__ head_pos, int32_t* __restrict__ qoff) {
+  extern __shared__ uint64_t hsh[];  // [BH] head costs, then [BH] int32 order
+  uint64_t* hcost = hsh;
+  int32_t* horder = (int32_t*)(hsh + BH);
+  for (int x = threadIdx.x; x < BH; x += blockDim.x) {
+    uint64_t s = 0;
+    if (lpt)
+      for (int i = 0; i < N; ++i) s += keys[(int64_t)x * N + i] >> 32;
+    hcost[x] = s;
+  }
+  __syncthreads();
+  for (int x = threadIdx.x; x < BH; x += blockDim.x) {
+    int r = 0;
+    for (int y = 0; y < BH; ++y)
+      if (hcost[y] > hcost[x] || (hcost[y] == hcost[x] && y < x)) ++r;
+    horder[r] = x;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint64_t load[NXCD];
+    int nh[NXCD], pos[NXCD];
+    for (int x = 0; x < NXCD; ++x) load[x] = 0, nh[x] = 0;
+    for (int r = 0; r < BH; ++r) {
+      const int hd = horder[r];
+      int best = 0;
+      if (lpt)
+        for (int x = 1; x < NXCD; ++x)
+          if (load[x] < load[best]) best = x;
+      load[best] += hcost[hd];
+      nh[best]++;
+      head_pos[hd] = best;  // XCD for now
+    }
+    int off = 0;
+    for (int x = 0; x < NXCD; ++x) {
+      qoff[x] = off;
+      pos[x] = off;
+      off += nh[x] * N;
+    }
+    qoff[NXCD] = off;
+    for (int r = 0; r < BH; ++r) {
+      const int hd = horder[r];
+      const int x = head_pos[hd];
+      head_pos[hd] = pos[x];
+      pos[x] += N;
+    }
+  }
+}
+
+// rank[a] += #{b in this tile of a's head : key[b] > key[a]}  (keys distinct)
+__global__ __launch_bounds__(256) void rank_kernel(const uint64_t* __restrict__ keys, int n_items, int N,
                                                    uint32_t* __restrict__ rank) {
   __shared__ uint64_t tile[2048];
   const int a = blockIdx.x * 256 + threadIdx.x;
@@ -481,15 +678,20 @@ __global__ __launch_bounds__(256) void rank_kernel(const uint64_t* __restrict__ 
   __syncthreads();
   if (a >= n_items) return;
   const uint64_t ka = keys[a];
+  const int head = a / N;
+  const int lo = max(0, head * N - b0), hi_ = min(nb, (head + 1) * N - b0);
   uint32_t c = 0;
-  for (int t = 0; t < nb; ++t) c += tile[t] > ka ? 1u : 0u;
+  for (int t = lo; t < hi_; ++t) c += tile[t] > ka ? 1u : 0u;
   if (c) atomicAdd(&rank[a], c);
 }
 
-__global__ __launch_bounds__(256) void scatter_kernel(const uint32_t* __restrict__ rank, int n_items,
-                                                      int32_t* __restrict__ order) {
+__global__ __launch_bounds__(256) void scatter_kernel(const uint32_t* __restrict__ rank,
+                                                      const int32_t* __restrict__ head_pos, int n_items, int N,
+                                                      bool lpt, int32_t* __restrict__ order) {
   const int a = blockIdx.x * 256 + threadIdx.x;
-  if (a < n_items) order[rank[a]] = a;
+  if (a >= n_items) return;
+  const int within = lpt ? (int)rank[a] : a % N;
+  order[head_pos[a / N] + within] = a;
 }
 
 // ---------------------------------------------------------------------------
@@ -500,6 +702,10 @@ int attn_waves_for_block(int vol) {
   if (vol <= 128) return 4;
   return 8;
 }
+
+int attn_chunks_per_block(int vol) { return (vol + KCH - 1) / KCH; }
+
+size_t attn_tile_bytes(int D, int64_t slots) { return (size_t)slots * 2 * KCH * D * sizeof(bf16_bits); }
 
 template <int D, int WAVES, bool DENSE>
 static const void* kernel_ptr() {
@@ -537,19 +743,31 @@ static void launch_sparse_t(const AttnParams& prm, int grid, hipStream_t st) {
 
 hipError_t launch_sparse_attn(const AttnLaunch& a, bool lpt, hipStream_t st) {
   const int n_items = a.B * a.heads * a.g.N;
+  const int BH = a.B * a.heads;
   const int words = (a.g.N + 31) / 32;
+  const int vol = a.g.bt * a.g.bh * a.g.bw;
+  const int cpb = attn_chunks_per_block(vol);
   hipLaunchKernelGGL(layout_kernel, dim3(a.g.N), dim3(256), 0, st, a.g, a.tok, a.blk_cnt);
+  const unsigned slots = (unsigned)(BH * a.g.N * cpb);
+  if (a.D == 128)
+    hipLaunchKernelGGL(tile_kernel<128>, dim3(slots), dim3(256), 0, st, (const bf16_bits*)a.k, (const bf16_bits*)a.v,
+                       a.tok, a.g, a.L, a.heads, cpb, a.tiles);
+  else
+    hipLaunchKernelGGL(tile_kernel<64>, dim3(slots), dim3(256), 0, st, (const bf16_bits*)a.k, (const bf16_bits*)a.v,
+                       a.tok, a.g, a.L, a.heads, cpb, a.tiles);
   hipLaunchKernelGGL(cost_kernel, dim3((n_items + 255) / 256), dim3(256), 0, st, a.mask, a.blk_cnt, a.g.N, words,
-                     n_items, lpt, a.keys, a.rank, a.order, a.queue);
-  if (lpt) {
+                     n_items, a.keys, a.rank, a.qctr);
+  hipLaunchKernelGGL(head_plan_kernel, dim3(1), dim3(256), (size_t)BH * 12, st, a.keys, a.g.N, BH, lpt, a.head_pos,
+                     a.qoff);
+  if (lpt)
     hipLaunchKernelGGL(rank_kernel, dim3((n_items + 255) / 256, (n_items + 2047) / 2048), dim3(256), 0, st, a.keys,
-                       n_items, a.rank);
-    hipLaunchKernelGGL(scatter_kernel, dim3((n_items + 255) / 256), dim3(256), 0, st, a.rank, n_items, a.order);
-  }
+                       n_items, a.g.N, a.rank);
+  hipLaunchKernelGGL(scatter_kernel, dim3((n_items + 255) / 256), dim3(256), 0, st, a.rank, a.head_pos, n_items,
+                     a.g.N, lpt, a.order);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  AttnParams prm;
+  AttnParams prm = {};
   prm.q = (const bf16_bits*)a.q;
   prm.k = (const bf16_bits*)a.k;
   prm.v = (const bf16_bits*)a.v;
@@ -559,16 +777,18 @@ hipError_t launch_sparse_attn(const AttnLaunch& a, bool lpt, hipStream_t st) {
   prm.heads = a.heads;
   prm.g = a.g;
   prm.words = words;
+  prm.cpb = cpb;
   prm.mask = a.mask;
   prm.tok = a.tok;
+  prm.tiles = a.tiles;
   prm.order = a.order;
-  prm.queue = a.queue;
+  prm.qoff = a.qoff;
+  prm.qctr = a.qctr;
   prm.n_items = n_items;
-  prm.q_tiles = 0;
   prm.scale_log2 = a.scale * 1.4426950408889634f;
   prm.trace = a.trace;
 
-  const int waves = attn_waves_for_block(a.g.bt * a.g.bh * a.g.bw);
+  const int waves = attn_waves_for_block(vol);
   int err = 0;
   const int grid = attn_persistent_workgroups(a.D, waves, &err);
   if (err) return hipErrorInvalidValue;
@@ -599,7 +819,7 @@ hipError_t launch_dense_attn(const void* q, const void* k, const void* v, void* 
   prm.n_items = B * heads * prm.q_tiles;
   prm.scale_log2 = scale * 1.4426950408889634f;
   prm.trace = nullptr;
-  const int grid = 8 * ((prm.n_items + 7) / 8);
+  const int grid = NXCD * ((prm.n_items + NXCD - 1) / NXCD);
   if (D == 128)
     hipLaunchKernelGGL((attn_kernel<128, WAVES, true>), dim3(grid), dim3(WAVES * 64), 0, st, prm);
   else

@@ -27,16 +27,23 @@ struct AttnLaunch {
   float scale;
   uint64_t* trace;
   // workspace views
-  int32_t* tok;
-  int32_t* blk_cnt;
-  uint64_t* keys;
-  uint32_t* rank;
-  int32_t* order;
-  uint32_t* queue;
+  int32_t* tok;        // [L] block-ordered token ids
+  int32_t* blk_cnt;    // [N] real tokens per block
+  uint16_t* tiles;     // [B*heads*N*chunks_per_block] chunk images of K and V
+  uint64_t* keys;      // [items] cost << 32 | ~item
+  uint32_t* rank;      // [items] rank inside the item's head
+  int32_t* order;      // [items] queue contents
+  int32_t* head_pos;   // [B*heads] first order slot of each head
+  int32_t* qoff;       // [9] queue segments (one per XCD)
+  uint32_t* qctr;      // [8] queue pop counters
 };
 
-// Query rows per work item for a block volume (32, 64, 128 or 256 rows).
+// Wavefronts per work item for a block volume (32, 64, 128 or 256 rows).
 int attn_waves_for_block(int block_volume);
+// 64-key chunk slots reserved per block.
+int attn_chunks_per_block(int block_volume);
+// Bytes of the chunk images for a number of slots.
+size_t attn_tile_bytes(int D, int64_t slots);
 // Persistent workgroups for a (D, waves) variant on the current device.
 int attn_persistent_workgroups(int D, int waves, int* err);
 hipError_t launch_sparse_attn(const AttnLaunch& a, bool lpt, hipStream_t st);

@@ -77,8 +77,12 @@ typedef struct {
 } fva_route_cfg;
 
 /* Schedules of the persistent attention kernel. */
-#define FVA_SCHED_LPT 0   /* work items in descending order of real token pairs */
-#define FVA_SCHED_NAIVE 1 /* work items in (batch, head, query block) order */
+/* LPT: heads go longest-first (summed real token pairs) to one queue per XCD;
+ * each queue holds its heads' items in descending real token pairs; an idle
+ * workgroup takes from its own XCD's queue first, then from the others.
+ * NAIVE: one queue in (batch, head, query block) order. */
+#define FVA_SCHED_LPT 0
+#define FVA_SCHED_NAIVE 1
 
 /* Number of blocks prod ceil(dim/block) (VSA guide, section 3), or -1 when a
  * dimension is not positive.  Host only. */
@@ -88,8 +92,10 @@ int32_t fva_num_blocks(const fva_grid* grid);
  * fp64), or 0 for invalid arguments.  Host only. */
 size_t fva_route_workspace_bytes(const fva_desc* desc, const fva_grid* grid);
 
-/* Device workspace fva_sparse_attn needs (block-ordered token table, work
- * item costs, ranks, order and queue counter), or 0 for invalid arguments. */
+/* Device workspace fva_sparse_attn needs, or 0 for invalid arguments: the
+ * block-ordered token table, the K and V of every (b, h, block) re-tiled into
+ * 64-key chunk images (about 2*B*L*heads*D*2 bytes plus ragged-block padding),
+ * work item costs, ranks, order and the per-XCD queues. */
 size_t fva_attn_workspace_bytes(const fva_desc* desc, const fva_grid* grid);
 
 /* Number of persistent workgroups fva_sparse_attn launches on the current
@@ -133,7 +139,8 @@ fva_status fva_route(const void* q, const void* k, const fva_desc* desc, const f
  *            workgroup first-item start, last-item end, summed item time
  *            (100 MHz ticks) and (items << 40 | xcc_id << 32 | hw_id)
  *   ws       device workspace of at least fva_attn_workspace_bytes()
- * Errors: INVALID_ARG, SHAPE, SCALE, UNSUPPORTED, WORKSPACE, DEVICE. */
+ * Errors: INVALID_ARG, SHAPE, SCALE, UNSUPPORTED (also B*heads > 4096),
+ * WORKSPACE, DEVICE. */
 fva_status fva_sparse_attn(const void* q, const void* k, const void* v, void* o, const fva_desc* desc,
                            const fva_grid* grid, const uint32_t* mask, float scale, int32_t sched, uint64_t* trace,
                            void* ws, size_t ws_bytes, void* stream);
