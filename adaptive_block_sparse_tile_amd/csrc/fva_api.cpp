@@ -162,7 +162,7 @@ int32_t fva_attn_workgroups(const fva_desc* desc, const fva_grid* grid) {
   fva::Geo g;
   if (check_desc(desc) != FVA_OK || check_grid(desc, grid, &g) != FVA_OK) return -1;
   int err = 0;
-  const int n = fva::attn_persistent_workgroups(desc->D, fva::attn_waves_for_block(g.bt * g.bh * g.bw), &err);
+  const int n = fva::attn_persistent_workgroups(desc->D, g.bt * g.bh * g.bw, &err);
   return err ? -1 : n;
 }
 

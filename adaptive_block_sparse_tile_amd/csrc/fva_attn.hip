@@ -15,11 +15,12 @@
 // and a workgroup whose queue is empty takes items from the other XCDs.
 //
 // Attention kernel (one work item = the real rows of one query block):
-//   - WAVES wavefronts, each owning 32 query rows held in registers as the B
-//     operand of v_mfma_f32_32x32x16_bf16;
-//   - chunks of 64 keys stream through a 3-stage LDS ring; a chunk's image is
-//     K [64][D] followed by V^T [D][64], 16-byte pieces XOR-swizzled by row so
-//     the MFMA operand reads of 32 rows hit distinct banks;
+//   - WAVES wavefronts, each owning QT sub-tiles of 32 query rows held in
+//     registers as B operands of v_mfma_f32_32x32x16_bf16, so each K or V^T
+//     operand read from LDS feeds QT MFMAs;
+//   - chunks of 64 keys stream through a 3-stage LDS ring; a chunk is K
+//     [64][D] followed by V^T [D][64], rows padded so the MFMA operand reads of
+//     16-lane groups hit distinct banks;
 //   - S^T = K Q^T gives each lane one query column, so the softmax row
 //     statistics need one cross-half lane swap per chunk, and the bf16
 //     probabilities feed O^T += V^T P^T from registers;
@@ -36,16 +37,34 @@ constexpr int KCH = 64;     // keys per chunk
 constexpr int STAGES = 3;   // LDS ring depth
 constexpr int NXCD = 8;     // XCDs of an MI355X
 
-// Byte image of one chunk in LDS and in the tiled copy.
+// A chunk's image in the tiled copy (compact): K [64][D] row-major, then
+// V^T [D][64] with key positions permuted by pi.
 template <int D>
 struct Img {
   static constexpr int KELEMS = KCH * D;
   static constexpr int ELEMS = 2 * KCH * D;
-  static constexpr int KSW = (D / 8 >= 16) ? 15 : (D / 8 - 1);
-  // K element (row, 8*piece + e)
-  __host__ __device__ static int k_off(int row, int piece) { return row * D + ((piece ^ (row & KSW)) << 3); }
-  // V^T element (d, 8*piece + e), position-ordered keys
-  __host__ __device__ static int v_off(int d, int piece) { return KELEMS + d * KCH + ((piece ^ (d & 7)) << 3); }
+};
+
+// The same chunk in LDS: every row padded by 16 bytes (K rows D+8, V^T rows
+// 64+8 elements).  Rows 16 bytes apart in bank order make the 16-byte operand
+// reads of 16 consecutive rows hit distinct banks (272 = 17*16 and
+// 144 = 9*16, both odd multiples of 16 bytes), and each operand address is a
+// per-lane base plus a compile-time offset.
+template <int D>
+struct Lds {
+  static constexpr int KROW = D + 8;
+  static constexpr int VROW = KCH + 8;
+  static constexpr int VBASE = KCH * KROW;
+  static constexpr int ELEMS = KCH * KROW + D * VROW;
+  __host__ __device__ static constexpr int k_off(int row, int col) { return row * KROW + col; }
+  __host__ __device__ static constexpr int v_off(int d, int pos) { return VBASE + d * VROW + pos; }
+  // element offset in LDS of the 16-byte piece s of the compact image
+  __host__ __device__ static int piece_off(int s) {
+    constexpr int KP = KCH * D / 8;
+    if (s < KP) return k_off(s / (D / 8), (s % (D / 8)) * 8);
+    s -= KP;
+    return v_off(s / 8, (s % 8) * 8);
+  }
 };
 
 // Key k of a chunk sits at V^T position pi(k): inside each group of 16 keys,
@@ -154,32 +173,35 @@ struct KvIter {
 template <int D, int THREADS, bool DENSE>
 struct Stager;
 
-// Sparse: the chunk image is contiguous; a linear copy.
+// Sparse: the chunk image is contiguous; a linear copy, staged in two halves
+// (part 0 = the K image, part 1 = the V^T image) so only half a chunk is held
+// in registers at a time.
 template <int D, int THREADS>
 struct Stager<D, THREADS, false> {
   static constexpr int N16 = Img<D>::ELEMS * 2 / 16;  // 16-byte pieces per image
-  static constexpr int PER = (N16 + THREADS - 1) / THREADS;
+  static constexpr int HALF = N16 / 2;
+  static constexpr int PER = (HALF + THREADS - 1) / THREADS;
   u32x4 r[PER];
 
-  __device__ void load(const AttnParams& p, int64_t, int64_t, Chunk ck) {
-    const u32x4* src = (const u32x4*)(p.tiles + (int64_t)ck.slot * Img<D>::ELEMS);
+  __device__ void load(const AttnParams& p, int64_t, int64_t, Chunk ck, int part) {
+    const u32x4* src = (const u32x4*)(p.tiles + (int64_t)ck.slot * Img<D>::ELEMS) + part * HALF;
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int s = threadIdx.x + u * THREADS;
-      if (N16 % THREADS == 0 || s < N16) r[u] = src[s];
+      if (HALF % THREADS == 0 || s < HALF) r[u] = src[s];
     }
   }
-  __device__ void store(bf16_bits* img) const {
-    u32x4* dst = (u32x4*)img;
+  __device__ void store(bf16_bits* lds, int part) const {
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int s = threadIdx.x + u * THREADS;
-      if (N16 % THREADS == 0 || s < N16) dst[s] = r[u];
+      if (HALF % THREADS == 0 || s < HALF) *(u32x4*)(lds + Lds<D>::piece_off(part * HALF + s)) = r[u];
     }
   }
 };
 
 // Dense: 64 consecutive tokens of BSHD K and V; V is transposed on the way.
+// Part 0 stages K, part 1 stages V.
 template <int D, int THREADS>
 struct Stager<D, THREADS, true> {
   static constexpr int KP = KCH * D / 8;  // (row, piece) pairs of K
@@ -189,10 +211,11 @@ struct Stager<D, THREADS, true> {
   u32x4 kr[KPER];
   uint32_t vr[VPER][8];
 
-  __device__ void load(const AttnParams& p, int64_t head_off, int64_t rs, Chunk ck) {
+  __device__ void load(const AttnParams& p, int64_t head_off, int64_t rs, Chunk ck, int part) {
     const bf16_bits* kb = p.k + head_off + (int64_t)ck.slot * rs;
     const bf16_bits* vb = p.v + head_off + (int64_t)ck.slot * rs;
     const bool full = ck.valid == KCH;
+    if (part == 0) {
 #pragma unroll
     for (int u = 0; u < KPER; ++u) {
       const int s = threadIdx.x + u * THREADS;
@@ -200,6 +223,8 @@ struct Stager<D, THREADS, true> {
       u32x4 x = {0u, 0u, 0u, 0u};
       if ((KP % THREADS == 0 || s < KP) && (full || row < ck.valid)) x = *(const u32x4*)(kb + row * rs + piece * 8);
       kr[u] = x;
+    }
+      return;
     }
 #pragma unroll
     for (int u = 0; u < VPER; ++u) {
@@ -214,14 +239,17 @@ struct Stager<D, THREADS, true> {
       }
     }
   }
-  __device__ void store(bf16_bits* img) const {
+  __device__ void store(bf16_bits* img, int part) const {
+    if (part == 0) {
 #pragma unroll
-    for (int u = 0; u < KPER; ++u) {
-      const int s = threadIdx.x + u * THREADS;
-      if (KP % THREADS == 0 || s < KP) {
-        const int row = s / (D / 8), piece = s % (D / 8);
-        *(u32x4*)(img + Img<D>::k_off(row, piece)) = kr[u];
+      for (int u = 0; u < KPER; ++u) {
+        const int s = threadIdx.x + u * THREADS;
+        if (KP % THREADS == 0 || s < KP) {
+          const int row = s / (D / 8), piece = s % (D / 8);
+          *(u32x4*)(img + Lds<D>::k_off(row, piece * 8)) = kr[u];
+        }
       }
+      return;
     }
 #pragma unroll
     for (int u = 0; u < VPER; ++u) {
@@ -241,11 +269,10 @@ struct Stager<D, THREADS, true> {
         hi1[0] = (w[4] >> 16) | (w[5] & 0xffff0000u);
         hi1[1] = (w[6] >> 16) | (w[7] & 0xffff0000u);
         const int d0 = 2 * dp, d1 = 2 * dp + 1;
-        const int pc0 = p0 >> 3, pc1 = (p0 + 8) >> 3, sub = p0 & 7;
-        *(u32x2*)(img + Img<D>::v_off(d0, pc0) + sub) = lo0;
-        *(u32x2*)(img + Img<D>::v_off(d0, pc1) + sub) = lo1;
-        *(u32x2*)(img + Img<D>::v_off(d1, pc0) + sub) = hi0;
-        *(u32x2*)(img + Img<D>::v_off(d1, pc1) + sub) = hi1;
+        *(u32x2*)(img + Lds<D>::v_off(d0, p0)) = lo0;
+        *(u32x2*)(img + Lds<D>::v_off(d0, p0 + 8)) = lo1;
+        *(u32x2*)(img + Lds<D>::v_off(d1, p0)) = hi0;
+        *(u32x2*)(img + Lds<D>::v_off(d1, p0 + 8)) = hi1;
       }
     }
   }
@@ -264,31 +291,18 @@ __device__ inline float swap_halves(float x) {
   return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
 }
 
-// S^T (64 keys x 32 queries) of one chunk.
-template <int D>
-__device__ inline void qk_chunk(const bf16_bits* img, const bf16x8* qf, int lr, int hi, f32x16* s) {
-#pragma unroll
-  for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
-#pragma unroll
-  for (int ds = 0; ds < D / 16; ++ds) {
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const bf16x8 a = *(const bf16x8*)(img + Img<D>::k_off(32 * kt + lr, 2 * ds + hi));
-      s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ds], s[kt], 0, 0, 0);
-    }
-  }
-}
-
-template <int D, int WAVES, bool DENSE>
+// The attention kernel.  A work item is processed by WAVES wavefronts; each
+// owns QT sub-tiles of 32 query rows (rows 32*(QT*wave + qt) + lr of the
+// item) and therefore reuses every K and V^T operand it reads from LDS for QT
+// MFMAs.  Per 64-key chunk and wavefront: 2*D/16 K reads feeding QT MFMAs each
+// (S^T), and 4*D/32 V^T reads feeding QT MFMAs each (O^T).
+template <int D, int WAVES, int QT, bool DENSE>
 __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
   constexpr int THREADS = WAVES * 64;
-  constexpr int QROWS = WAVES * 32;
+  constexpr int QROWS = WAVES * QT * 32;
   constexpr int DS = D / 16;  // 16-wide d steps of Q K^T
   constexpr int DT = D / 32;  // 32-row d tiles of O^T
-  constexpr int IMG = Img<D>::ELEMS;
-  __shared__ __attribute__((aligned(16))) bf16_bits ring[STAGES][IMG];
+  __shared__ __attribute__((aligned(16))) bf16_bits ring[STAGES][Lds<D>::ELEMS];
   __shared__ int item_s;
 
   const int tid = threadIdx.x;
@@ -346,11 +360,13 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
     const int64_t rs = (int64_t)p.heads * D;
     const int64_t head_off = (int64_t)b * p.L * rs + (int64_t)h * D;
 
-    // ---- Q fragment: row 32*wave + lr, d = 16s + 8hi .. +7
-    const int qrow = wave * 32 + lr;
-    const bool wave_active = wave * 32 < qcount;
-    bf16x8 qf[DS];
-    {
+    // ---- Q fragments: sub-tile qt holds row 32*(QT*wave + qt) + lr, d = 16s + 8hi .. +7
+    const int row0 = 32 * QT * wave;
+    const bool wave_active = row0 < qcount;
+    bf16x8 qf[QT][DS];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const int qrow = row0 + 32 * qt + lr;
       const bool ok = qrow < qcount;
       int64_t qtok = 0;
       if (ok) qtok = pos_to_token<DENSE>(p, qbase + qrow);
@@ -358,16 +374,21 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
       for (int s = 0; s < DS; ++s) {
         u32x4 x = {0u, 0u, 0u, 0u};
         if (ok) x = *(const u32x4*)(p.q + head_off + qtok * rs + 16 * s + 8 * hi);
-        qf[s] = __builtin_bit_cast(bf16x8, x);
+        qf[qt][s] = __builtin_bit_cast(bf16x8, x);
       }
     }
 
-    f32x16 acc[DT];
+    f32x16 acc[QT][DT];
+    float m_run[QT], lsum[QT];
 #pragma unroll
-    for (int t = 0; t < DT; ++t)
+    for (int qt = 0; qt < QT; ++qt) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
-    float m_run = -INFINITY, lsum = 0.f;
+      for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[qt][t][r] = 0.f;
+      m_run[qt] = -INFINITY;
+      lsum[qt] = 0.f;
+    }
 
     // ---- pipeline: `it` is the next chunk to load; the ring holds `ready`
     //      loaded chunks starting at stage `cur`, with real key counts v0, v1
@@ -375,108 +396,160 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
     it.template first<DENSE>(p.g, mrow, p.words, p.L, bh, p.cpb);
     Stager<D, THREADS, DENSE> st;
     int ready = 0, v0 = 0, v1 = 0;
-    if (!it.done) {
+    for (int sidx = 0; sidx < 2 && !it.done; ++sidx) {
       const Chunk ck = it.template chunk<DENSE>();
-      st.load(p, head_off, rs, ck);
-      st.store(ring[0]);
-      v0 = ck.valid;
-      ++ready;
-      it.template advance<DENSE>(p.g, bh, p.cpb);
-    }
-    if (!it.done) {
-      const Chunk ck = it.template chunk<DENSE>();
-      st.load(p, head_off, rs, ck);
-      st.store(ring[1]);
-      v1 = ck.valid;
+#pragma unroll
+      for (int part = 0; part < 2; ++part) {
+        st.load(p, head_off, rs, ck, part);
+        st.store(ring[sidx], part);
+      }
+      if (sidx == 0) v0 = ck.valid;
+      else v1 = ck.valid;
       ++ready;
       it.template advance<DENSE>(p.g, bh, p.cpb);
     }
     __syncthreads();
 
-    f32x16 s_cur[2];
-    if (wave_active && ready > 0) qk_chunk<D>(ring[0], qf, lr, hi, s_cur);
-
-    int cur = 0;  // stage of the chunk being finished
-    while (ready > 0) {
-      const int valid = v0;
-      const bool has1 = ready >= 2, has2 = !it.done;
-      const int st1 = cur == STAGES - 1 ? 0 : cur + 1;
-      const int st2 = st1 == STAGES - 1 ? 0 : st1 + 1;
-      int v2 = 0;
-      if (has2) {
-        const Chunk ck = it.template chunk<DENSE>();
-        v2 = ck.valid;
-        st.load(p, head_off, rs, ck);
-      }
-
-      if (wave_active) {
-        // Q K^T of the next chunk, independent of this chunk's softmax
-        f32x16 s_nxt[2];
-        if (has1) qk_chunk<D>(ring[st1], qf, lr, hi, s_nxt);
-
-        // ---- online softmax of this chunk (log2 units); lane holds keys
-        //      32kt + 8(r/4) + 4hi + r%4 of query lr
-        if (valid < KCH) {
+    // The pipeline runs on 32-key halves of the chunks (the online softmax
+    // is exact at any key granularity): while the MFMAs compute S^T of the
+    // next half, the VALU turns the current half into probabilities, then the
+    // current half's P V MFMAs run.  sA and sB hold S^T of a half for each
+    // sub-tile and trade roles every half, so nothing is copied.
+    constexpr int NQK = DS;       // K operand reads per half (one per 16-wide d step)
+    constexpr int NPV = 2 * DT;   // V^T operand reads per half (2 key groups x d tiles)
+    constexpr int AHEAD = 4;
+    constexpr int VPM = 16 / NQK;  // probabilities per sub-tile per Q K^T step
+    f32x16 sA[QT], sB[QT];
+    auto kread_at = [&](const bf16_bits* img, int kt, int ds) -> bf16x8 {
+      return *(const bf16x8*)(img + Lds<D>::k_off(32 * kt + lr, 16 * ds + 8 * hi));
+    };
+    if (wave_active && ready > 0) {
 #pragma unroll
-          for (int kt = 0; kt < 2; ++kt)
+      for (int ds = 0; ds < DS; ++ds) {
+        const bf16x8 a = kread_at(ring[0], 0, ds);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = 32 * kt + 8 * (r >> 2) + 4 * hi + (r & 3);
-              if (key >= valid) s_cur[kt][r] = -INFINITY;
-            }
+        for (int qt = 0; qt < QT; ++qt) {
+          const f32x16 c0 = {};
+          sA[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qt][ds], ds == 0 ? c0 : sA[qt], 0, 0, 0);
         }
-        float mx = s_cur[0][0];
+      }
+    }
+    // K operands of the next Q K^T (its first AHEAD d-steps), read one half ahead
+    bf16x8 kw[AHEAD];
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+    for (int q = 0; q < AHEAD; ++q) kw[q] = kread_at(ring[0], 1, q);
+
+    // One half: keys 32*kt_cur .. +31 of the chunk in LDS image imgv (S^T in
+    // sc, `valid` real keys in the chunk).  S^T of the next half (key half
+    // kt_nxt of image imgk, first operands already in kw) goes to sn; during
+    // the P V part the first operands of the half after that (key half
+    // kt_nn of image imgk2) are read into kw.
+    auto half = [&](f32x16 (&sc)[QT], f32x16 (&sn)[QT], int kt_cur, int valid, const bf16_bits* imgv,
+                    const bf16_bits* imgk, int kt_nxt, const bf16_bits* imgk2, int kt_nn)
+                    __attribute__((always_inline)) {
+      // lane holds keys 32kt_cur + 8(r/4) + 4hi + r%4 of query lr of each sub-tile
+      if (valid < 32 * kt_cur + 32) {
+        const int thr = valid - 32 * kt_cur - 4 * hi;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[kt][r]);
-        mx = fmaxf(mx, swap_halves(mx)) * cl2;
-        if (__any(mx > m_run + 8.0f)) {
-          const float m_new = fmaxf(m_run, mx);
-          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (8 * (r >> 2) + (r & 3) >= thr) sc[qt][r] = -INFINITY;
+      }
+      float mx[QT];
+      bool raise = false;
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        float m = sc[qt][0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) m = fmaxf(m, sc[qt][r]);
+        mx[qt] = fmaxf(m, swap_halves(m)) * cl2;
+        raise = raise || (mx[qt] > m_run[qt] + 8.0f);
+      }
+      if (__any(raise)) {
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+          const float m_new = fmaxf(m_run[qt], mx[qt]);
+          const float alpha = __builtin_amdgcn_exp2f(m_run[qt] - m_new);
 #pragma unroll
           for (int t = 0; t < DT; ++t)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[t][r] *= alpha;
-          lsum *= alpha;
-          m_run = m_new;
-        }
-        const float nm = -m_run;
-        bf16x8 pb[2][2];
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int qh = 0; qh < 2; ++qh) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              pb[kt][qh][e] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[kt][8 * qh + e], cl2, nm));
-            typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-            const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-              const bf16x2_t pr = {pb[kt][qh][e], pb[kt][qh][e + 1]};
-              lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, one, lsum, false);
-            }
-          }
-        // ---- O^T (d x queries) += V^T P^T
-        const bf16_bits* img = ring[cur];
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int qh = 0; qh < 2; ++qh)
-#pragma unroll
-            for (int t = 0; t < DT; ++t) {
-              const bf16x8 a = *(const bf16x8*)(img + Img<D>::v_off(32 * t + lr, 4 * kt + 2 * qh + hi));
-              acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kt][qh], acc[t], 0, 0, 0);
-            }
-        if (has1) {
-          s_cur[0] = s_nxt[0];
-          s_cur[1] = s_nxt[1];
+            for (int r = 0; r < 16; ++r) acc[qt][t][r] *= alpha;
+          lsum[qt] *= alpha;
+          m_run[qt] = m_new;
         }
       }
+      float nm[QT];
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) nm[qt] = -m_run[qt];
 
+      // ---- one basic block in program order (sched_barrier fences)
+      // PV step q: d tile t = q % DT, key group qh = q / DT (keys 32kt_cur + 16qh ..)
+      auto vread = [&](int q) -> bf16x8 {
+        return *(const bf16x8*)(imgv + Lds<D>::v_off(32 * (q % DT) + lr, 32 * kt_cur + 16 * (q / DT) + 8 * hi));
+      };
+      typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+      const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+      bf16x8 pb[2][QT];
+      bf16x8 vw[AHEAD];
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int q = 0; q < NQK; ++q) {
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+          const f32x16 c0 = {};
+          sn[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kw[q % AHEAD], qf[qt][q], q == 0 ? c0 : sn[qt], 0, 0, 0);
+          if (qt == QT - 1) {
+            if (q + AHEAD < NQK) kw[q % AHEAD] = kread_at(imgk, kt_nxt, q + AHEAD);
+            if (q >= NQK - AHEAD) vw[q - (NQK - AHEAD)] = vread(q - (NQK - AHEAD));
+          }
+          // probabilities r = VPM*q .. of sub-tile qt
+#pragma unroll
+          for (int u = 0; u < VPM; ++u) {
+            const int r = VPM * q + u;
+            pb[r >> 3][qt][r & 7] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[qt][r], cl2, nm[qt]));
+          }
+#pragma unroll
+          for (int u = 0; u < VPM; u += 2) {
+            const int r = VPM * q + u;
+            const bf16x2_t pr = {pb[r >> 3][qt][r & 7], pb[r >> 3][qt][(r & 7) + 1]};
+            lsum[qt] = __builtin_amdgcn_fdot2_f32_bf16(pr, one, lsum[qt], false);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < NPV; ++q) {
+        const int t = q % DT, qh = q / DT;
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+          acc[qt][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vw[q % AHEAD], pb[qh][qt], acc[qt][t], 0, 0, 0);
+        if (q + AHEAD < NPV) vw[q % AHEAD] = vread(q + AHEAD);
+        if (q >= NPV - AHEAD) kw[q - (NPV - AHEAD)] = kread_at(imgk2, kt_nn, q - (NPV - AHEAD));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+
+    int cur = 0;  // stage of the chunk being finished
+    Stager<D, THREADS, DENSE> st2k;  // chunk c+2, K image
+    while (ready > 0) {
+      const int valid = v0;
+      const bool has2 = !it.done;
+      const int st1 = cur == STAGES - 1 ? 0 : cur + 1;
+      const int st2 = st1 == STAGES - 1 ? 0 : st1 + 1;
+      Chunk ck2 = {0, 0};
       if (has2) {
-        st.store(ring[st2]);
+        ck2 = it.template chunk<DENSE>();
+        st2k.load(p, head_off, rs, ck2, 0);
+        st.load(p, head_off, rs, ck2, 1);
+      }
+      if (wave_active) {
+        half(sA, sB, 0, valid, ring[cur], ring[cur], 1, ring[st1], 0);
+        half(sB, sA, 1, valid, ring[cur], ring[st1], 0, ring[st1], 1);
+      }
+      if (has2) {
+        st2k.store(ring[st2], 0);
+        st.store(ring[st2], 1);
         ++ready;
         it.template advance<DENSE>(p.g, bh, p.cpb);
       }
@@ -484,26 +557,30 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
       --ready;
       cur = st1;
       v0 = v1;
-      v1 = v2;
+      v1 = ck2.valid;
     }
 
     // ---- normalise and store the real rows (lane and lane ^ 32 share a row)
     if (wave_active) {
-      const float lt = lsum + swap_halves(lsum);
-      if (qrow < qcount) {
-        const float inv = lt > 0.f ? 1.f / lt : 0.f;
-        const int64_t otok = pos_to_token<DENSE>(p, qbase + qrow);
-        bf16_bits* dst = p.o + head_off + otok * rs;
 #pragma unroll
-        for (int t = 0; t < DT; ++t)
+      for (int qt = 0; qt < QT; ++qt) {
+        const float lt = lsum[qt] + swap_halves(lsum[qt]);
+        const int qrow = row0 + 32 * qt + lr;
+        if (qrow < qcount) {
+          const float inv = lt > 0.f ? 1.f / lt : 0.f;
+          const int64_t otok = pos_to_token<DENSE>(p, qbase + qrow);
+          bf16_bits* dst = p.o + head_off + otok * rs;
 #pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-            bf16x4_t w;
+          for (int t = 0; t < DT; ++t)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) w[e] = (__bf16)(acc[t][4 * g4 + e] * inv);
-            *(bf16x4_t*)(dst + 32 * t + 8 * g4 + 4 * hi) = w;
-          }
+            for (int g4 = 0; g4 < 4; ++g4) {
+              typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+              bf16x4_t w;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) w[e] = (__bf16)(acc[qt][t][4 * g4 + e] * inv);
+              *(bf16x4_t*)(dst + 32 * t + 8 * g4 + 4 * hi) = w;
+            }
+        }
       }
     }
     const uint64_t t_end = wall_ticks();
@@ -569,7 +646,7 @@ __global__ __launch_bounds__(256) void tile_kernel(const bf16_bits* __restrict__
       kx = *(const u32x4*)(k + head_off + t * rs + piece * 8);
       vx = *(const u32x4*)(v + head_off + t * rs + piece * 8);
     }
-    *(u32x4*)(img + Img<D>::k_off(row, piece)) = kx;
+    *(u32x4*)(img + row * D + piece * 8) = kx;
     *(u32x4*)&vs[row][piece * 8] = vx;
   }
   __syncthreads();
@@ -582,7 +659,7 @@ __global__ __launch_bounds__(256) void tile_kernel(const bf16_bits* __restrict__
       w[e] = (uint32_t)vs[k0][d] | ((uint32_t)vs[k1][d] << 16);
     }
     u32x4 x = {w[0], w[1], w[2], w[3]};
-    *(u32x4*)(img + Img<D>::v_off(d, piece)) = x;
+    *(u32x4*)(img + Img<D>::KELEMS + d * KCH + piece * 8) = x;
   }
 }
 
@@ -623,11 +700,15 @@ __global__ __launch_bounds__(256) void head_plan_kernel(const uint64_t* __restri
   extern __shared__ uint64_t hsh[];  // [BH] head costs, then [BH] int32 order
   uint64_t* hcost = hsh;
   int32_t* horder = (int32_t*)(hsh + BH);
-  for (int x = threadIdx.x; x < BH; x += blockDim.x) {
+  // one wavefront per head: lanes sum strided items, then a lane reduction
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+  for (int x = wave; x < BH; x += nwaves) {
     uint64_t s = 0;
     if (lpt)
-      for (int i = 0; i < N; ++i) s += keys[(int64_t)x * N + i] >> 32;
-    hcost[x] = s;
+      for (int i = lane; i < N; i += 64) s += keys[(int64_t)x * N + i] >> 32;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+    if (lane == 0) hcost[x] = s;
   }
   __syncthreads();
   for (int x = threadIdx.x; x < BH; x += blockDim.x) {
@@ -697,48 +778,47 @@ __global__ __launch_bounds__(256) void scatter_kernel(const uint32_t* __restrict
 // ---------------------------------------------------------------------------
 // launches
 // ---------------------------------------------------------------------------
-int attn_waves_for_block(int vol) {
-  if (vol <= 64) return 2;
-  if (vol <= 128) return 4;
-  return 8;
-}
+// Kernel shape per block volume: (wavefronts, 32-row sub-tiles per wavefront).
+//   <= 64 rows: 2 x 1;  <= 128: 4 x 1;  <= 256: 8 x 1.
+// One sub-tile per wavefront keeps two wavefronts per SIMD, which hides LDS
+// and exp latency better than one wavefront with two sub-tiles.
+int attn_waves_for_block(int vol) { return vol <= 64 ? 2 : (vol <= 128 ? 4 : 8); }
+static int attn_qt_for_block(int) { return 1; }
 
 int attn_chunks_per_block(int vol) { return (vol + KCH - 1) / KCH; }
 
 size_t attn_tile_bytes(int D, int64_t slots) { return (size_t)slots * 2 * KCH * D * sizeof(bf16_bits); }
 
-template <int D, int WAVES, bool DENSE>
+template <int D, int WAVES, int QT, bool DENSE>
 static const void* kernel_ptr() {
-  return reinterpret_cast<const void*>(&attn_kernel<D, WAVES, DENSE>);
+  return reinterpret_cast<const void*>(&attn_kernel<D, WAVES, QT, DENSE>);
 }
 
-static const void* sparse_kernel(int D, int waves) {
+static const void* sparse_kernel(int D, int vol) {
+  const int waves = attn_waves_for_block(vol), qt = attn_qt_for_block(vol);
+  (void)qt;
   if (D == 128) {
-    if (waves == 2) return kernel_ptr<128, 2, false>();
-    if (waves == 4) return kernel_ptr<128, 4, false>();
-    return kernel_ptr<128, 8, false>();
+    if (waves == 2) return kernel_ptr<128, 2, 1, false>();
+    if (waves == 4) return kernel_ptr<128, 4, 1, false>();
+    return kernel_ptr<128, 8, 1, false>();
   }
-  if (waves == 2) return kernel_ptr<64, 2, false>();
-  if (waves == 4) return kernel_ptr<64, 4, false>();
-  return kernel_ptr<64, 8, false>();
+  if (waves == 2) return kernel_ptr<64, 2, 1, false>();
+  if (waves == 4) return kernel_ptr<64, 4, 1, false>();
+  return kernel_ptr<64, 8, 1, false>();
 }
 
-int attn_persistent_workgroups(int D, int waves, int* err) {
+int attn_persistent_workgroups(int D, int vol, int* err) {
   int dev = 0, cus = 0, occ = 0;
   *err = 0;
+  const int threads = attn_waves_for_block(vol) * 64;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, sparse_kernel(D, waves), waves * 64, 0) != hipSuccess) {
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, sparse_kernel(D, vol), threads, 0) != hipSuccess) {
     *err = 1;
     return 0;
   }
   if (occ < 1) occ = 1;
   return cus * occ;
-}
-
-template <int D, int WAVES>
-static void launch_sparse_t(const AttnParams& prm, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((attn_kernel<D, WAVES, false>), dim3(grid), dim3(WAVES * 64), 0, st, prm);
 }
 
 hipError_t launch_sparse_attn(const AttnLaunch& a, bool lpt, hipStream_t st) {
@@ -788,25 +868,17 @@ hipError_t launch_sparse_attn(const AttnLaunch& a, bool lpt, hipStream_t st) {
   prm.scale_log2 = a.scale * 1.4426950408889634f;
   prm.trace = a.trace;
 
-  const int waves = attn_waves_for_block(vol);
   int err = 0;
-  const int grid = attn_persistent_workgroups(a.D, waves, &err);
+  const int grid = attn_persistent_workgroups(a.D, vol, &err);
   if (err) return hipErrorInvalidValue;
-  if (a.D == 128) {
-    if (waves == 2) launch_sparse_t<128, 2>(prm, grid, st);
-    else if (waves == 4) launch_sparse_t<128, 4>(prm, grid, st);
-    else launch_sparse_t<128, 8>(prm, grid, st);
-  } else {
-    if (waves == 2) launch_sparse_t<64, 2>(prm, grid, st);
-    else if (waves == 4) launch_sparse_t<64, 4>(prm, grid, st);
-    else launch_sparse_t<64, 8>(prm, grid, st);
-  }
-  return hipGetLastError();
+  const void* k = sparse_kernel(a.D, vol);
+  void* args[] = {&prm};
+  return hipLaunchKernel(k, dim3(grid), dim3(attn_waves_for_block(vol) * 64), args, 0, st);
 }
 
 hipError_t launch_dense_attn(const void* q, const void* k, const void* v, void* o, int B, int L, int heads, int D,
                              float scale, hipStream_t st) {
-  constexpr int WAVES = 8;
+  constexpr int WAVES = 8, QT = 1;
   AttnParams prm = {};
   prm.q = (const bf16_bits*)q;
   prm.k = (const bf16_bits*)k;
@@ -815,15 +887,15 @@ hipError_t launch_dense_attn(const void* q, const void* k, const void* v, void* 
   prm.B = B;
   prm.L = L;
   prm.heads = heads;
-  prm.q_tiles = (L + WAVES * 32 - 1) / (WAVES * 32);
+  prm.q_tiles = (L + WAVES * QT * 32 - 1) / (WAVES * QT * 32);
   prm.n_items = B * heads * prm.q_tiles;
   prm.scale_log2 = scale * 1.4426950408889634f;
   prm.trace = nullptr;
   const int grid = NXCD * ((prm.n_items + NXCD - 1) / NXCD);
   if (D == 128)
-    hipLaunchKernelGGL((attn_kernel<128, WAVES, true>), dim3(grid), dim3(WAVES * 64), 0, st, prm);
+    hipLaunchKernelGGL((attn_kernel<128, WAVES, QT, true>), dim3(grid), dim3(WAVES * 64), 0, st, prm);
   else
-    hipLaunchKernelGGL((attn_kernel<64, WAVES, true>), dim3(grid), dim3(WAVES * 64), 0, st, prm);
+    hipLaunchKernelGGL((attn_kernel<64, WAVES, QT, true>), dim3(grid), dim3(WAVES * 64), 0, st, prm);
   return hipGetLastError();
 }
 

@@ -38,14 +38,15 @@ struct AttnLaunch {
   uint32_t* qctr;      // [8] queue pop counters
 };
 
-// Wavefronts per work item for a block volume (32, 64, 128 or 256 rows).
+// Wavefronts per work item for a block volume.
 int attn_waves_for_block(int block_volume);
 // 64-key chunk slots reserved per block.
 int attn_chunks_per_block(int block_volume);
 // Bytes of the chunk images for a number of slots.
 size_t attn_tile_bytes(int D, int64_t slots);
-// Persistent workgroups for a (D, waves) variant on the current device.
-int attn_persistent_workgroups(int D, int waves, int* err);
+// Persistent workgroups of the sparse kernel for (D, block volume) on the
+// current device.
+int attn_persistent_workgroups(int D, int block_volume, int* err);
 hipError_t launch_sparse_attn(const AttnLaunch& a, bool lpt, hipStream_t st);
 hipError_t launch_dense_attn(const void* q, const void* k, const void* v, void* o, int B, int L, int heads, int D,
                              float scale, hipStream_t st);
