@@ -38,7 +38,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--oracle-items", type=int, default=48, help="work items in the CPU oracle sample")
     ap.add_argument("--no-dense", action="store_true", help="skip timing the dense reference")
-    ap.add_argument("--traffic", default=None, help="JSON file with rocprofv3 FETCH/WRITE per attention launch")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only copy 2 GiB device-to-device three times (reference for rocprofv3 FETCH/WRITE_SIZE)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -47,6 +48,16 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.calibrate_copy:
+        n = 2 << 30
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_per_launch": n}))
+        return
 
     import adaptive_block_sparse_tile_amd as fva
     import fvgen
@@ -141,10 +152,7 @@ def main():
         busy, finish, ncu = fva.trace_imbalance(tr.cpu().numpy())
         imb[sched] = {"busy_max_over_mean": round(busy, 4), "finish_max_over_mean": round(finish, 4), "cus": ncu}
 
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        with open(args.traffic) as f:
-            traffic = json.load(f).get("bytes_per_launch")
+    traffic = _profiled_traffic(wl.name)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -192,6 +200,26 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
+
+
+def _profiled_traffic(workload: str):
+    """HBM bytes per launch of the sparse attention kernel from the committed
+    rocprofv3 summary, or None if it was taken on another version of the
+    kernel source (or another workload)."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", "attn_%s_traffic.md" % workload)
+    src = os.path.join(ROOT, "adaptive_block_sparse_tile_amd", "csrc", "fva_attn.hip")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes:
+        return None
+    if hashlib.sha256(open(src, "rb").read()).hexdigest() != m_hash.group(1):
+        return None
+    return float(m_bytes.group(1))
 
 
 def _block_counts(wl):
