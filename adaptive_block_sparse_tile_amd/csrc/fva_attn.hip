@@ -88,27 +88,46 @@ struct AttnParams {
   uint32_t* qctr;          // [NXCD] pop counters (sparse)
   int n_items;
   int q_tiles;  // dense: query tiles per (b, h)
+  // sparse work items are groups of up to 4 query blocks: a (gt, gh, gw) box
+  // of blocks on the block grid, gT x gH x gW groups per (b, h); each member
+  // block gets wpb wavefronts
+  int gt, gh, gw, gT, gH, gW, n_groups, wpb;
   float scale_log2;
   uint64_t* trace;
 };
+
+// Block index of member k of group gid, or -1 past the grid's edge.
+__device__ inline int group_member(const AttnParams& p, int gid, int k) {
+  const int gwi = gid % p.gW, ghi = (gid / p.gW) % p.gH, gti = gid / (p.gW * p.gH);
+  const int c = k % p.gw, b = (k / p.gw) % p.gh, a = k / (p.gw * p.gh);
+  const int it = gti * p.gt + a, ih = ghi * p.gh + b, iw = gwi * p.gw + c;
+  if (it >= p.g.nT || ih >= p.g.nH || iw >= p.g.nW) return -1;
+  return (it * p.g.nH + ih) * p.g.nW + iw;
+}
 
 // One chunk of a work item's key sequence.
 struct Chunk {
   int slot;   // sparse: chunk image index; dense: first token
   int valid;  // real keys in the chunk (1..64)
+  int blk;    // sparse: key block of the chunk
 };
 
-// Walks the chunks of one work item: the set bits of the item's mask row in
-// ascending block order (sparse) or the whole sequence (dense).  Every thread
-// of the workgroup holds the same state.
+// Walks the chunks of one work item: the set bits of the union of its (up to
+// NR) member blocks' mask rows in ascending block order (sparse) or the whole
+// sequence (dense).  Every thread of the workgroup holds the same state.
+template <int NR>
 struct KvIter {
-  const uint32_t* mrow;
-  int w, words, c, nch, count, slot0;
+  const uint32_t* rows[NR];
+  int nrows;
+  int w, words, c, nch, count, slot0, blk;
   uint32_t bits;
   bool done;
 
   __device__ uint32_t load_word(const Geo& g, int wi) const {
-    uint32_t x = mrow[wi];
+    uint32_t x = rows[0][wi];
+#pragma unroll
+    for (int r = 1; r < NR; ++r)
+      if (r < nrows) x |= rows[r][wi];
     const int rem = g.N - wi * 32;
     if (rem < 32) x &= (1u << rem) - 1u;  // bits of blocks >= N are not blocks
     return x;
@@ -122,27 +141,31 @@ struct KvIter {
       }
       bits = load_word(g, w);
     }
-    const int j = w * 32 + __builtin_ctz(bits);
+    blk = w * 32 + __builtin_ctz(bits);
     bits &= bits - 1u;
-    count = block_box(g, j).count;
+    count = block_box(g, blk).count;
     nch = (count + KCH - 1) / KCH;
-    slot0 = (bh * g.N + j) * cpb;
+    slot0 = (bh * g.N + blk) * cpb;
     c = 0;
   }
 
   template <bool DENSE>
-  __device__ void first(const Geo& g, const uint32_t* row, int nwords, int L, int bh, int cpb) {
+  __device__ void first(const Geo& g, int nwords, int L, int bh, int cpb) {
     done = false;
     c = 0;
+    blk = -1;
     if (DENSE) {
       count = L;
       nch = (L + KCH - 1) / KCH;
       slot0 = 0;
       return;
     }
-    mrow = row;
     words = nwords;
     w = 0;
+    if (nrows == 0) {
+      done = true;
+      return;
+    }
     bits = load_word(g, 0);
     next_block(g, bh, cpb);
   }
@@ -165,6 +188,7 @@ struct KvIter {
     Chunk ck;
     ck.slot = DENSE ? c * KCH : slot0 + c;
     ck.valid = min(KCH, count - c * KCH);
+    ck.blk = blk;
     return ck;
   }
 };
@@ -296,8 +320,12 @@ __device__ inline float swap_halves(float x) {
 // item) and therefore reuses every K and V^T operand it reads from LDS for QT
 // MFMAs.  Per 64-key chunk and wavefront: 2*D/16 K reads feeding QT MFMAs each
 // (S^T), and 4*D/32 V^T reads feeding QT MFMAs each (O^T).
-template <int D, int WAVES, int QT, bool DENSE>
+//
+// GRP: work items are groups of query blocks (p.wpb wavefronts per block).
+template <int D, int WAVES, int QT, bool DENSE, bool GRP>
 __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
+  static_assert(!(DENSE && GRP), "dense items are query tiles");
+  constexpr int NR = GRP ? 4 : 1;
   constexpr int THREADS = WAVES * 64;
   constexpr int QROWS = WAVES * QT * 32;
   constexpr int DS = D / 16;  // 16-wide d steps of Q K^T
@@ -340,28 +368,53 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
     }
     const uint64_t t_start = wall_ticks();
 
-    int b, h, bh, qbase, qcount;
-    const uint32_t* mrow = nullptr;
+    int b, h, bh;
+    int qbase, qcount;             // this wavefront's query block: first position, real rows
+    int row0;                      // first row of this wavefront inside that block
+    const uint32_t* my_row = nullptr;  // this wavefront's mask row (sparse)
+    KvIter<NR> it;
+    it.nrows = 0;
     if (DENSE) {
       const int tile = item % p.q_tiles;
       bh = item / p.q_tiles;
       qbase = tile * QROWS;
       qcount = min(QROWS, p.L - qbase);
-    } else {
-      const int i = item % p.g.N;
+      row0 = 32 * QT * wave;
+    } else if (!GRP) {
+      const int n = item % p.g.N;
       bh = item / p.g.N;
-      const Box bx = block_box(p.g, i);
+      it.rows[0] = p.mask + ((int64_t)bh * p.g.N + n) * p.words;
+      it.nrows = 1;
+      const Box bx = block_box(p.g, n);
       qbase = bx.start;
       qcount = bx.count;
-      mrow = p.mask + (int64_t)item * p.words;
+      row0 = 32 * QT * wave;
+    } else {
+      const int gid = item % p.n_groups;
+      bh = item / p.n_groups;
+      const int ng = p.gt * p.gh * p.gw;
+      for (int k = 0; k < ng; ++k) {
+        const int n = group_member(p, gid, k);
+        if (n >= 0) it.rows[it.nrows++] = p.mask + ((int64_t)bh * p.g.N + n) * p.words;
+      }
+      const int mine = group_member(p, gid, wave / p.wpb);
+      row0 = 32 * QT * (wave % p.wpb);
+      if (mine >= 0) {
+        const Box bx = block_box(p.g, mine);
+        qbase = bx.start;
+        qcount = bx.count;
+        my_row = p.mask + ((int64_t)bh * p.g.N + mine) * p.words;
+      } else {
+        qbase = 0;
+        qcount = 0;
+      }
     }
     h = bh % p.heads;
     b = bh / p.heads;
     const int64_t rs = (int64_t)p.heads * D;
     const int64_t head_off = (int64_t)b * p.L * rs + (int64_t)h * D;
 
-    // ---- Q fragments: sub-tile qt holds row 32*(QT*wave + qt) + lr, d = 16s + 8hi .. +7
-    const int row0 = 32 * QT * wave;
+    // ---- Q fragments: sub-tile qt holds row row0 + 32*qt + lr of the block, d = 16s + 8hi .. +7
     const bool wave_active = row0 < qcount;
     bf16x8 qf[QT][DS];
 #pragma unroll
@@ -392,9 +445,15 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
 
     // ---- pipeline: `it` is the next chunk to load; the ring holds `ready`
     //      loaded chunks starting at stage `cur`, with real key counts v0, v1
-    KvIter it;
-    it.template first<DENSE>(p.g, mrow, p.words, p.L, bh, p.cpb);
+    it.template first<DENSE>(p.g, p.words, p.L, bh, p.cpb);
     Stager<D, THREADS, DENSE> st;
+    // real keys of the chunks in the ring as this wavefront sees them: a key
+    // block its own query block did not keep counts as 0 real keys
+    auto seen = [&](const Chunk& ck) -> int {
+      if (!GRP) return ck.valid;  // a single member: the union is its own row
+      if (!my_row) return 0;
+      return ((my_row[ck.blk >> 5] >> (ck.blk & 31)) & 1u) ? ck.valid : 0;
+    };
     int ready = 0, v0 = 0, v1 = 0;
     for (int sidx = 0; sidx < 2 && !it.done; ++sidx) {
       const Chunk ck = it.template chunk<DENSE>();
@@ -403,8 +462,8 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
         st.load(p, head_off, rs, ck, part);
         st.store(ring[sidx], part);
       }
-      if (sidx == 0) v0 = ck.valid;
-      else v1 = ck.valid;
+      if (sidx == 0) v0 = seen(ck);
+      else v1 = seen(ck);
       ++ready;
       it.template advance<DENSE>(p.g, bh, p.cpb);
     }
@@ -479,9 +538,10 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
           m_run[qt] = m_new;
         }
       }
+      // (while a row has seen no real key, m_run is -inf and every p is 0)
       float nm[QT];
 #pragma unroll
-      for (int qt = 0; qt < QT; ++qt) nm[qt] = -m_run[qt];
+      for (int qt = 0; qt < QT; ++qt) nm[qt] = m_run[qt] == -INFINITY ? 0.f : -m_run[qt];
 
       // ---- one basic block in program order (sched_barrier fences)
       // PV step q: d tile t = q % DT, key group qh = q / DT (keys 32kt_cur + 16qh ..)
@@ -537,7 +597,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
       const bool has2 = !it.done;
       const int st1 = cur == STAGES - 1 ? 0 : cur + 1;
       const int st2 = st1 == STAGES - 1 ? 0 : st1 + 1;
-      Chunk ck2 = {0, 0};
+      Chunk ck2 = {0, 0, -1};
       if (has2) {
         ck2 = it.template chunk<DENSE>();
         st2k.load(p, head_off, rs, ck2, 0);
@@ -557,7 +617,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
       --ready;
       cur = st1;
       v0 = v1;
-      v1 = ck2.valid;
+      v1 = has2 ? seen(ck2) : 0;
     }
 
     // ---- normalise and store the real rows (lane and lane ^ 32 share a row)
@@ -663,21 +723,32 @@ __global__ __launch_bounds__(256) void tile_kernel(const bf16_bits* __restrict__
   }
 }
 
-// Work of every item (real query-key token pairs), its LPT sort key, and the
-// reset of the queue counters.  cost < 2^32: a block holds at most 256 tokens
-// and L < 2^24.  key = cost << 32 | ~item: descending keys give descending
-// cost, ties to the lower item id.
-__global__ __launch_bounds__(256) void cost_kernel(const uint32_t* __restrict__ mask, const int32_t* __restrict__ cnt,
-                                                   int N, int words, int n_items, uint64_t* __restrict__ keys,
-                                                   uint32_t* __restrict__ rank, uint32_t* __restrict__ qctr) {
+// Work of every item (query rows x real key tokens of the union of its
+// members' kept blocks: the time the item takes), its LPT sort key, and the
+// reset of the queue counters.  cost < 2^32: an item holds at most 256 query
+// rows and L < 2^24.  key = cost << 32 | ~item: descending keys give
+// descending cost, ties to the lower item id.
+__global__ __launch_bounds__(256) void cost_kernel(AttnParams p, const int32_t* __restrict__ cnt,
+                                                   uint64_t* __restrict__ keys, uint32_t* __restrict__ rank,
+                                                   uint32_t* __restrict__ qctr) {
   const int item = blockIdx.x * blockDim.x + threadIdx.x;
   if (item < NXCD) qctr[item] = 0u;
-  if (item >= n_items) return;
-  const uint32_t* row = mask + (int64_t)item * words;
+  if (item >= p.n_items) return;
+  const int gid = item % p.n_groups, bh = item / p.n_groups;
+  const uint32_t* rows[4];
+  int nrows = 0;
+  uint32_t qrows = 0;
+  for (int k = 0; k < p.gt * p.gh * p.gw; ++k) {
+    const int n = group_member(p, gid, k);
+    if (n < 0) continue;
+    rows[nrows++] = p.mask + ((int64_t)bh * p.g.N + n) * p.words;
+    qrows += (uint32_t)cnt[n];
+  }
   uint32_t kv = 0;
-  for (int w = 0; w < words; ++w) {
-    uint32_t bits = row[w];
-    const int rem = N - w * 32;
+  for (int w = 0; w < p.words; ++w) {
+    uint32_t bits = 0u;
+    for (int r = 0; r < nrows; ++r) bits |= rows[r][w];
+    const int rem = p.g.N - w * 32;
     if (rem < 32) bits &= (1u << rem) - 1u;
     while (bits) {
       const int j = w * 32 + __builtin_ctz(bits);
@@ -685,7 +756,7 @@ __global__ __launch_bounds__(256) void cost_kernel(const uint32_t* __restrict__ 
       kv += (uint32_t)cnt[j];
     }
   }
-  const uint32_t cost = (uint32_t)cnt[item % N] * kv;
+  const uint32_t cost = qrows * kv;
   keys[item] = ((uint64_t)cost << 32) | (uint64_t)(~(uint32_t)item);
   rank[item] = 0u;
 }
@@ -778,42 +849,44 @@ __global__ __launch_bounds__(256) void scatter_kernel(const uint32_t* __restrict
 // ---------------------------------------------------------------------------
 // launches
 // ---------------------------------------------------------------------------
-// Kernel shape per block volume: (wavefronts, 32-row sub-tiles per wavefront).
-//   <= 64 rows: 2 x 1;  <= 128: 4 x 1;  <= 256: 8 x 1.
-// One sub-tile per wavefront keeps two wavefronts per SIMD, which hides LDS
-// and exp latency better than one wavefront with two sub-tiles.
-int attn_waves_for_block(int vol) { return vol <= 64 ? 2 : (vol <= 128 ? 4 : 8); }
-static int attn_qt_for_block(int) { return 1; }
+// Work item shape per block volume.  Every item is 8 wavefronts x 32 query
+// rows; small blocks are grouped so an item still fills them:
+//   volume <= 64:  2x1x2 blocks (t, y, x) per item, 2 wavefronts per block
+//   volume <= 128: 1x1x2 blocks per item, 4 wavefronts per block
+//   otherwise:     one block per item
+// A group walks the union of its blocks' kept key blocks; each wavefront
+// masks the key blocks its own query block did not keep.
+constexpr int WAVES = 8;
+int attn_waves_for_block(int) { return WAVES; }
+
+struct GroupShape {
+  int gt, gh, gw, wpb;
+};
+static GroupShape group_shape(int vol) {
+  if (vol <= 64) return {2, 1, 2, 2};
+  if (vol <= 128) return {1, 1, 2, 4};
+  return {1, 1, 1, 8};
+}
 
 int attn_chunks_per_block(int vol) { return (vol + KCH - 1) / KCH; }
 
 size_t attn_tile_bytes(int D, int64_t slots) { return (size_t)slots * 2 * KCH * D * sizeof(bf16_bits); }
 
-template <int D, int WAVES, int QT, bool DENSE>
-static const void* kernel_ptr() {
-  return reinterpret_cast<const void*>(&attn_kernel<D, WAVES, QT, DENSE>);
+static const void* sparse_kernel(int D, bool grouped) {
+  if (D == 128)
+    return grouped ? reinterpret_cast<const void*>(&attn_kernel<128, WAVES, 1, false, true>)
+                   : reinterpret_cast<const void*>(&attn_kernel<128, WAVES, 1, false, false>);
+  return grouped ? reinterpret_cast<const void*>(&attn_kernel<64, WAVES, 1, false, true>)
+                 : reinterpret_cast<const void*>(&attn_kernel<64, WAVES, 1, false, false>);
 }
 
-static const void* sparse_kernel(int D, int vol) {
-  const int waves = attn_waves_for_block(vol), qt = attn_qt_for_block(vol);
-  (void)qt;
-  if (D == 128) {
-    if (waves == 2) return kernel_ptr<128, 2, 1, false>();
-    if (waves == 4) return kernel_ptr<128, 4, 1, false>();
-    return kernel_ptr<128, 8, 1, false>();
-  }
-  if (waves == 2) return kernel_ptr<64, 2, 1, false>();
-  if (waves == 4) return kernel_ptr<64, 4, 1, false>();
-  return kernel_ptr<64, 8, 1, false>();
-}
-
-int attn_persistent_workgroups(int D, int vol, int* err) {
+int attn_persistent_workgroups(int D, int block_volume, int* err) {
   int dev = 0, cus = 0, occ = 0;
   *err = 0;
-  const int threads = attn_waves_for_block(vol) * 64;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, sparse_kernel(D, vol), threads, 0) != hipSuccess) {
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, sparse_kernel(D, group_shape(block_volume).wpb < WAVES),
+                                                   WAVES * 64, 0) != hipSuccess) {
     *err = 1;
     return 0;
   }
@@ -822,30 +895,11 @@ int attn_persistent_workgroups(int D, int vol, int* err) {
 }
 
 hipError_t launch_sparse_attn(const AttnLaunch& a, bool lpt, hipStream_t st) {
-  const int n_items = a.B * a.heads * a.g.N;
   const int BH = a.B * a.heads;
   const int words = (a.g.N + 31) / 32;
   const int vol = a.g.bt * a.g.bh * a.g.bw;
   const int cpb = attn_chunks_per_block(vol);
-  hipLaunchKernelGGL(layout_kernel, dim3(a.g.N), dim3(256), 0, st, a.g, a.tok, a.blk_cnt);
-  const unsigned slots = (unsigned)(BH * a.g.N * cpb);
-  if (a.D == 128)
-    hipLaunchKernelGGL(tile_kernel<128>, dim3(slots), dim3(256), 0, st, (const bf16_bits*)a.k, (const bf16_bits*)a.v,
-                       a.tok, a.g, a.L, a.heads, cpb, a.tiles);
-  else
-    hipLaunchKernelGGL(tile_kernel<64>, dim3(slots), dim3(256), 0, st, (const bf16_bits*)a.k, (const bf16_bits*)a.v,
-                       a.tok, a.g, a.L, a.heads, cpb, a.tiles);
-  hipLaunchKernelGGL(cost_kernel, dim3((n_items + 255) / 256), dim3(256), 0, st, a.mask, a.blk_cnt, a.g.N, words,
-                     n_items, a.keys, a.rank, a.qctr);
-  hipLaunchKernelGGL(head_plan_kernel, dim3(1), dim3(256), (size_t)BH * 12, st, a.keys, a.g.N, BH, lpt, a.head_pos,
-                     a.qoff);
-  if (lpt)
-    hipLaunchKernelGGL(rank_kernel, dim3((n_items + 255) / 256, (n_items + 2047) / 2048), dim3(256), 0, st, a.keys,
-                       n_items, a.g.N, a.rank);
-  hipLaunchKernelGGL(scatter_kernel, dim3((n_items + 255) / 256), dim3(256), 0, st, a.rank, a.head_pos, n_items,
-                     a.g.N, lpt, a.order);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  const GroupShape gs = group_shape(vol);
 
   AttnParams prm = {};
   prm.q = (const bf16_bits*)a.q;
@@ -864,21 +918,49 @@ hipError_t launch_sparse_attn(const AttnLaunch& a, bool lpt, hipStream_t st) {
   prm.order = a.order;
   prm.qoff = a.qoff;
   prm.qctr = a.qctr;
-  prm.n_items = n_items;
+  prm.gt = gs.gt;
+  prm.gh = gs.gh;
+  prm.gw = gs.gw;
+  prm.wpb = gs.wpb;
+  prm.gT = (a.g.nT + gs.gt - 1) / gs.gt;
+  prm.gH = (a.g.nH + gs.gh - 1) / gs.gh;
+  prm.gW = (a.g.nW + gs.gw - 1) / gs.gw;
+  prm.n_groups = prm.gT * prm.gH * prm.gW;
+  prm.n_items = BH * prm.n_groups;
   prm.scale_log2 = a.scale * 1.4426950408889634f;
   prm.trace = a.trace;
+  const int n_items = prm.n_items, per_head = prm.n_groups;
+
+  hipLaunchKernelGGL(layout_kernel, dim3(a.g.N), dim3(256), 0, st, a.g, a.tok, a.blk_cnt);
+  const unsigned slots = (unsigned)(BH * a.g.N * cpb);
+  if (a.D == 128)
+    hipLaunchKernelGGL(tile_kernel<128>, dim3(slots), dim3(256), 0, st, (const bf16_bits*)a.k, (const bf16_bits*)a.v,
+                       a.tok, a.g, a.L, a.heads, cpb, a.tiles);
+  else
+    hipLaunchKernelGGL(tile_kernel<64>, dim3(slots), dim3(256), 0, st, (const bf16_bits*)a.k, (const bf16_bits*)a.v,
+                       a.tok, a.g, a.L, a.heads, cpb, a.tiles);
+  hipLaunchKernelGGL(cost_kernel, dim3((n_items + 255) / 256), dim3(256), 0, st, prm, a.blk_cnt, a.keys, a.rank,
+                     a.qctr);
+  hipLaunchKernelGGL(head_plan_kernel, dim3(1), dim3(256), (size_t)BH * 12, st, a.keys, per_head, BH, lpt,
+                     a.head_pos, a.qoff);
+  if (lpt)
+    hipLaunchKernelGGL(rank_kernel, dim3((n_items + 255) / 256, (n_items + 2047) / 2048), dim3(256), 0, st, a.keys,
+                       n_items, per_head, a.rank);
+  hipLaunchKernelGGL(scatter_kernel, dim3((n_items + 255) / 256), dim3(256), 0, st, a.rank, a.head_pos, n_items,
+                     per_head, lpt, a.order);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
 
   int err = 0;
   const int grid = attn_persistent_workgroups(a.D, vol, &err);
   if (err) return hipErrorInvalidValue;
-  const void* k = sparse_kernel(a.D, vol);
   void* args[] = {&prm};
-  return hipLaunchKernel(k, dim3(grid), dim3(attn_waves_for_block(vol) * 64), args, 0, st);
+  return hipLaunchKernel(sparse_kernel(a.D, gs.wpb < WAVES), dim3(grid), dim3(WAVES * 64), args, 0, st);
 }
 
 hipError_t launch_dense_attn(const void* q, const void* k, const void* v, void* o, int B, int L, int heads, int D,
                              float scale, hipStream_t st) {
-  constexpr int WAVES = 8, QT = 1;
+  constexpr int QT = 1;
   AttnParams prm = {};
   prm.q = (const bf16_bits*)q;
   prm.k = (const bf16_bits*)k;
@@ -893,9 +975,9 @@ hipError_t launch_dense_attn(const void* q, const void* k, const void* v, void* 
   prm.trace = nullptr;
   const int grid = NXCD * ((prm.n_items + NXCD - 1) / NXCD);
   if (D == 128)
-    hipLaunchKernelGGL((attn_kernel<128, WAVES, QT, true>), dim3(grid), dim3(WAVES * 64), 0, st, prm);
+    hipLaunchKernelGGL((attn_kernel<128, WAVES, QT, true, false>), dim3(grid), dim3(WAVES * 64), 0, st, prm);
   else
-    hipLaunchKernelGGL((attn_kernel<64, WAVES, QT, true>), dim3(grid), dim3(WAVES * 64), 0, st, prm);
+    hipLaunchKernelGGL((attn_kernel<64, WAVES, QT, true, false>), dim3(grid), dim3(WAVES * 64), 0, st, prm);
   return hipGetLastError();
 }
 

@@ -11,9 +11,11 @@
 // reference would):
 //   pool_kernel        HBM stream of Q and K -> fp64 block means [B,h,N,D]
 //   scores_kernel      per (b,h): S = Qbar Kbar^T / sqrt(D), 64x64 tiles
-//   route_rows_kernel  one workgroup per row: softmax, bitonic sort on
-//                      (score desc, index asc), scan, Top-p count, floor,
-//                      mask words and kept count
+//   route_rows_kernel  N <= 512: one wavefront per row: softmax, bitonic
+//                      sort on (score desc, index asc), scan, Top-p count,
+//                      floor, mask words and kept count
+//   route_select_kernel N > 512: the same decisions by bisection on
+//                      order-preserving keys (no full sort)
 #include "fva_dev.h"
 #include "fva_kernels.h"
 
@@ -324,6 +326,240 @@ __global__ __launch_bounds__(THREADS) void route_rows_kernel(const double* __res
 }
 
 // ---------------------------------------------------------------------------
+// Row routing for large N (N > 512): selection instead of a full sort.
+// One workgroup of ceil(N/32) lanes (rounded up to whole wavefronts) per row;
+// lane t owns blocks 32t .. 32t+31 and writes mask word t.  Blocks are ranked
+// by a 64-bit key that orders fp64 scores exactly (ties by lower index), and
+//   n* = the smallest prefix whose probability mass reaches p is found by
+//        bisecting the key for the largest K with mass(key >= K) >= p,
+//   the kept set = the top `keep` blocks is found by bisecting the key for the
+//        largest K with count(key >= K) >= keep, ties taken in index order.
+// Every sum is a per-lane sequential sum in index order followed by a fixed
+// tree over lanes and wavefronts, so results do not depend on timing.
+// ---------------------------------------------------------------------------
+__device__ inline uint64_t order_key(double d) {
+  const uint64_t b = (uint64_t)__double_as_longlong(d);
+  return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+}
+
+template <typename T>
+__device__ inline T wave_sum(T v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+// fixed-order workgroup sum (lane tree, then wavefronts in order); all lanes get it
+template <typename T>
+__device__ inline T group_sum(T v, T* red, int nwaves) {
+  v = wave_sum(v);
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  T s = red[0];
+  for (int w = 1; w < nwaves; ++w) s += red[w];
+  return s;
+}
+
+__device__ inline double group_max(double v, double* red, int nwaves) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmax(v, __shfl_xor(v, off));
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  double s = red[0];
+  for (int w = 1; w < nwaves; ++w) s = fmax(s, red[w]);
+  return s;
+}
+
+__global__ __launch_bounds__(256) void route_select_kernel(const double* __restrict__ S, int N, int words,
+                                                           float top_p, int k_floor, uint32_t* __restrict__ mask,
+                                                           int32_t* __restrict__ kv_cnt,
+                                                           uint32_t* __restrict__ status) {
+  __shared__ double redd[4];
+  __shared__ uint32_t redu[4];
+  const int nwaves = blockDim.x >> 6;
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const double* s = S + row * N;
+  const int j0 = tid * 32;
+
+  double pr[32];
+  uint64_t key[32];
+  bool bad = false;
+  double lmax = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < 32; ++e) {
+    const int j = j0 + e;
+    double v = -INFINITY;
+    if (j < N) {
+      v = s[j];
+      if (!isfinite(v)) bad = true;
+      lmax = fmax(lmax, v);
+    }
+    pr[e] = v;
+  }
+  if (__syncthreads_or(bad)) {
+    if (tid < words) {
+      const int nb = min(32, N - j0);
+      mask[row * words + tid] = nb == 32 ? 0xffffffffu : ((1u << nb) - 1u);
+    }
+    if (tid == 0) {
+      if (kv_cnt) kv_cnt[row] = N;
+      if (status) atomicOr(status, 1u);
+    }
+    return;
+  }
+  const double M = group_max(lmax, redd, nwaves);
+  double lz = 0.0;
+#pragma unroll
+  for (int e = 0; e < 32; ++e)
+    if (j0 + e < N) lz += exp(pr[e] - M);
+  const double Z = group_sum(lz, redd, nwaves);
+#pragma unroll
+  for (int e = 0; e < 32; ++e) {
+    const bool in = j0 + e < N;
+    key[e] = in ? order_key(pr[e]) : 0ull;  // below every finite score
+    pr[e] = in ? exp(pr[e] - M) / Z : 0.0;
+  }
+  uint64_t kmin = ~0ull, kmax = 0ull;
+#pragma unroll
+  for (int e = 0; e < 32; ++e)
+    if (j0 + e < N) {
+      kmin = key[e] < kmin ? key[e] : kmin;
+      kmax = key[e] > kmax ? key[e] : kmax;
+    }
+  // workgroup min / max of the keys (as two u32 halves is not order safe: use
+  // the monotone map to double instead: keys of real blocks are > 0)
+  {
+    __shared__ unsigned long long kred[2][4];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const unsigned long long a = __shfl_xor((unsigned long long)kmin, off);
+      const unsigned long long b = __shfl_xor((unsigned long long)kmax, off);
+      kmin = a < kmin ? a : kmin;
+      kmax = b > kmax ? b : kmax;
+    }
+    __syncthreads();
+    if ((tid & 63) == 0) {
+      kred[0][tid >> 6] = kmin;
+      kred[1][tid >> 6] = kmax;
+    }
+    __syncthreads();
+    kmin = kred[0][0];
+    kmax = kred[1][0];
+    for (int w = 1; w < nwaves; ++w) {
+      kmin = kred[0][w] < kmin ? kred[0][w] : kmin;
+      kmax = kred[1][w] > kmax ? kred[1][w] : kmax;
+    }
+  }
+  auto mass_ge = [&](uint64_t K) -> double {
+    double m = 0.0;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) m += key[e] >= K ? pr[e] : 0.0;
+    return group_sum(m, redd, nwaves);
+  };
+  auto count_ge = [&](uint64_t K) -> uint32_t {
+    uint32_t c = 0;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) c += (j0 + e < N && key[e] >= K) ? 1u : 0u;
+    return group_sum(c, redu, nwaves);
+  };
+
+  const double p = (double)top_p;
+  int nstar;
+  if (p >= 1.0) {
+    nstar = N;
+  } else if (p <= 0.0) {
+    nstar = 0;
+  } else if (mass_ge(kmin) < p) {
+    nstar = N;  // rounding left the total below p: every block
+  } else {
+    // largest K with mass(key >= K) >= p: the key of the crossing block
+    uint64_t lo = kmin, hi = kmax;
+    if (mass_ge(hi) >= p) {
+      lo = hi;
+    } else {
+      while (hi - lo > 1) {
+        const uint64_t mid = lo + (hi - lo) / 2;
+        if (mass_ge(mid) >= p) lo = mid;
+        else hi = mid;
+      }
+    }
+    // blocks above the crossing key, then as many tied blocks as needed
+    const double above = lo == ~0ull ? 0.0 : mass_ge(lo + 1);
+    const uint32_t n_above = lo == ~0ull ? 0u : count_ge(lo + 1);
+    double ptie = 0.0;
+#pragma unroll
+    for (int e = 0; e < 32; ++e)
+      if (key[e] == lo) ptie = pr[e];
+    // every tied block has the same probability; any holder reports it
+    ptie = group_max(ptie, redd, nwaves);
+    int need = 1;
+    double c = above + ptie;
+    const int n_tie = (int)(count_ge(lo) - n_above);
+    while (c < p && need < n_tie) {
+      c += ptie;
+      ++need;
+    }
+    nstar = (int)n_above + need;
+  }
+  const int keep = min(N, max(k_floor, nstar));
+
+  uint32_t word = 0u;
+  if (keep >= N) {
+    const int nb = min(32, N - j0);
+    word = nb >= 32 ? 0xffffffffu : (nb > 0 ? ((1u << nb) - 1u) : 0u);
+  } else {
+    // largest K with count(key >= K) >= keep
+    uint64_t lo = kmin, hi = kmax;
+    if (count_ge(hi) >= (uint32_t)keep) {
+      lo = hi;
+    } else {
+      while (hi - lo > 1) {
+        const uint64_t mid = lo + (hi - lo) / 2;
+        if (count_ge(mid) >= (uint32_t)keep) lo = mid;
+        else hi = mid;
+      }
+    }
+    const uint32_t n_above = lo == ~0ull ? 0u : count_ge(lo + 1);
+    const uint32_t need = (uint32_t)keep - n_above;
+    // ties at the cut key, in index order: exclusive prefix over lanes
+    uint32_t my_ties = 0;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) my_ties += (j0 + e < N && key[e] == lo) ? 1u : 0u;
+    uint32_t incl = my_ties;
+    const int lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t o = __shfl_up(incl, off);
+      if (lane >= off) incl += o;
+    }
+    __shared__ uint32_t wt[4];
+    __syncthreads();
+    if (lane == 63) wt[wave] = incl;
+    __syncthreads();
+    uint32_t rank = incl - my_ties;
+    for (int w = 0; w < wave; ++w) rank += wt[w];
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      const int j = j0 + e;
+      if (j >= N) continue;
+      bool kept = key[e] > lo;
+      if (key[e] == lo) {
+        kept = rank < need;
+        ++rank;
+      }
+      if (kept) word |= 1u << e;
+    }
+  }
+  if (tid < words) mask[row * words + tid] = word;
+  if (tid == 0 && kv_cnt) kv_cnt[row] = keep;
+}
+
+// ---------------------------------------------------------------------------
 // launches
 // ---------------------------------------------------------------------------
 hipError_t launch_pool(const void* q, const void* k, const Geo& g, int B, int L, int heads, int D, double* qbar,
@@ -356,11 +592,13 @@ hipError_t launch_route_rows(const double* S, int64_t rows, int N, float top_p, 
   FVA_ROUTE_CASE(128, 64)
   FVA_ROUTE_CASE(256, 64)
   FVA_ROUTE_CASE(512, 64)
-  FVA_ROUTE_CASE(1024, 128)
-  FVA_ROUTE_CASE(2048, 256)
-  FVA_ROUTE_CASE(4096, 512)
-  FVA_ROUTE_CASE(8192, 1024)
 #undef FVA_ROUTE_CASE
+  if (N <= 8192) {
+    const int threads = 64 * ((words + 63) / 64);
+    hipLaunchKernelGGL(route_select_kernel, grid, dim3(threads), 0, st, S, N, words, top_p, k_floor, mask, kv_cnt,
+                       status);
+    return hipGetLastError();
+  }
   return hipErrorInvalidValue;
 }
 

@@ -215,6 +215,11 @@ def _custom(name, heads, D, grid, block, top_p, k_floor, batch=1, modes=8):
     _custom("small_blocks", 2, 64, (6, 8, 8), (2, 4, 4), 0.6, 3),
     _custom("fixed_topk", 3, 128, (9, 17, 23), (4, 8, 8), 0.0, 5),
     _custom("dense_floor", 2, 128, (9, 17, 23), (4, 8, 8), 0.5, 18),
+    # 65..128-token blocks: two query blocks per work item, the last group ragged
+    _custom("vol128_ragged", 2, 128, (7, 9, 21), (4, 4, 8), 0.8, 2),
+    # N = 576 > 512 key blocks: the bisection router
+    _custom("select_n576", 2, 64, (12, 16, 24), (2, 2, 2), 0.7, 3),
+    _custom("select_topk", 1, 128, (12, 16, 24), (2, 2, 2), 0.0, 7),
 ], ids=lambda w: w.name)
 def test_edge_cases(wl):
     (q, k, v), (qd, kd, vd) = _inputs(wl)
@@ -237,3 +242,44 @@ def test_topk_error_text():
     (q, k, v), (qd, kd, vd) = _inputs(wl)
     with pytest.raises(fva.FvaError, match="k_floor 9 > num_blocks 8"):
         fva.route(qd, kd, wl.grid, wl.block, 0.9, 9)
+
+
+def _with_tied_key_blocks(wl, k, period):
+    """K with every full key block a copy of one of the first `period` full
+    blocks (same tokens in the same in-block order), so block scores tie
+    exactly and the ties reach the Top-p / top-k cut."""
+    k = k.copy()
+    tab = oracle.block_table(wl.grid, wl.block)
+    tb = oracle.token_block(wl.grid, wl.block)
+    full = np.nonzero(tab[:, 6] == tab[:, 6].max())[0]
+    toks = {int(n): np.nonzero(tb == n)[0] for n in full}
+    for i, n in enumerate(full[period:]):
+        src = full[i % period]
+        k[:, toks[int(n)]] = k[:, toks[int(src)]]
+    return k
+
+
+@pytest.mark.parametrize("wl,period", [
+    (_custom("ties_bitonic", 2, 128, (8, 16, 24), (2, 4, 4), 0.6, 4), 5),
+    (_custom("ties_topk_bitonic", 2, 128, (8, 16, 24), (2, 4, 4), 0.0, 9), 4),
+    (_custom("ties_select", 2, 64, (12, 16, 24), (2, 2, 2), 0.5, 3), 7),
+    (_custom("ties_topk_select", 2, 64, (12, 16, 24), (2, 2, 2), 0.0, 10), 6),
+], ids=lambda x: x.name if hasattr(x, "name") else str(x))
+def test_route_ties_lower_index_first(wl, period):
+    q, k, v = fvgen.generate_qkv(wl)
+    k = _with_tied_key_blocks(wl, k, period)
+    qd, kd = _dev(q), _dev(k)
+    (mg, cg, sg), (mo, co, flags, so) = _route_both(wl, q, k, qd, kd)
+    N = oracle.num_blocks(wl.grid, wl.block)
+    # the cut falls inside a group of equal scores on most rows
+    kept = oracle.mask_to_bool(mo, N).reshape(-1, N)
+    S = oracle.scores(oracle.pool(q, wl.grid, wl.block), oracle.pool(k, wl.grid, wl.block)).reshape(-1, N)
+    tie_at_cut = sum(bool((S[r][~kept[r]] == S[r][kept[r]].min()).any()) for r in range(S.shape[0]))
+    assert tie_at_cut > 0.9 * S.shape[0]
+    print("\n[%s] N %d rows %d flagged %d" % (wl.name, N, flags.size, int((flags != 0).sum())), flush=True)
+    assert sg == so == 0
+    ok = flags == 0
+    assert ok.mean() > 0.9
+    assert not ((mg != mo).any(-1) & ok).any()
+    assert np.array_equal(cg[ok], co[ok])
+    assert kept.sum(-1).min() >= wl.k_floor
