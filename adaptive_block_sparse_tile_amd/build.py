@@ -16,10 +16,16 @@ HIPCC_FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     # no packed fp32 instructions anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
+# Per-source extras.  The attention kernels never test for NaN (their inputs
+# are finite by contract, and -inf marks excluded keys), so max/min need no
+# NaN canonicalisation there; the router keeps IEEE NaN handling because it
+# detects non-finite score rows.
+SOURCE_FLAGS = {
+    "fva_attn.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
+}
 
 
 def hipcc() -> str:
@@ -27,16 +33,31 @@ def hipcc() -> str:
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc()] + HIPCC_FLAGS + ["-I", os.path.join(HERE, "..", "include")] + srcs + ["-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + res.stderr[-8000:])
-    os.replace(tmp, LIB)
+
+
+def build(verbose: bool = False) -> str:
+    inc = ["-I", os.path.join(HERE, "..", "include")]
+    tag = ".tmp%d" % os.getpid()
+    objs = []
+    try:
+        for src in SOURCES:
+            obj = os.path.join(CSRC, src + tag + ".o")
+            _run([hipcc()] + HIPCC_FLAGS + SOURCE_FLAGS.get(src, []) + inc +
+                 ["-c", os.path.join(CSRC, src), "-o", obj], verbose)
+            objs.append(obj)
+        tmp = LIB + tag
+        _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp], verbose)
+        os.replace(tmp, LIB)
+    finally:
+        for o in objs:
+            if os.path.exists(o):
+                os.remove(o)
     return LIB
 
 

@@ -309,11 +309,26 @@ __device__ inline int pos_to_token(const AttnParams& p, int pos) {
 
 __device__ inline uint64_t wall_ticks() { return __builtin_amdgcn_s_memrealtime(); }
 
-// value of lane l ^ 32
-__device__ inline float swap_halves(float x) {
+// max and sum of the values of lanes l and l ^ 32.  permlane32_swap on two
+// copies of x leaves the low half of x in every lane of one result and the
+// high half in every lane of the other.
+__device__ inline float max_halves(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+__device__ inline float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Running max of a row before it has seen a real key: finite, so the
+// exponent argument needs no special case, and far enough below any real
+// score (in log2 units) that the first real key raises it and scales the
+// empty accumulators by exp2(-huge) = 0.
+constexpr float M_NONE = -1.0e30f;
+// lazy raise: the running max moves only when a new score exceeds it by more
+// than this many log2 units, so probabilities stay <= 2^RAISE_SLACK
+constexpr float RAISE_SLACK = 8.0f;
 
 // The attention kernel.  A work item is processed by WAVES wavefronts; each
 // owns QT sub-tiles of 32 query rows (rows 32*(QT*wave + qt) + lr of the
@@ -337,6 +352,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
   const int lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 31, hi = lane >> 5;
   const float cl2 = p.scale_log2;
+  const float inv_cl2 = 1.0f / cl2;
 
   uint64_t t_first = 0, t_last = 0, busy = 0, nitems = 0;
   int my_xcd = 0;
@@ -432,14 +448,15 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
     }
 
     f32x16 acc[QT][DT];
-    float m_run[QT], lsum[QT];
+    float m_run[QT], lsum[QT], thr[QT];  // thr: raise threshold on raw scores
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
 #pragma unroll
       for (int t = 0; t < DT; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[qt][t][r] = 0.f;
-      m_run[qt] = -INFINITY;
+      m_run[qt] = M_NONE;
+      thr[qt] = (M_NONE + RAISE_SLACK) * inv_cl2;
       lsum[qt] = 0.f;
     }
 
@@ -470,18 +487,80 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
     __syncthreads();
 
     // The pipeline runs on 32-key halves of the chunks (the online softmax
-    // is exact at any key granularity): while the MFMAs compute S^T of the
-    // next half, the VALU turns the current half into probabilities, then the
-    // current half's P V MFMAs run.  sA and sB hold S^T of a half for each
-    // sub-tile and trade roles every half, so nothing is copied.
-    constexpr int NQK = DS;       // K operand reads per half (one per 16-wide d step)
-    constexpr int NPV = 2 * DT;   // V^T operand reads per half (2 key groups x d tiles)
-    constexpr int AHEAD = 4;
-    constexpr int VPM = 16 / NQK;  // probabilities per sub-tile per Q K^T step
+    // is exact at any key granularity).  A half issues, in this order:
+    //   A: Q K^T steps 0..DT-1 of the next half (a dependent MFMA chain), with
+    //      the probabilities of the current half's first 16 keys;
+    //   B: P V of those 16 keys (one MFMA per d tile) alternating with Q K^T
+    //      steps DT..2DT-1, with the probabilities of the other 16 keys;
+    //   C: P V of the other 16 keys, with the statistics of the next half.
+    // Independent P V MFMAs cover the latency of the Q K^T chain, and the
+    // vector work is spread over the whole half rather than packed into the
+    // Q K^T chain.  sA and sB hold S^T of a half for each sub-tile and trade
+    // roles every half, so nothing is copied.
+    constexpr int NOPS = 4 * DT;  // LDS operands per half: 2DT of K, 2DT of V^T
+    constexpr int AHEAD = 4;      // operands in flight (a ring in consumption order)
+    constexpr int EPS = 8 / DT;   // probabilities per sub-tile per step of A or B
+    static_assert(NOPS % AHEAD == 0 && EPS % 2 == 0, "operand ring and probability pairs");
     f32x16 sA[QT], sB[QT];
     auto kread_at = [&](const bf16_bits* img, int kt, int ds) -> bf16x8 {
       return *(const bf16x8*)(img + Lds<D>::k_off(32 * kt + lr, 16 * ds + 8 * hi));
     };
+    auto vread_at = [&](const bf16_bits* img, int kt, int kg, int t) -> bf16x8 {
+      return *(const bf16x8*)(img + Lds<D>::v_off(32 * t + lr, 32 * kt + 16 * kg + 8 * hi));
+    };
+    // operand i of a half: a K d-step (isk, a = d-step) or a V^T tile (a = key
+    // group, t = d tile), in the order the MFMAs of A, B and C consume them
+    struct HalfOp {
+      bool isk;
+      int a, t;
+    };
+    auto half_op = [](int i) -> HalfOp {
+      if (i < DT) return {true, i, 0};
+      if (i < 3 * DT) {
+        const int j = i - DT;
+        return (j & 1) ? HalfOp{true, DT + j / 2, 0} : HalfOp{false, 0, j / 2};
+      }
+      return {false, 1, i - 3 * DT};
+    };
+
+    // Row statistics of a freshly computed S^T half: the tail mask (keys past
+    // the chunk's real count become -inf), the row max in raw score units and
+    // whether some row's running max must move.  Split into STAT_STEPS steps
+    // so they sit between the P V MFMAs of the half before the one that uses
+    // them, off the critical path.
+    constexpr int STAT_STEPS = 7;
+    float mxc[QT];    // row max of the half to be exponentiated next
+    float mpart[QT];  // partial row max
+    bool rc = false;  // some row of that half needs its running max raised
+    auto stat_step = [&](int step, f32x16 (&sx)[QT], int valid, int kt) __attribute__((always_inline)) {
+      if (step == 0) {
+        // lane holds keys 32kt + 8(r/4) + 4hi + r%4 of query lr of each sub-tile
+        if (valid < 32 * kt + 32) {
+          const int lim = valid - 32 * kt - 4 * hi;
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (8 * (r >> 2) + (r & 3) >= lim) sx[qt][r] = -INFINITY;
+        }
+      } else if (step <= 4) {
+        const int r0 = 4 * (step - 1);
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+          const float m = step == 1 ? sx[qt][0] : fmaxf(mpart[qt], sx[qt][r0]);
+          mpart[qt] = fmaxf(fmaxf(m, sx[qt][r0 + 1]), fmaxf(sx[qt][r0 + 2], sx[qt][r0 + 3]));
+        }
+      } else if (step == 5) {
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) mxc[qt] = max_halves(mpart[qt]);
+      } else {
+        bool r = false;
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) r = r || (mxc[qt] > thr[qt]);
+        rc = __any(r);
+      }
+    };
+
     if (wave_active && ready > 0) {
 #pragma unroll
       for (int ds = 0; ds < DS; ++ds) {
@@ -492,44 +571,34 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
           sA[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qt][ds], ds == 0 ? c0 : sA[qt], 0, 0, 0);
         }
       }
+#pragma unroll
+      for (int step = 0; step < STAT_STEPS; ++step) stat_step(step, sA, v0, 0);
     }
-    // K operands of the next Q K^T (its first AHEAD d-steps), read one half ahead
-    bf16x8 kw[AHEAD];
+    // the first AHEAD operands of the first half (key half 0 of chunk 0; its
+    // Q K^T computes key half 1 of chunk 0)
+    bf16x8 opw[AHEAD];
 #pragma unroll
-    for (int q = 0; q < AHEAD; ++q) kw[q] = kread_at(ring[0], 1, q);
+    for (int i = 0; i < AHEAD; ++i) {
+      const HalfOp o = half_op(i);
+      opw[i] = o.isk ? kread_at(ring[0], 1, o.a) : vread_at(ring[0], 0, o.a, o.t);
+    }
 
-    // One half: keys 32*kt_cur .. +31 of the chunk in LDS image imgv (S^T in
-    // sc, `valid` real keys in the chunk).  S^T of the next half (key half
-    // kt_nxt of image imgk, first operands already in kw) goes to sn; during
-    // the P V part the first operands of the half after that (key half
-    // kt_nn of image imgk2) are read into kw.
-    auto half = [&](f32x16 (&sc)[QT], f32x16 (&sn)[QT], int kt_cur, int valid, const bf16_bits* imgv,
-                    const bf16_bits* imgk, int kt_nxt, const bf16_bits* imgk2, int kt_nn)
-                    __attribute__((always_inline)) {
-      // lane holds keys 32kt_cur + 8(r/4) + 4hi + r%4 of query lr of each sub-tile
-      if (valid < 32 * kt_cur + 32) {
-        const int thr = valid - 32 * kt_cur - 4 * hi;
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (8 * (r >> 2) + (r & 3) >= thr) sc[qt][r] = -INFINITY;
-      }
-      float mx[QT];
-      bool raise = false;
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) {
-        float m = sc[qt][0];
-#pragma unroll
-        for (int r = 1; r < 16; ++r) m = fmaxf(m, sc[qt][r]);
-        mx[qt] = fmaxf(m, swap_halves(m)) * cl2;
-        raise = raise || (mx[qt] > m_run[qt] + 8.0f);
-      }
-      if (__any(raise)) {
+    // One half: keys 32*kt_cur .. +31 of the chunk in LDS image imgv, S^T
+    // (masked, statistics in mxc / rc) in sc.  S^T of the next half (key half
+    // kt_nxt of image imgk, valid_nxt real keys in its chunk) goes to sn and
+    // its statistics are taken in C.  The operand ring runs AHEAD operands
+    // into the half after (its V^T from imgk / kt_nxt, its K from imgk2 /
+    // kt_nn).
+    constexpr int STAT_C0 = 1;  // first step of C followed by statistics (the Q K^T result has landed)
+    constexpr int STAT_PER = (STAT_STEPS + DT - STAT_C0 - 1) / (DT - STAT_C0);
+    auto half = [&](f32x16 (&sc)[QT], f32x16 (&sn)[QT], int kt_cur, const bf16_bits* imgv, const bf16_bits* imgk,
+                    int kt_nxt, int valid_nxt, const bf16_bits* imgk2, int kt_nn) __attribute__((always_inline)) {
+      if (rc) {
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) {
-          const float m_new = fmaxf(m_run[qt], mx[qt]);
+          const float m_new = fmaxf(m_run[qt], mxc[qt] * cl2);
           const float alpha = __builtin_amdgcn_exp2f(m_run[qt] - m_new);
+          thr[qt] = (m_new + RAISE_SLACK) * inv_cl2;
 #pragma unroll
           for (int t = 0; t < DT; ++t)
 #pragma unroll
@@ -538,54 +607,81 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
           m_run[qt] = m_new;
         }
       }
-      // (while a row has seen no real key, m_run is -inf and every p is 0)
       float nm[QT];
 #pragma unroll
-      for (int qt = 0; qt < QT; ++qt) nm[qt] = m_run[qt] == -INFINITY ? 0.f : -m_run[qt];
+      for (int qt = 0; qt < QT; ++qt) nm[qt] = -m_run[qt];
 
-      // ---- one basic block in program order (sched_barrier fences)
-      // PV step q: d tile t = q % DT, key group qh = q / DT (keys 32kt_cur + 16qh ..)
-      auto vread = [&](int q) -> bf16x8 {
-        return *(const bf16x8*)(imgv + Lds<D>::v_off(32 * (q % DT) + lr, 32 * kt_cur + 16 * (q / DT) + 8 * hi));
+      // consume operand i from the ring and read operand i + AHEAD into its slot
+      auto refill = [&](int i) __attribute__((always_inline)) {
+        const int j = i + AHEAD;
+        const HalfOp o = half_op(j % NOPS);
+        bf16x8 x;
+        if (j < NOPS) x = o.isk ? kread_at(imgk, kt_nxt, o.a) : vread_at(imgv, kt_cur, o.a, o.t);
+        else x = o.isk ? kread_at(imgk2, kt_nn, o.a) : vread_at(imgk, kt_nxt, o.a, o.t);
+        opw[i % AHEAD] = x;
       };
       typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
       const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
-      bf16x8 pb[2][QT];
-      bf16x8 vw[AHEAD];
-      __builtin_amdgcn_sched_barrier(0);
+      u32x4 pw[2][QT];  // bf16 probability pairs: B operands of the P V MFMAs
+      // probabilities r0 .. r0+EPS-1 of every sub-tile, rounded to bf16 in
+      // pairs; the row sum adds the same rounded values the MFMA uses
+      auto probs = [&](int r0) __attribute__((always_inline)) {
 #pragma unroll
-      for (int q = 0; q < NQK; ++q) {
+        for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+          for (int u = 0; u < EPS; u += 2) {
+            const int r = r0 + u;
+            const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[qt][r], cl2, nm[qt]));
+            const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[qt][r + 1], cl2, nm[qt]));
+            const bf16x2_t pr = {(__bf16)e0, (__bf16)e1};
+            pw[r >> 3][qt][(r & 7) >> 1] = __builtin_bit_cast(uint32_t, pr);
+            lsum[qt] = __builtin_amdgcn_fdot2_f32_bf16(pr, one, lsum[qt], false);
+          }
+      };
+      auto pv = [&](int i, int kg, int t) __attribute__((always_inline)) {
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+          acc[qt][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opw[i % AHEAD], __builtin_bit_cast(bf16x8, pw[kg][qt]),
+                                                              acc[qt][t], 0, 0, 0);
+        refill(i);
+      };
+      auto qk = [&](int i, int ds) __attribute__((always_inline)) {
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) {
           const f32x16 c0 = {};
-          sn[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kw[q % AHEAD], qf[qt][q], q == 0 ? c0 : sn[qt], 0, 0, 0);
-          if (qt == QT - 1) {
-            if (q + AHEAD < NQK) kw[q % AHEAD] = kread_at(imgk, kt_nxt, q + AHEAD);
-            if (q >= NQK - AHEAD) vw[q - (NQK - AHEAD)] = vread(q - (NQK - AHEAD));
-          }
-          // probabilities r = VPM*q .. of sub-tile qt
-#pragma unroll
-          for (int u = 0; u < VPM; ++u) {
-            const int r = VPM * q + u;
-            pb[r >> 3][qt][r & 7] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[qt][r], cl2, nm[qt]));
-          }
-#pragma unroll
-          for (int u = 0; u < VPM; u += 2) {
-            const int r = VPM * q + u;
-            const bf16x2_t pr = {pb[r >> 3][qt][r & 7], pb[r >> 3][qt][(r & 7) + 1]};
-            lsum[qt] = __builtin_amdgcn_fdot2_f32_bf16(pr, one, lsum[qt], false);
-          }
-          __builtin_amdgcn_sched_barrier(0);
+          sn[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opw[i % AHEAD], qf[qt][ds], ds == 0 ? c0 : sn[qt], 0, 0, 0);
         }
+        refill(i);
+      };
+
+      // ---- program order is kept by sched_barrier fences
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < DT; ++j) {  // A
+        qk(j, j);
+        probs(EPS * j);
+        __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
-      for (int q = 0; q < NPV; ++q) {
-        const int t = q % DT, qh = q / DT;
+      for (int j = 0; j < DT; ++j) {  // B
+        pv(DT + 2 * j, 0, j);
+        qk(DT + 2 * j + 1, DT + j);
+        probs(8 + EPS * j);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // Every probability of the half exists here: otherwise the compiler
+      // sinks the second key group's exponentials past the tail-mask branch
+      // in C, out of the MFMA gaps they are meant to fill.
 #pragma unroll
-        for (int qt = 0; qt < QT; ++qt)
-          acc[qt][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vw[q % AHEAD], pb[qh][qt], acc[qt][t], 0, 0, 0);
-        if (q + AHEAD < NPV) vw[q % AHEAD] = vread(q + AHEAD);
-        if (q >= NPV - AHEAD) kw[q - (NPV - AHEAD)] = kread_at(imgk2, kt_nn, q - (NPV - AHEAD));
+      for (int qt = 0; qt < QT; ++qt) asm volatile("" : : "v"(pw[0][qt]), "v"(pw[1][qt]), "v"(lsum[qt]));
+#pragma unroll
+      for (int j = 0; j < DT; ++j) {  // C
+        pv(3 * DT + j, 1, j);
+        if (j >= STAT_C0) {
+#pragma unroll
+          for (int k = (j - STAT_C0) * STAT_PER; k < (j - STAT_C0 + 1) * STAT_PER && k < STAT_STEPS; ++k)
+            stat_step(k, sn, valid_nxt, kt_nxt);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     };
@@ -593,7 +689,6 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
     int cur = 0;  // stage of the chunk being finished
     Stager<D, THREADS, DENSE> st2k;  // chunk c+2, K image
     while (ready > 0) {
-      const int valid = v0;
       const bool has2 = !it.done;
       const int st1 = cur == STAGES - 1 ? 0 : cur + 1;
       const int st2 = st1 == STAGES - 1 ? 0 : st1 + 1;
@@ -604,8 +699,8 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
         st.load(p, head_off, rs, ck2, 1);
       }
       if (wave_active) {
-        half(sA, sB, 0, valid, ring[cur], ring[cur], 1, ring[st1], 0);
-        half(sB, sA, 1, valid, ring[cur], ring[st1], 0, ring[st1], 1);
+        half(sA, sB, 0, ring[cur], ring[cur], 1, v0, ring[st1], 0);
+        half(sB, sA, 1, ring[cur], ring[st1], 0, v1, ring[st1], 1);
       }
       if (has2) {
         st2k.store(ring[st2], 0);
@@ -624,7 +719,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
     if (wave_active) {
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
-        const float lt = lsum[qt] + swap_halves(lsum[qt]);
+        const float lt = sum_halves(lsum[qt]);
         const int qrow = row0 + 32 * qt + lr;
         if (qrow < qcount) {
           const float inv = lt > 0.f ? 1.f / lt : 0.f;
