@@ -34,19 +34,15 @@
 namespace fva {
 
 constexpr int KCH = 64;     // keys per chunk
-constexpr int STAGES = 3;   // LDS ring depth
+constexpr int STAGES = 4;   // LDS ring depth
+constexpr int MAX_WORDS = 256;  // mask words per row (8192 blocks)
 constexpr int NXCD = 8;     // XCDs of an MI355X
 
-// A chunk's image in the tiled copy (compact): K [64][D] row-major, then
-// V^T [D][64] with key positions permuted by pi.
-template <int D>
-struct Img {
-  static constexpr int KELEMS = KCH * D;
-  static constexpr int ELEMS = 2 * KCH * D;
-};
-
-// The same chunk in LDS: every row padded by 16 bytes (K rows D+8, V^T rows
-// 64+8 elements).  Rows 16 bytes apart in bank order make the 16-byte operand
+// A chunk of 64 keys, in LDS and in the tiled copy in HBM alike (the copy
+// is byte-identical to the LDS image, so it moves by direct global-to-LDS
+// loads): K [64][D] row-major, then V^T [D][64] with key positions permuted
+// by pi, every row padded by 16 bytes (K rows D+8, V^T rows 64+8 elements;
+// the pad is zero).  Rows 16 bytes apart in bank order make the 16-byte operand
 // reads of 16 consecutive rows hit distinct banks (272 = 17*16 and
 // 144 = 9*16, both odd multiples of 16 bytes), and each operand address is a
 // per-lane base plus a compile-time offset.
@@ -112,26 +108,17 @@ struct Chunk {
   int blk;    // sparse: key block of the chunk
 };
 
-// Walks the chunks of one work item: the set bits of the union of its (up to
-// NR) member blocks' mask rows in ascending block order (sparse) or the whole
-// sequence (dense).  Every thread of the workgroup holds the same state.
-template <int NR>
+// Walks the chunks of one work item: the set bits of the union of its member
+// blocks' mask rows (staged in LDS, bits >= N cleared) in ascending block
+// order (sparse) or the whole sequence (dense).  Every thread of the
+// workgroup holds the same state.
 struct KvIter {
-  const uint32_t* rows[NR];
-  int nrows;
+  const uint32_t* umask;  // LDS
   int w, words, c, nch, count, slot0, blk;
   uint32_t bits;
   bool done;
 
-  __device__ uint32_t load_word(const Geo& g, int wi) const {
-    uint32_t x = rows[0][wi];
-#pragma unroll
-    for (int r = 1; r < NR; ++r)
-      if (r < nrows) x |= rows[r][wi];
-    const int rem = g.N - wi * 32;
-    if (rem < 32) x &= (1u << rem) - 1u;  // bits of blocks >= N are not blocks
-    return x;
-  }
+  __device__ uint32_t load_word(const Geo&, int wi) const { return umask[wi]; }
 
   __device__ void next_block(const Geo& g, int bh, int cpb) {
     while (bits == 0u) {
@@ -162,10 +149,6 @@ struct KvIter {
     }
     words = nwords;
     w = 0;
-    if (nrows == 0) {
-      done = true;
-      return;
-    }
     bits = load_word(g, 0);
     next_block(g, bh, cpb);
   }
@@ -197,32 +180,64 @@ struct KvIter {
 template <int D, int THREADS, bool DENSE>
 struct Stager;
 
-// Sparse: the chunk image is contiguous; a linear copy, staged in two halves
-// (part 0 = the K image, part 1 = the V^T image) so only half a chunk is held
-// in registers at a time.
-template <int D, int THREADS>
-struct Stager<D, THREADS, false> {
-  static constexpr int N16 = Img<D>::ELEMS * 2 / 16;  // 16-byte pieces per image
-  static constexpr int HALF = N16 / 2;
-  static constexpr int PER = (HALF + THREADS - 1) / THREADS;
-  u32x4 r[PER];
-
-  __device__ void load(const AttnParams& p, int64_t, int64_t, Chunk ck, int part) {
-    const u32x4* src = (const u32x4*)(p.tiles + (int64_t)ck.slot * Img<D>::ELEMS) + part * HALF;
+// Sparse: a chunk image moves from HBM straight into LDS, 1 KB per wavefront
+// instruction (global_load_lds_dwordx4: lane l's 16 bytes land at the LDS
+// address in M0 + 16 l).  It is written as inline assembly so that the
+// compiler's wait counting stays blind to these loads: its LDS waits inside
+// the attention loop then stay fine-grained.  The instruction has no
+// register result; completion is tracked here, by the explicit vmcnt waits
+// before each barrier (wait_vmem), and the barrier (barrier_lds) orders
+// every LDS read of a stage after the wait for the loads into it.
+// Every wavefront issues the same number (PER_WAVE) of instructions per
+// chunk, so that a wait for "all but the newest chunk" is one vmcnt
+// immediate: a wavefront with fewer pieces repeats its last one (the same
+// bytes to the same place).
+template <int D, int WAVES>
+struct ChunkDma {
+  static constexpr int BYTES = Lds<D>::ELEMS * 2;
+  static constexpr int PIECES = BYTES / 1024;
+  static constexpr int PER_WAVE = (PIECES + WAVES - 1) / WAVES;
+  static_assert(BYTES % 1024 == 0, "a chunk image is a whole number of 1 KB pieces");
+  static_assert(PIECES >= WAVES && PER_WAVE <= 15, "every wavefront has a piece; vmcnt range");
+  __device__ static void issue(const bf16_bits* tiles, int slot, bf16_bits* lds, int wave, int lane) {
+    const char* src = (const char*)tiles + (int64_t)slot * BYTES + lane * 16;
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int s = threadIdx.x + u * THREADS;
-      if (HALF % THREADS == 0 || s < HALF) r[u] = src[s];
-    }
-  }
-  __device__ void store(bf16_bits* lds, int part) const {
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int s = threadIdx.x + u * THREADS;
-      if (HALF % THREADS == 0 || s < HALF) *(u32x4*)(lds + Lds<D>::piece_off(part * HALF + s)) = r[u];
+    for (int u = 0; u < PER_WAVE; ++u) {
+      int j = wave + u * WAVES;
+      if (j >= PIECES) j -= WAVES;
+      const uint32_t ldsa = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)((char*)lds + j * 1024);
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(ldsa), "v"(src + j * 1024) : "memory", "m0");
     }
   }
 };
+
+// (sparse chunks need no register staging)
+template <int D, int THREADS>
+struct Stager<D, THREADS, false> {
+  __device__ void load(const AttnParams&, int64_t, int64_t, Chunk, int) {}
+  __device__ void store(bf16_bits*, int) const {}
+};
+
+// Workgroup barrier for LDS data: waits for this wavefront's LDS operations
+// and meets the other wavefronts, but leaves global loads in flight (a
+// __syncthreads() would wait for all of them, including the chunk loads
+// issued ahead; callers wait for the loads they need with wait_vmem).  The
+// empty asm statements keep the compiler from moving memory accesses
+// across the barrier.
+__device__ inline void barrier_lds() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt untouched
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// wait until at most N of this wavefront's global loads (including those
+// into LDS) are outstanding; expcnt and lgkmcnt are not waited for
+template <int N>
+__device__ inline void wait_vmem() {
+  static_assert(N >= 0 && N <= 15, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
 
 // Dense: 64 consecutive tokens of BSHD K and V; V is transposed on the way.
 // Part 0 stages K, part 1 stages V.
@@ -340,16 +355,29 @@ constexpr float RAISE_SLACK = 8.0f;
 template <int D, int WAVES, int QT, bool DENSE, bool GRP>
 __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
   static_assert(!(DENSE && GRP), "dense items are query tiles");
-  constexpr int NR = GRP ? 4 : 1;
   constexpr int THREADS = WAVES * 64;
   constexpr int QROWS = WAVES * QT * 32;
   constexpr int DS = D / 16;  // 16-wide d steps of Q K^T
   constexpr int DT = D / 32;  // 32-row d tiles of O^T
-  __shared__ __attribute__((aligned(16))) bf16_bits ring[STAGES][Lds<D>::ELEMS];
+  // the LDS ring: one array per stage, so that the compiler sees that the
+  // loads in flight into one stage do not touch the stages being read
+  __shared__ __attribute__((aligned(16))) bf16_bits ring0[Lds<D>::ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16_bits ring1[Lds<D>::ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16_bits ring2[Lds<D>::ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16_bits ring3[Lds<D>::ELEMS];
+  // the item's mask: the union of its members' rows, and (groups) each
+  // member's own row
+  __shared__ uint32_t umask[DENSE ? 1 : MAX_WORDS];
+  __shared__ uint32_t gmask[GRP ? 4 : 1][GRP ? MAX_WORDS : 1];
   __shared__ int item_s;
+  static_assert(STAGES == 4, "four ring stages");
+  auto stage = [&](int sidx) -> bf16_bits* {
+    return sidx == 0 ? ring0 : (sidx == 1 ? ring1 : (sidx == 2 ? ring2 : ring3));
+  };
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform in the wavefront
   const int lr = lane & 31, hi = lane >> 5;
   const float cl2 = p.scale_log2;
   const float inv_cl2 = 1.0f / cl2;
@@ -385,11 +413,11 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
     const uint64_t t_start = wall_ticks();
 
     int b, h, bh;
-    int qbase, qcount;             // this wavefront's query block: first position, real rows
-    int row0;                      // first row of this wavefront inside that block
-    const uint32_t* my_row = nullptr;  // this wavefront's mask row (sparse)
-    KvIter<NR> it;
-    it.nrows = 0;
+    int qbase, qcount;  // this wavefront's query block: first position, real rows
+    int row0;           // first row of this wavefront inside that block
+    int mine = -1;      // groups: this wavefront's member index, or -1
+    KvIter it;
+    it.umask = umask;
     if (DENSE) {
       const int tile = item % p.q_tiles;
       bh = item / p.q_tiles;
@@ -399,8 +427,11 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
     } else if (!GRP) {
       const int n = item % p.g.N;
       bh = item / p.g.N;
-      it.rows[0] = p.mask + ((int64_t)bh * p.g.N + n) * p.words;
-      it.nrows = 1;
+      const uint32_t* row = p.mask + ((int64_t)bh * p.g.N + n) * p.words;
+      for (int wi = tid; wi < p.words; wi += THREADS) {
+        const int rem = p.g.N - wi * 32;
+        umask[wi] = rem < 32 ? row[wi] & ((1u << rem) - 1u) : row[wi];
+      }
       const Box bx = block_box(p.g, n);
       qbase = bx.start;
       qcount = bx.count;
@@ -409,17 +440,24 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
       const int gid = item % p.n_groups;
       bh = item / p.n_groups;
       const int ng = p.gt * p.gh * p.gw;
-      for (int k = 0; k < ng; ++k) {
-        const int n = group_member(p, gid, k);
-        if (n >= 0) it.rows[it.nrows++] = p.mask + ((int64_t)bh * p.g.N + n) * p.words;
+      for (int wi = tid; wi < p.words; wi += THREADS) {
+        uint32_t u = 0u;
+        for (int k = 0; k < 4; ++k) {
+          const int n = k < ng ? group_member(p, gid, k) : -1;
+          const uint32_t x = n >= 0 ? p.mask[((int64_t)bh * p.g.N + n) * p.words + wi] : 0u;
+          gmask[k][wi] = x;
+          u |= x;
+        }
+        const int rem = p.g.N - wi * 32;
+        umask[wi] = rem < 32 ? u & ((1u << rem) - 1u) : u;
       }
-      const int mine = group_member(p, gid, wave / p.wpb);
+      const int n_mine = group_member(p, gid, wave / p.wpb);
       row0 = 32 * QT * (wave % p.wpb);
-      if (mine >= 0) {
-        const Box bx = block_box(p.g, mine);
+      if (n_mine >= 0) {
+        mine = wave / p.wpb;
+        const Box bx = block_box(p.g, n_mine);
         qbase = bx.start;
         qcount = bx.count;
-        my_row = p.mask + ((int64_t)bh * p.g.N + mine) * p.words;
       } else {
         qbase = 0;
         qcount = 0;
@@ -446,6 +484,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
         qf[qt][s] = __builtin_bit_cast(bf16x8, x);
       }
     }
+    wait_vmem<0>();  // Q is in before any chunk load is issued
 
     f32x16 acc[QT][DT];
     float m_run[QT], lsum[QT], thr[QT];  // thr: raise threshold on raw scores
@@ -461,30 +500,48 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
     }
 
     // ---- pipeline: `it` is the next chunk to load; the ring holds `ready`
-    //      loaded chunks starting at stage `cur`, with real key counts v0, v1
+    //      chunks (loaded or in flight) starting with the one being
+    //      computed, with real key counts v0, v1, v2 as this wavefront sees them
+    if (!DENSE) __syncthreads();  // the item's mask is in LDS
     it.template first<DENSE>(p.g, p.words, p.L, bh, p.cpb);
     Stager<D, THREADS, DENSE> st;
     // real keys of the chunks in the ring as this wavefront sees them: a key
     // block its own query block did not keep counts as 0 real keys
     auto seen = [&](const Chunk& ck) -> int {
       if (!GRP) return ck.valid;  // a single member: the union is its own row
-      if (!my_row) return 0;
-      return ((my_row[ck.blk >> 5] >> (ck.blk & 31)) & 1u) ? ck.valid : 0;
+      if (mine < 0) return 0;
+      return ((gmask[mine][ck.blk >> 5] >> (ck.blk & 31)) & 1u) ? ck.valid : 0;
     };
-    int ready = 0, v0 = 0, v1 = 0;
-    for (int sidx = 0; sidx < 2 && !it.done; ++sidx) {
-      const Chunk ck = it.template chunk<DENSE>();
+    // sparse chunks arrive by direct loads three chunks ahead of the one
+    // being computed; dense chunks pass through registers two ahead
+    constexpr int LOOK = DENSE ? 2 : 3;
+    using Dma = ChunkDma<D, WAVES>;
+    int ready = 0, v0 = 0, v1 = 0, v2 = 0;
 #pragma unroll
-      for (int part = 0; part < 2; ++part) {
-        st.load(p, head_off, rs, ck, part);
-        st.store(ring[sidx], part);
+    for (int sidx = 0; sidx < LOOK; ++sidx) {
+      if (it.done) break;
+      const Chunk ck = it.template chunk<DENSE>();
+      if (DENSE) {
+#pragma unroll
+        for (int part = 0; part < 2; ++part) {
+          st.load(p, head_off, rs, ck, part);
+          st.store(stage(sidx), part);
+        }
+      } else {
+        Dma::issue(p.tiles, ck.slot, stage(sidx), wave, lane);
       }
-      if (sidx == 0) v0 = seen(ck);
-      else v1 = seen(ck);
+      const int sv = seen(ck);
+      if (sidx == 0) v0 = sv;
+      else if (sidx == 1) v1 = sv;
+      else v2 = sv;
       ++ready;
       it.template advance<DENSE>(p.g, bh, p.cpb);
     }
-    __syncthreads();
+    if (!DENSE) {  // chunks 0 and 1 must be in; chunk 2 may still be in flight
+      if (ready == LOOK) wait_vmem<Dma::PER_WAVE>();
+      else wait_vmem<0>();
+    }
+    barrier_lds();
 
     // The pipeline runs on 32-key halves of the chunks (the online softmax
     // is exact at any key granularity).  A half issues, in this order:
@@ -564,7 +621,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
     if (wave_active && ready > 0) {
 #pragma unroll
       for (int ds = 0; ds < DS; ++ds) {
-        const bf16x8 a = kread_at(ring[0], 0, ds);
+        const bf16x8 a = kread_at(ring0, 0, ds);
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) {
           const f32x16 c0 = {};
@@ -580,7 +637,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
 #pragma unroll
     for (int i = 0; i < AHEAD; ++i) {
       const HalfOp o = half_op(i);
-      opw[i] = o.isk ? kread_at(ring[0], 1, o.a) : vread_at(ring[0], 0, o.a, o.t);
+      opw[i] = o.isk ? kread_at(ring0, 1, o.a) : vread_at(ring0, 0, o.a, o.t);
     }
 
     // One half: keys 32*kt_cur .. +31 of the chunk in LDS image imgv, S^T
@@ -686,33 +743,59 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
       }
     };
 
-    int cur = 0;  // stage of the chunk being finished
-    Stager<D, THREADS, DENSE> st2k;  // chunk c+2, K image
-    while (ready > 0) {
-      const bool has2 = !it.done;
-      const int st1 = cur == STAGES - 1 ? 0 : cur + 1;
-      const int st2 = st1 == STAGES - 1 ? 0 : st1 + 1;
-      Chunk ck2 = {0, 0, -1};
-      if (has2) {
-        ck2 = it.template chunk<DENSE>();
-        st2k.load(p, head_off, rs, ck2, 0);
-        st.load(p, head_off, rs, ck2, 1);
+    // One chunk c (stage s0): the load of chunk c+LOOK is issued, the two
+    // halves of c run (the second also reads K of chunk c+1), then every
+    // wavefront waits until chunk c+2 has landed (dense: stores chunk c+2)
+    // and the workgroup meets at the barrier.  s0 is a compile-time constant
+    // in each of the four unrolled copies below.
+    Stager<D, THREADS, DENSE> st2k;  // dense: chunk c+2, K part
+    auto chunk_step = [&](int s0) __attribute__((always_inline)) -> bool {
+      const int s1 = (s0 + 1) % STAGES;
+      const int sl = (s0 + LOOK) % STAGES;
+      const bool more = !it.done;
+      Chunk ckl = {0, 0, -1};
+      if (more) {
+        ckl = it.template chunk<DENSE>();
+        if (DENSE) {
+          st2k.load(p, head_off, rs, ckl, 0);
+          st.load(p, head_off, rs, ckl, 1);
+        } else {
+          Dma::issue(p.tiles, ckl.slot, stage(sl), wave, lane);
+        }
       }
       if (wave_active) {
-        half(sA, sB, 0, ring[cur], ring[cur], 1, v0, ring[st1], 0);
-        half(sB, sA, 1, ring[cur], ring[st1], 0, v1, ring[st1], 1);
+        half(sA, sB, 0, stage(s0), stage(s0), 1, v0, stage(s1), 0);
+        half(sB, sA, 1, stage(s0), stage(s1), 0, v1, stage(s1), 1);
       }
-      if (has2) {
-        st2k.store(ring[st2], 0);
-        st.store(ring[st2], 1);
+      if (more) {
+        if (DENSE) {
+          st2k.store(stage(sl), 0);
+          st.store(stage(sl), 1);
+        }
         ++ready;
         it.template advance<DENSE>(p.g, bh, p.cpb);
       }
-      __syncthreads();
+      if (!DENSE) {
+        if (more) wait_vmem<Dma::PER_WAVE>();
+        else wait_vmem<0>();
+      }
+      barrier_lds();
       --ready;
-      cur = st1;
+      const int sv = more ? seen(ckl) : 0;
       v0 = v1;
-      v1 = has2 ? seen(ck2) : 0;
+      if (DENSE) {
+        v1 = sv;
+      } else {
+        v1 = v2;
+        v2 = sv;
+      }
+      return ready > 0;
+    };
+    while (ready > 0) {
+      if (!chunk_step(0)) break;
+      if (!chunk_step(1)) break;
+      if (!chunk_step(2)) break;
+      if (!chunk_step(3)) break;
     }
 
     // ---- normalise and store the real rows (lane and lane ^ 32 share a row)
@@ -774,12 +857,15 @@ __global__ __launch_bounds__(256) void layout_kernel(Geo g, int32_t* __restrict_
   }
 }
 
-// Chunk images of K and V: one workgroup per (b, h, block, chunk) slot.
-// Rows past the block's real count are zero.
+// Chunk images of K and V in the LDS layout: one workgroup per (b, h,
+// block, chunk) slot.  Rows past the block's real count and the row pads are
+// zero.  The image is assembled in LDS and written out linearly, so every
+// store covers whole cache lines.
 template <int D>
 __global__ __launch_bounds__(256) void tile_kernel(const bf16_bits* __restrict__ k, const bf16_bits* __restrict__ v,
                                                    const int32_t* __restrict__ tok, Geo g, int L, int heads, int cpb,
                                                    bf16_bits* __restrict__ tiles) {
+  __shared__ __attribute__((aligned(16))) bf16_bits im[Lds<D>::ELEMS];
   __shared__ __attribute__((aligned(16))) bf16_bits vs[KCH][D + 8];
   const int cs = blockIdx.x;
   const int c = cs % cpb;
@@ -791,17 +877,21 @@ __global__ __launch_bounds__(256) void tile_kernel(const bf16_bits* __restrict__
   if (valid <= 0) return;  // slot past the block's chunks: never read
   const int64_t rs = (int64_t)heads * D;
   const int64_t head_off = (int64_t)b * L * rs + (int64_t)h * D;
-  bf16_bits* img = tiles + (int64_t)cs * Img<D>::ELEMS;
   constexpr int PIECES = KCH * D / 8;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  for (int s = threadIdx.x; s < KCH + D; s += 256) {  // the 16-byte pad of every K and V^T row
+    if (s < KCH) *(u32x4*)(im + Lds<D>::k_off(s, D)) = zero;
+    else *(u32x4*)(im + Lds<D>::v_off(s - KCH, KCH)) = zero;
+  }
   for (int s = threadIdx.x; s < PIECES; s += 256) {
     const int row = s / (D / 8), piece = s % (D / 8);
-    u32x4 kx = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
+    u32x4 kx = zero, vx = zero;
     if (row < valid) {
       const int64_t t = tok[bx.start + c * KCH + row];
       kx = *(const u32x4*)(k + head_off + t * rs + piece * 8);
       vx = *(const u32x4*)(v + head_off + t * rs + piece * 8);
     }
-    *(u32x4*)(img + row * D + piece * 8) = kx;
+    *(u32x4*)(im + Lds<D>::k_off(row, piece * 8)) = kx;
     *(u32x4*)&vs[row][piece * 8] = vx;
   }
   __syncthreads();
@@ -814,8 +904,12 @@ __global__ __launch_bounds__(256) void tile_kernel(const bf16_bits* __restrict__
       w[e] = (uint32_t)vs[k0][d] | ((uint32_t)vs[k1][d] << 16);
     }
     u32x4 x = {w[0], w[1], w[2], w[3]};
-    *(u32x4*)(img + Img<D>::KELEMS + d * KCH + piece * 8) = x;
+    *(u32x4*)(im + Lds<D>::v_off(d, piece * 8)) = x;
   }
+  __syncthreads();
+  u32x4* dst = (u32x4*)(tiles + (int64_t)cs * Lds<D>::ELEMS);
+  const u32x4* src = (const u32x4*)im;
+  for (int s = threadIdx.x; s < Lds<D>::ELEMS / 8; s += 256) dst[s] = src[s];
 }
 
 // Work of every item (query rows x real key tokens of the union of its
@@ -965,7 +1059,9 @@ static GroupShape group_shape(int vol) {
 
 int attn_chunks_per_block(int vol) { return (vol + KCH - 1) / KCH; }
 
-size_t attn_tile_bytes(int D, int64_t slots) { return (size_t)slots * 2 * KCH * D * sizeof(bf16_bits); }
+size_t attn_tile_bytes(int D, int64_t slots) {
+  return (size_t)slots * (D == 128 ? Lds<128>::ELEMS : Lds<64>::ELEMS) * sizeof(bf16_bits);
+}
 
 static const void* sparse_kernel(int D, bool grouped) {
   if (D == 128)
