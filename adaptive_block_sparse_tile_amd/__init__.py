@@ -24,8 +24,8 @@ SCHED_NAIVE = 1
 
 # every symbol include/fva.h declares
 EXPORTS = ["fva_num_blocks", "fva_route_workspace_bytes", "fva_attn_workspace_bytes", "fva_attn_workgroups",
-           "fva_route", "fva_sparse_attn", "fva_dense_attn_ref", "fva_trace_imbalance", "fva_last_error",
-           "fva_status_name"]
+           "fva_route", "fva_sparse_attn", "fva_attn_plan", "fva_attn_exec", "fva_dense_attn_ref",
+           "fva_trace_imbalance", "fva_last_error", "fva_status_name"]
 
 
 class FvaError(RuntimeError):
@@ -74,6 +74,10 @@ def load():
     lib.fva_sparse_attn.restype = ctypes.c_int
     lib.fva_sparse_attn.argtypes = [_P, _P, _P, _P, D, G, _P, ctypes.c_float, ctypes.c_int32, _P, _P,
                                     ctypes.c_size_t, _P]
+    lib.fva_attn_plan.restype = ctypes.c_int
+    lib.fva_attn_plan.argtypes = [_P, _P, D, G, _P, ctypes.c_int32, _P, ctypes.c_size_t, _P]
+    lib.fva_attn_exec.restype = ctypes.c_int
+    lib.fva_attn_exec.argtypes = [_P, _P, D, G, _P, ctypes.c_float, _P, _P, ctypes.c_size_t, _P]
     lib.fva_dense_attn_ref.restype = ctypes.c_int
     lib.fva_dense_attn_ref.argtypes = [_P, _P, _P, _P, D, ctypes.c_float, _P]
     lib.fva_trace_imbalance.restype = ctypes.c_int
@@ -190,6 +194,35 @@ def sparse_attn(q, k, v, grid, block, mask, scale=None, sched: str = "lpt", trac
                                   ctypes.byref(make_desc(*shape)), ctypes.byref(make_grid(grid, block)),
                                   mask.data_ptr(), float(scale), sch, tp, ws.data_ptr(), ws.numel(),
                                   _stream_ptr(stream)))
+    return o
+
+
+def attn_plan(k, v, grid, block, mask, sched: str = "lpt", ws=None, stream=None):
+    """First half of sparse_attn: chunk images, item costs and the schedule,
+    written into ws (allocated if None and returned)."""
+    shape = _check_qkv(k, k, v)
+    need = attn_workspace_bytes(shape, grid, block)
+    if ws is None:
+        ws = workspace(need, k.device)
+    sch = {"lpt": SCHED_LPT, "naive": SCHED_NAIVE}[sched]
+    _check(load().fva_attn_plan(k.data_ptr(), v.data_ptr(), ctypes.byref(make_desc(*shape)),
+                                ctypes.byref(make_grid(grid, block)), mask.data_ptr(), sch, ws.data_ptr(),
+                                ws.numel(), _stream_ptr(stream)))
+    return ws
+
+
+def attn_exec(q, grid, block, mask, ws, scale=None, trace=None, out=None, stream=None):
+    """Second half of sparse_attn: the attention kernel over the plan in ws."""
+    torch = _torch()
+    shape = _check_qkv(q, q, q)
+    D = shape[3]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = torch.empty_like(q) if out is None else out
+    tp = trace.data_ptr() if trace is not None else None
+    _check(load().fva_attn_exec(q.data_ptr(), o.data_ptr(), ctypes.byref(make_desc(*shape)),
+                                ctypes.byref(make_grid(grid, block)), mask.data_ptr(), float(scale), tp,
+                                ws.data_ptr(), ws.numel(), _stream_ptr(stream)))
     return o
 
 

@@ -196,15 +196,17 @@ fva_status fva_route(const void* q, const void* k, const fva_desc* desc, const f
   return ok();
 }
 
-fva_status fva_sparse_attn(const void* q, const void* k, const void* v, void* o, const fva_desc* desc,
-                           const fva_grid* grid, const uint32_t* mask, float scale, int32_t sched, uint64_t* trace,
-                           void* ws, size_t ws_bytes, void* stream) {
-  if (!q || !k || !v || !o || !mask) return fail(FVA_ERR_INVALID_ARG, "q, k, v, o and mask must not be null");
+// Shared validation and workspace views of the sparse attention calls.
+static fva_status sparse_setup(const void* q, const void* k, const void* v, void* o, bool need_q, bool need_kv,
+                               const fva_desc* desc, const fva_grid* grid, const uint32_t* mask, float scale,
+                               bool check_scale_arg, int32_t sched, void* ws, size_t ws_bytes, fva::AttnLaunch* a) {
+  if ((need_q && (!q || !o)) || (need_kv && (!k || !v)) || !mask)
+    return fail(FVA_ERR_INVALID_ARG, "tensor and mask pointers must not be null");
   fva_status st = check_desc(desc);
   if (st != FVA_OK) return st;
   fva::Geo g;
   if ((st = check_grid(desc, grid, &g)) != FVA_OK) return st;
-  if ((st = check_scale(desc->D, scale)) != FVA_OK) return st;
+  if (check_scale_arg && (st = check_scale(desc->D, scale)) != FVA_OK) return st;
   if (sched != FVA_SCHED_LPT && sched != FVA_SCHED_NAIVE) return fail(FVA_ERR_INVALID_ARG, "unknown schedule %d", sched);
   const int64_t items = (int64_t)desc->B * desc->heads * g.N;
   const int64_t slots = items * fva::attn_chunks_per_block(g.bt * g.bh * g.bw);
@@ -213,25 +215,58 @@ fva_status fva_sparse_attn(const void* q, const void* k, const void* v, void* o,
     return fail(FVA_ERR_UNSUPPORTED, "B*heads = %lld > %d not supported", (long long)desc->B * desc->heads, kMaxHeads);
   const AttnWs lay = attn_ws_layout(desc, g);
   if ((st = check_ws(ws, ws_bytes, lay.total)) != FVA_OK) return st;
-
   char* w = (char*)ws;
+  a->q = q; a->k = k; a->v = v; a->o = o;
+  a->B = desc->B; a->L = desc->L; a->heads = desc->heads; a->D = desc->D;
+  a->g = g;
+  a->mask = mask;
+  a->scale = scale;
+  a->trace = nullptr;
+  a->tok = (int32_t*)(w + lay.tok);
+  a->blk_cnt = (int32_t*)(w + lay.cnt);
+  a->tiles = (uint16_t*)(w + lay.tiles);
+  a->keys = (uint64_t*)(w + lay.keys);
+  a->rank = (uint32_t*)(w + lay.rank);
+  a->order = (int32_t*)(w + lay.order);
+  a->head_pos = (int32_t*)(w + lay.head_pos);
+  a->qoff = (int32_t*)(w + lay.qoff);
+  a->qctr = (uint32_t*)(w + lay.qctr);
+  return FVA_OK;
+}
+
+fva_status fva_sparse_attn(const void* q, const void* k, const void* v, void* o, const fva_desc* desc,
+                           const fva_grid* grid, const uint32_t* mask, float scale, int32_t sched, uint64_t* trace,
+                           void* ws, size_t ws_bytes, void* stream) {
   fva::AttnLaunch a;
-  a.q = q; a.k = k; a.v = v; a.o = o;
-  a.B = desc->B; a.L = desc->L; a.heads = desc->heads; a.D = desc->D;
-  a.g = g;
-  a.mask = mask;
-  a.scale = scale;
+  fva_status st = sparse_setup(q, k, v, o, true, true, desc, grid, mask, scale, true, sched, ws, ws_bytes, &a);
+  if (st != FVA_OK) return st;
   a.trace = trace;
-  a.tok = (int32_t*)(w + lay.tok);
-  a.blk_cnt = (int32_t*)(w + lay.cnt);
-  a.tiles = (uint16_t*)(w + lay.tiles);
-  a.keys = (uint64_t*)(w + lay.keys);
-  a.rank = (uint32_t*)(w + lay.rank);
-  a.order = (int32_t*)(w + lay.order);
-  a.head_pos = (int32_t*)(w + lay.head_pos);
-  a.qoff = (int32_t*)(w + lay.qoff);
-  a.qctr = (uint32_t*)(w + lay.qctr);
-  hipError_t e = fva::launch_sparse_attn(a, sched == FVA_SCHED_LPT, (hipStream_t)stream);
+  hipError_t e = fva::launch_sparse_plan(a, sched == FVA_SCHED_LPT, (hipStream_t)stream);
+  if (e != hipSuccess) return device_error(e, "sparse attention plan launch");
+  e = fva::launch_sparse_exec(a, (hipStream_t)stream);
+  if (e != hipSuccess) return device_error(e, "sparse attention launch");
+  return ok();
+}
+
+fva_status fva_attn_plan(const void* k, const void* v, const fva_desc* desc, const fva_grid* grid,
+                         const uint32_t* mask, int32_t sched, void* ws, size_t ws_bytes, void* stream) {
+  fva::AttnLaunch a;
+  fva_status st = sparse_setup(nullptr, k, v, nullptr, false, true, desc, grid, mask, 0.f, false, sched, ws, ws_bytes,
+                               &a);
+  if (st != FVA_OK) return st;
+  hipError_t e = fva::launch_sparse_plan(a, sched == FVA_SCHED_LPT, (hipStream_t)stream);
+  if (e != hipSuccess) return device_error(e, "sparse attention plan launch");
+  return ok();
+}
+
+fva_status fva_attn_exec(const void* q, void* o, const fva_desc* desc, const fva_grid* grid, const uint32_t* mask,
+                         float scale, uint64_t* trace, void* ws, size_t ws_bytes, void* stream) {
+  fva::AttnLaunch a;
+  fva_status st = sparse_setup(q, nullptr, nullptr, o, true, false, desc, grid, mask, scale, true, FVA_SCHED_LPT, ws,
+                               ws_bytes, &a);
+  if (st != FVA_OK) return st;
+  a.trace = trace;
+  hipError_t e = fva::launch_sparse_exec(a, (hipStream_t)stream);
   if (e != hipSuccess) return device_error(e, "sparse attention launch");
   return ok();
 }

@@ -1085,13 +1085,9 @@ int attn_persistent_workgroups(int D, int block_volume, int* err) {
   return cus * occ;
 }
 
-hipError_t launch_sparse_attn(const AttnLaunch& a, bool lpt, hipStream_t st) {
-  const int BH = a.B * a.heads;
-  const int words = (a.g.N + 31) / 32;
+static AttnParams sparse_params(const AttnLaunch& a) {
   const int vol = a.g.bt * a.g.bh * a.g.bw;
-  const int cpb = attn_chunks_per_block(vol);
   const GroupShape gs = group_shape(vol);
-
   AttnParams prm = {};
   prm.q = (const bf16_bits*)a.q;
   prm.k = (const bf16_bits*)a.k;
@@ -1101,8 +1097,8 @@ hipError_t launch_sparse_attn(const AttnLaunch& a, bool lpt, hipStream_t st) {
   prm.L = a.L;
   prm.heads = a.heads;
   prm.g = a.g;
-  prm.words = words;
-  prm.cpb = cpb;
+  prm.words = (a.g.N + 31) / 32;
+  prm.cpb = attn_chunks_per_block(vol);
   prm.mask = a.mask;
   prm.tok = a.tok;
   prm.tiles = a.tiles;
@@ -1117,11 +1113,16 @@ hipError_t launch_sparse_attn(const AttnLaunch& a, bool lpt, hipStream_t st) {
   prm.gH = (a.g.nH + gs.gh - 1) / gs.gh;
   prm.gW = (a.g.nW + gs.gw - 1) / gs.gw;
   prm.n_groups = prm.gT * prm.gH * prm.gW;
-  prm.n_items = BH * prm.n_groups;
+  prm.n_items = a.B * a.heads * prm.n_groups;
   prm.scale_log2 = a.scale * 1.4426950408889634f;
   prm.trace = a.trace;
-  const int n_items = prm.n_items, per_head = prm.n_groups;
+  return prm;
+}
 
+hipError_t launch_sparse_plan(const AttnLaunch& a, bool lpt, hipStream_t st) {
+  const AttnParams prm = sparse_params(a);
+  const int BH = a.B * a.heads;
+  const int n_items = prm.n_items, per_head = prm.n_groups, cpb = prm.cpb;
   hipLaunchKernelGGL(layout_kernel, dim3(a.g.N), dim3(256), 0, st, a.g, a.tok, a.blk_cnt);
   const unsigned slots = (unsigned)(BH * a.g.N * cpb);
   if (a.D == 128)
@@ -1139,14 +1140,17 @@ hipError_t launch_sparse_attn(const AttnLaunch& a, bool lpt, hipStream_t st) {
                        n_items, per_head, a.rank);
   hipLaunchKernelGGL(scatter_kernel, dim3((n_items + 255) / 256), dim3(256), 0, st, a.rank, a.head_pos, n_items,
                      per_head, lpt, a.order);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
 
+hipError_t launch_sparse_exec(const AttnLaunch& a, hipStream_t st) {
+  AttnParams prm = sparse_params(a);
+  const int vol = a.g.bt * a.g.bh * a.g.bw;
   int err = 0;
   const int grid = attn_persistent_workgroups(a.D, vol, &err);
   if (err) return hipErrorInvalidValue;
   void* args[] = {&prm};
-  return hipLaunchKernel(sparse_kernel(a.D, gs.wpb < WAVES), dim3(grid), dim3(WAVES * 64), args, 0, st);
+  return hipLaunchKernel(sparse_kernel(a.D, group_shape(vol).wpb < WAVES), dim3(grid), dim3(WAVES * 64), args, 0, st);
 }
 
 hipError_t launch_dense_attn(const void* q, const void* k, const void* v, void* o, int B, int L, int heads, int D,

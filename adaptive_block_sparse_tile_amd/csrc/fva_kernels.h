@@ -47,7 +47,10 @@ size_t attn_tile_bytes(int D, int64_t slots);
 // Persistent workgroups of the sparse kernel for (D, block volume) on the
 // current device.
 int attn_persistent_workgroups(int D, int block_volume, int* err);
-hipError_t launch_sparse_attn(const AttnLaunch& a, bool lpt, hipStream_t st);
+// plan: token table, chunk images, item costs and the LPT (or naive) queues
+// in the workspace; exec: the persistent attention kernel over that plan
+hipError_t launch_sparse_plan(const AttnLaunch& a, bool lpt, hipStream_t st);
+hipError_t launch_sparse_exec(const AttnLaunch& a, hipStream_t st);
 hipError_t launch_dense_attn(const void* q, const void* k, const void* v, void* o, int B, int L, int heads, int D,
                              float scale, hipStream_t st);
 

@@ -145,6 +145,20 @@ fva_status fva_sparse_attn(const void* q, const void* k, const void* v, void* o,
                            const fva_grid* grid, const uint32_t* mask, float scale, int32_t sched, uint64_t* trace,
                            void* ws, size_t ws_bytes, void* stream);
 
+/* fva_sparse_attn in two calls, for callers that time or overlap the two
+ * parts.  fva_attn_plan enqueues the preparation: the block-ordered token
+ * table, the 64-key chunk images of K and V, the work item costs (from mask)
+ * and the schedule, all written into ws.  fva_attn_exec enqueues the
+ * attention kernel that reads them.  exec must run after a plan with the same
+ * desc, grid, k, v, mask and sched (same stream, or ordered after it), with
+ * ws untouched in between; one plan serves one exec (the queue counters are
+ * consumed).  Arguments and errors as for fva_sparse_attn; plan does not read
+ * q, exec does not read k or v. */
+fva_status fva_attn_plan(const void* k, const void* v, const fva_desc* desc, const fva_grid* grid,
+                         const uint32_t* mask, int32_t sched, void* ws, size_t ws_bytes, void* stream);
+fva_status fva_attn_exec(const void* q, void* o, const fva_desc* desc, const fva_grid* grid, const uint32_t* mask,
+                         float scale, uint64_t* trace, void* ws, size_t ws_bytes, void* stream);
+
 /* Dense softmax attention over all L tokens (the FlashAttention baseline the
  * FVAttn abstract measures against), same numerics as fva_sparse_attn and
  * no workspace.  Errors: INVALID_ARG, SCALE, UNSUPPORTED, DEVICE. */

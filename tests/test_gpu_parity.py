@@ -283,3 +283,19 @@ def test_route_ties_lower_index_first(wl, period):
     assert not ((mg != mo).any(-1) & ok).any()
     assert np.array_equal(cg[ok], co[ok])
     assert kept.sum(-1).min() >= wl.k_floor
+
+
+@pytest.mark.parametrize("name", ["tiny", "wan14b", "long"])
+def test_plan_exec_equals_sparse_attn(name):
+    """fva_attn_plan + fva_attn_exec is fva_sparse_attn split in two: bitwise equal O."""
+    wl = fvgen.WORKLOADS[name]
+    (q, k, v), (qd, kd, vd) = _inputs(wl)
+    mask_g, _, _ = fva.route(qd, kd, wl.grid, wl.block, wl.top_p, wl.k_floor)
+    o1 = fva.sparse_attn(qd, kd, vd, wl.grid, wl.block, mask_g)
+    ws = fva.attn_plan(kd, vd, wl.grid, wl.block, mask_g)
+    o2 = fva.attn_exec(qd, wl.grid, wl.block, mask_g, ws)
+    ws = fva.attn_plan(kd, vd, wl.grid, wl.block, mask_g, sched="naive", ws=ws)
+    o3 = fva.attn_exec(qd, wl.grid, wl.block, mask_g, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(o1.view(torch.int16), o3.view(torch.int16))
