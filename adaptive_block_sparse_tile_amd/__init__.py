@@ -24,7 +24,7 @@ SCHED_NAIVE = 1
 
 # every symbol include/fva.h declares
 EXPORTS = ["fva_num_blocks", "fva_route_workspace_bytes", "fva_attn_workspace_bytes", "fva_attn_workgroups",
-           "fva_route", "fva_sparse_attn", "fva_attn_plan", "fva_attn_exec", "fva_dense_attn_ref",
+           "fva_route", "fva_static_mask", "fva_sparse_attn", "fva_attn_plan", "fva_attn_exec", "fva_dense_attn_ref",
            "fva_trace_imbalance", "fva_last_error", "fva_status_name"]
 
 
@@ -46,6 +46,10 @@ class Desc(ctypes.Structure):
 
 class RouteCfg(ctypes.Structure):
     _fields_ = [("top_p", ctypes.c_float), ("k_floor", ctypes.c_int32)]
+
+
+class StaticCfg(ctypes.Structure):
+    _fields_ = [("lt", ctypes.c_int32), ("lh", ctypes.c_int32), ("lw", ctypes.c_int32), ("anchor_t", ctypes.c_int32)]
 
 
 _lib = None
@@ -71,6 +75,8 @@ def load():
     lib.fva_attn_workgroups.argtypes = [D, G]
     lib.fva_route.restype = ctypes.c_int
     lib.fva_route.argtypes = [_P, _P, D, G, C, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.fva_static_mask.restype = ctypes.c_int
+    lib.fva_static_mask.argtypes = [D, G, ctypes.POINTER(StaticCfg), _P, _P, _P]
     lib.fva_sparse_attn.restype = ctypes.c_int
     lib.fva_sparse_attn.argtypes = [_P, _P, _P, _P, D, G, _P, ctypes.c_float, ctypes.c_int32, _P, _P,
                                     ctypes.c_size_t, _P]
@@ -195,6 +201,23 @@ def sparse_attn(q, k, v, grid, block, mask, scale=None, sched: str = "lpt", trac
                                   mask.data_ptr(), float(scale), sch, tp, ws.data_ptr(), ws.numel(),
                                   _stream_ptr(stream)))
     return o
+
+
+def static_mask(shape, grid, block, local=(1, 1, 1), anchor_t=0, out=None, device="cuda", stream=None):
+    """Static local-box + anchor-slab block mask of every (b, h) on the GPU -> (mask, kv_cnt)."""
+    torch = _torch()
+    B, L, heads, D = (int(x) for x in shape)
+    N = num_blocks(grid, block)
+    words = (N + 31) // 32
+    if out is None:
+        mask = torch.empty((B, heads, N, words), dtype=torch.int32, device=device)
+        cnt = torch.empty((B, heads, N), dtype=torch.int32, device=device)
+    else:
+        mask, cnt = out
+    cfg = StaticCfg(*[int(x) for x in local], int(anchor_t))
+    _check(load().fva_static_mask(ctypes.byref(make_desc(B, L, heads, D)), ctypes.byref(make_grid(grid, block)),
+                                  ctypes.byref(cfg), mask.data_ptr(), cnt.data_ptr(), _stream_ptr(stream)))
+    return mask, cnt
 
 
 def attn_plan(k, v, grid, block, mask, sched: str = "lpt", ws=None, stream=None):

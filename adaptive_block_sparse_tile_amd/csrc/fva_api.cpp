@@ -234,6 +234,23 @@ static fva_status sparse_setup(const void* q, const void* k, const void* v, void
   return FVA_OK;
 }
 
+fva_status fva_static_mask(const fva_desc* desc, const fva_grid* grid, const fva_static_cfg* cfg, uint32_t* mask,
+                           int32_t* kv_cnt, void* stream) {
+  if (!mask || !cfg) return fail(FVA_ERR_INVALID_ARG, "mask and cfg must not be null");
+  if (cfg->lt < 1 || cfg->lh < 1 || cfg->lw < 1)
+    return fail(FVA_ERR_INVALID_ARG, "local box %d x %d x %d must be at least 1 block", cfg->lt, cfg->lh, cfg->lw);
+  if (cfg->anchor_t < 0) return fail(FVA_ERR_INVALID_ARG, "anchor_t %d < 0", cfg->anchor_t);
+  fva_status st = check_desc(desc);
+  if (st != FVA_OK) return st;
+  fva::Geo g;
+  if ((st = check_grid(desc, grid, &g)) != FVA_OK) return st;
+  const int64_t rows = (int64_t)desc->B * desc->heads * g.N;
+  hipError_t e = fva::launch_static_mask(g, rows, cfg->lt, cfg->lh, cfg->lw, cfg->anchor_t, mask, kv_cnt,
+                                         (hipStream_t)stream);
+  if (e != hipSuccess) return device_error(e, "static mask launch");
+  return ok();
+}
+
 fva_status fva_sparse_attn(const void* q, const void* k, const void* v, void* o, const fva_desc* desc,
                            const fva_grid* grid, const uint32_t* mask, float scale, int32_t sched, uint64_t* trace,
                            void* ws, size_t ws_bytes, void* stream) {

@@ -12,6 +12,9 @@ namespace fva {
 hipError_t launch_pool(const void* q, const void* k, const Geo& g, int B, int L, int heads, int D, double* qbar,
                        double* kbar, uint32_t* status, hipStream_t st);
 hipError_t launch_scores(const double* qbar, const double* kbar, int BH, int N, int D, double* S, hipStream_t st);
+// Static block mask of every (b, h): rows = B*heads*N.
+hipError_t launch_static_mask(const Geo& g, int64_t rows, int lt, int lh, int lw, int anchor_t, uint32_t* mask,
+                              int32_t* kv_cnt, hipStream_t st);
 hipError_t launch_route_rows(const double* S, int64_t rows, int N, float top_p, int k_floor, uint32_t* mask,
                              int32_t* kv_cnt, uint32_t* status, hipStream_t st);
 

@@ -80,9 +80,17 @@ def main():
     ws_a = fva.workspace(fva.attn_workspace_bytes(shape, wl.grid, wl.block), q.device)
     stream = torch.cuda.current_stream()
 
+    def make_mask():
+        # the router, or for a static-mask workload the local + anchor block mask
+        if wl.static:
+            fva.static_mask(shape, wl.grid, wl.block, local=wl.static[0], anchor_t=wl.static[1], out=(mask, cnt),
+                            stream=stream)
+        else:
+            fva.route(q, k, wl.grid, wl.block, wl.top_p, wl.k_floor, ws=ws_r, out=(mask, cnt, status), stream=stream)
+
     def step():
-        # one layer: route, then the sparse attention call (plan + attention kernel)
-        fva.route(q, k, wl.grid, wl.block, wl.top_p, wl.k_floor, ws=ws_r, out=(mask, cnt, status), stream=stream)
+        # one layer: the mask, then the sparse attention call (plan + attention kernel)
+        make_mask()
         fva.attn_plan(k, v, wl.grid, wl.block, mask, sched=args.sched, ws=ws_a, stream=stream)
         fva.attn_exec(q, wl.grid, wl.block, mask, ws_a, out=o, stream=stream)
 
@@ -99,7 +107,7 @@ def main():
     start.record(stream)
     for s in range(args.steps):
         ev[s][0].record(stream)
-        fva.route(q, k, wl.grid, wl.block, wl.top_p, wl.k_floor, ws=ws_r, out=(mask, cnt, status), stream=stream)
+        make_mask()
         ev[s][1].record(stream)
         fva.attn_plan(k, v, wl.grid, wl.block, mask, sched=args.sched, ws=ws_a, stream=stream)
         ev[s][2].record(stream)
@@ -165,7 +173,9 @@ def main():
         cpu = _cpu_baseline(wl, host, mask_h, counts, args.oracle_items)
 
     res = {
-        "metric": "effective TFLOP/s of routed sparse attention per layer (Wan 27280-token, 40-head layer)",
+        "metric": ("effective TFLOP/s of block-sparse attention per layer under a static local + anchor block mask"
+                   if wl.static else
+                   "effective TFLOP/s of routed sparse attention per layer (Wan 27280-token, 40-head layer)"),
         "value": round(eff_tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -178,9 +188,11 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded smooth-field + noise Q/K/V; no model weights)",
         "config": {
-            "workload": "%s: B=%d, heads=%d, head_dim=%d, grid=%s=%d tokens, block=%s -> %d blocks, "
-                        "top_p=%g, k_floor=%d, sched=%s" % (wl.name, B, heads, D, list(wl.grid), L, list(wl.block),
-                                                             N, wl.top_p, wl.k_floor, args.sched),
+            "workload": "%s: B=%d, heads=%d, head_dim=%d, grid=%s=%d tokens, block=%s -> %d blocks, %s, sched=%s"
+                        % (wl.name, B, heads, D, list(wl.grid), L, list(wl.block), N,
+                           ("static mask: local boxes %s blocks, anchor slabs every %d temporal blocks"
+                            % (list(wl.static[0]), wl.static[1])) if wl.static else
+                           "top_p=%g, k_floor=%d" % (wl.top_p, wl.k_floor), args.sched),
         },
         "ms_per_layer": round(ms_step, 4),
         "route_ms": round(route_ms, 4),
@@ -252,7 +264,10 @@ def _cpu_baseline(wl, host, mask_h, counts, n_items):
     print("[bench] cpu baseline: oracle router + %d attention items on %d threads" % (n_items, threads),
           file=sys.stderr, flush=True)
     t0 = time.time()
-    oracle.route(q, k, wl.grid, wl.block, wl.top_p, wl.k_floor, nthreads=threads)
+    if wl.static:
+        oracle.static_mask(wl.grid, wl.block, wl.static[0], wl.static[1], B=B, heads=heads)
+    else:
+        oracle.route(q, k, wl.grid, wl.block, wl.top_p, wl.k_floor, nthreads=threads)
     route_s = time.time() - t0
     kept = ((mask_h[..., :, None] >> np.arange(32, dtype=np.uint32)) & 1).reshape(B * heads * N, -1)[:, :N]
     cost = counts[np.arange(B * heads * N) % N] * (kept * counts[None, :]).sum(1)
@@ -272,8 +287,9 @@ def _cpu_baseline(wl, host, mask_h, counts, n_items):
         "cores": threads,
         "kind": "oracle",
         "sample": "%d of %d work items (heaviest, lightest, seeded random), %.2f%% of the layer's effective FLOPs; "
-                  "attention %.1fs, full router %.2fs; whole layer extrapolated %.0fs"
-                  % (len(items), cost.size, 100 * flop / total_flop, attn_s, route_s,
+                  "attention %.1fs, full %s %.2fs; whole layer extrapolated %.0fs"
+                  % (len(items), cost.size, 100 * flop / total_flop, attn_s,
+                     "static mask" if wl.static else "router", route_s,
                      route_s + attn_s * total_flop / flop),
     }
 

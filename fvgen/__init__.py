@@ -84,6 +84,7 @@ class Workload:
     k_floor: int
     batch: int = 1
     global_heads: tuple = field(default_factory=tuple)   # (first_head, tau) overrides
+    static: tuple = field(default_factory=tuple)         # ((lt, lh, lw), anchor_t): static block mask, no router
 
     @property
     def L(self) -> int:
@@ -111,6 +112,10 @@ WORKLOADS = {
     "720p": Workload("720p", 3, 40, 128, (21, 45, 80), (4, 8, 8), 8, "loguniform", (0.3, 6.0), 0.95, 16,
                      global_heads=(36, 0.2)),
     "long": Workload("long", 4, 5, 128, (96, 64, 64), (4, 4, 4), 16, "list", (0.5, 1.0, 2.0, 4.0, 8.0), 0.85, 32),
+    # the long-video grid under a static local + anchor block mask: local boxes of 2 x 16 x 16 blocks (8 latent
+    # frames, whole frames), anchor slabs every 6 temporal blocks (24 latent frames)
+    "static": Workload("static", 5, 5, 128, (96, 64, 64), (4, 4, 4), 16, "list", (0.5, 1.0, 2.0, 4.0, 8.0), 0.0, 1,
+                       static=((2, 16, 16), 6)),
 }
 
 

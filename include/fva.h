@@ -122,6 +122,33 @@ fva_status fva_route(const void* q, const void* k, const fva_desc* desc, const f
                      const fva_route_cfg* cfg, uint32_t* mask, int32_t* kv_cnt, uint32_t* status, void* ws,
                      size_t ws_bytes, void* stream);
 
+/* Static block mask: a second source of masks for fva_sparse_attn besides
+ * the router (Sol-Attn article, section 3: tokens attend in full inside
+ * their local window, and anchors link every window; here both rules act on
+ * block coordinates).  With (t, y, x) the block coordinates of query block i
+ * and key block j:
+ *   kept(i, j) = (t_i/lt == t_j/lt && y_i/lh == y_j/lh && x_i/lw == x_j/lw)
+ *             || (anchor_t > 0 && (t_i % anchor_t == 0 || t_j % anchor_t == 0))
+ * (integer division): local boxes of lt x lh x lw blocks partition the block
+ * grid, and the block slabs at temporal indices that are multiples of
+ * anchor_t are anchors, kept by every row and keeping every block.  Every
+ * row keeps at least its own block.  On a (T, 1, 1) grid of (1, 1, 1)
+ * blocks this is the article's token mask with block_size = lt and
+ * anchor_stride = anchor_t. */
+typedef struct {
+  int32_t lt, lh, lw;  /* local box, in blocks; each >= 1 */
+  int32_t anchor_t;    /* anchor period along t, in blocks; 0 = no anchors */
+} fva_static_cfg;
+
+/* Writes the static mask of every (b, h) (the same pattern each time) and
+ * its kept counts, in the layout fva_route writes.
+ *   mask    out, uint32 [B, heads, N, ceil(N/32)] (device)
+ *   kv_cnt  out, int32 [B, heads, N] (device, nullable)
+ * Errors: INVALID_ARG (null mask, lt/lh/lw < 1, anchor_t < 0), SHAPE,
+ * UNSUPPORTED, DEVICE.  No workspace. */
+fva_status fva_static_mask(const fva_desc* desc, const fva_grid* grid, const fva_static_cfg* cfg, uint32_t* mask,
+                           int32_t* kv_cnt, void* stream);
+
 /* Block-sparse attention (VSA guide sections 1 and 6: each query block
  * attends only to its selected key/value blocks; ragged edge blocks run on
  * their real prefix and padding never acts as a key).  For every real token

@@ -204,6 +204,37 @@ def real_pairs(grid, block, mask) -> int:
     return int(_load().fvo_real_pairs(g.ctypes.data, mask.ctypes.data, rows))
 
 
+def static_mask(grid, block, local=(1, 1, 1), anchor_t=0, B=1, heads=1):
+    """Static block mask: local boxes plus anchor slabs.
+
+    Sol-Attn article (bjdmk.com.cn), section 3.2: a query-key pair is kept
+    when both lie in the same local window or when either is an anchor.  The
+    rule is applied to block coordinates: (t, y, x) of a block is its origin
+    (from the oracle's own block table) divided by the block size; the local
+    windows are boxes of local = (lt, lh, lw) blocks partitioning the block
+    grid; the anchors are the blocks whose temporal coordinate is a multiple
+    of anchor_t (none when anchor_t == 0).
+
+    Returns (mask uint32 [B, heads, N, ceil(N/32)], counts int32 [B, heads, N]),
+    the same pattern for every (b, h).
+    """
+    tab = block_table(grid, block)
+    coords = tab[:, 0:3].astype(np.int64) // np.array(block, dtype=np.int64)
+    box = coords // np.array(local, dtype=np.int64)
+    keep = (box[:, None, :] == box[None, :, :]).all(-1)
+    if anchor_t > 0:
+        anchor = coords[:, 0] % anchor_t == 0
+        keep = keep | anchor[:, None] | anchor[None, :]
+    N = keep.shape[0]
+    words = (N + 31) // 32
+    padded = np.zeros((N, words * 32), dtype=np.uint64)
+    padded[:, :N] = keep
+    row = (padded.reshape(N, words, 32) << np.arange(32, dtype=np.uint64)).sum(-1).astype(np.uint32)
+    mask = np.broadcast_to(row, (B, heads, N, words)).copy()
+    counts = np.broadcast_to(keep.sum(1).astype(np.int32), (B, heads, N)).copy()
+    return mask, counts
+
+
 def dense_mask(B, heads, N) -> np.ndarray:
     words = (N + 31) // 32
     m = np.zeros((B, heads, N, words), dtype=np.uint32)
