@@ -21,10 +21,13 @@ STATUS_NAMES = ["FVA_OK", "FVA_ERR_INVALID_ARG", "FVA_ERR_SHAPE", "FVA_ERR_TOPK"
                 "FVA_ERR_WORKSPACE", "FVA_ERR_UNSUPPORTED", "FVA_ERR_DEVICE"]
 SCHED_LPT = 0
 SCHED_NAIVE = 1
+SCHED_XCD = 2
+SCHEDS = {"lpt": SCHED_LPT, "naive": SCHED_NAIVE, "xcd": SCHED_XCD}
 
 # every symbol include/fva.h declares
 EXPORTS = ["fva_num_blocks", "fva_route_workspace_bytes", "fva_attn_workspace_bytes", "fva_attn_workgroups",
-           "fva_route", "fva_static_mask", "fva_sparse_attn", "fva_attn_plan", "fva_attn_exec", "fva_dense_attn_ref",
+           "fva_route", "fva_static_mask", "fva_sparse_attn", "fva_attn_plan", "fva_attn_exec", "fva_sasa_workspace_bytes", "fva_sasa",
+           "fva_dense_attn_ref",
            "fva_trace_imbalance", "fva_last_error", "fva_status_name"]
 
 
@@ -81,9 +84,13 @@ def load():
     lib.fva_sparse_attn.argtypes = [_P, _P, _P, _P, D, G, _P, ctypes.c_float, ctypes.c_int32, _P, _P,
                                     ctypes.c_size_t, _P]
     lib.fva_attn_plan.restype = ctypes.c_int
-    lib.fva_attn_plan.argtypes = [_P, _P, D, G, _P, ctypes.c_int32, _P, ctypes.c_size_t, _P]
+    lib.fva_attn_plan.argtypes = [_P, _P, D, G, _P, ctypes.c_int32, _P, _P, ctypes.c_size_t, _P]
     lib.fva_attn_exec.restype = ctypes.c_int
-    lib.fva_attn_exec.argtypes = [_P, _P, D, G, _P, ctypes.c_float, _P, _P, ctypes.c_size_t, _P]
+    lib.fva_attn_exec.argtypes = [_P, _P, D, G, _P, ctypes.c_float, ctypes.c_int32, _P, _P, ctypes.c_size_t, _P]
+    lib.fva_sasa_workspace_bytes.restype = ctypes.c_size_t
+    lib.fva_sasa_workspace_bytes.argtypes = [D, G, ctypes.c_int32]
+    lib.fva_sasa.restype = ctypes.c_int
+    lib.fva_sasa.argtypes = [D, G, _P, _P, ctypes.c_size_t, ctypes.c_int32, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
     lib.fva_dense_attn_ref.restype = ctypes.c_int
     lib.fva_dense_attn_ref.argtypes = [_P, _P, _P, _P, D, ctypes.c_float, _P]
     lib.fva_trace_imbalance.restype = ctypes.c_int
@@ -194,7 +201,7 @@ def sparse_attn(q, k, v, grid, block, mask, scale=None, sched: str = "lpt", trac
     need = attn_workspace_bytes(shape, grid, block)
     if ws is None:
         ws = workspace(need, q.device)
-    sch = {"lpt": SCHED_LPT, "naive": SCHED_NAIVE}[sched]
+    sch = SCHEDS[sched]
     tp = trace.data_ptr() if trace is not None else None
     _check(load().fva_sparse_attn(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                   ctypes.byref(make_desc(*shape)), ctypes.byref(make_grid(grid, block)),
@@ -220,22 +227,24 @@ def static_mask(shape, grid, block, local=(1, 1, 1), anchor_t=0, out=None, devic
     return mask, cnt
 
 
-def attn_plan(k, v, grid, block, mask, sched: str = "lpt", ws=None, stream=None):
+def attn_plan(k, v, grid, block, mask, sched: str = "lpt", head_xcd=None, ws=None, stream=None):
     """First half of sparse_attn: chunk images, item costs and the schedule,
-    written into ws (allocated if None and returned)."""
+    written into ws (allocated if None and returned).  head_xcd: optional
+    device int32 [B*heads] (from sasa) for sched="xcd"."""
     shape = _check_qkv(k, k, v)
     need = attn_workspace_bytes(shape, grid, block)
     if ws is None:
         ws = workspace(need, k.device)
-    sch = {"lpt": SCHED_LPT, "naive": SCHED_NAIVE}[sched]
+    hx = head_xcd.data_ptr() if head_xcd is not None else None
     _check(load().fva_attn_plan(k.data_ptr(), v.data_ptr(), ctypes.byref(make_desc(*shape)),
-                                ctypes.byref(make_grid(grid, block)), mask.data_ptr(), sch, ws.data_ptr(),
-                                ws.numel(), _stream_ptr(stream)))
+                                ctypes.byref(make_grid(grid, block)), mask.data_ptr(), SCHEDS[sched], hx,
+                                ws.data_ptr(), ws.numel(), _stream_ptr(stream)))
     return ws
 
 
-def attn_exec(q, grid, block, mask, ws, scale=None, trace=None, out=None, stream=None):
-    """Second half of sparse_attn: the attention kernel over the plan in ws."""
+def attn_exec(q, grid, block, mask, ws, scale=None, sched: str = "lpt", trace=None, out=None, stream=None):
+    """Second half of sparse_attn: the attention kernel over the plan in ws
+    (sched as given to attn_plan)."""
     torch = _torch()
     shape = _check_qkv(q, q, q)
     D = shape[3]
@@ -244,9 +253,37 @@ def attn_exec(q, grid, block, mask, ws, scale=None, trace=None, out=None, stream
     o = torch.empty_like(q) if out is None else out
     tp = trace.data_ptr() if trace is not None else None
     _check(load().fva_attn_exec(q.data_ptr(), o.data_ptr(), ctypes.byref(make_desc(*shape)),
-                                ctypes.byref(make_grid(grid, block)), mask.data_ptr(), float(scale), tp,
-                                ws.data_ptr(), ws.numel(), _stream_ptr(stream)))
+                                ctypes.byref(make_grid(grid, block)), mask.data_ptr(), float(scale), SCHEDS[sched],
+                                tp, ws.data_ptr(), ws.numel(), _stream_ptr(stream)))
     return o
+
+
+def sasa_workspace_bytes(shape, grid, block, rounds) -> int:
+    return load().fva_sasa_workspace_bytes(ctypes.byref(make_desc(*shape)), ctypes.byref(make_grid(grid, block)),
+                                           int(rounds))
+
+
+def sasa(shape, grid, block, mask, route_ws, rounds=4, out=None, ws=None, stream=None):
+    """Slack-aware augmentation of a routed mask on the GPU (8 XCDs as ranks).
+
+    route_ws: the workspace of the fva_route call that produced mask.
+    Returns (mask_out, kv_cnt, head_xcd int32 [B*heads], xcd_load int64 [16])."""
+    torch = _torch()
+    B, L, heads, D = (int(x) for x in shape)
+    desc, g = make_desc(B, L, heads, D), make_grid(grid, block)
+    if out is None:
+        mask_out = torch.empty_like(mask)
+        cnt = torch.empty(mask.shape[:-1], dtype=torch.int32, device=mask.device)
+    else:
+        mask_out, cnt = out
+    head_xcd = torch.empty(B * heads, dtype=torch.int32, device=mask.device)
+    xcd_load = torch.empty(16, dtype=torch.int64, device=mask.device)
+    if ws is None:
+        ws = workspace(sasa_workspace_bytes(shape, grid, block, rounds), mask.device)
+    _check(load().fva_sasa(ctypes.byref(desc), ctypes.byref(g), mask.data_ptr(), route_ws.data_ptr(),
+                           route_ws.numel(), int(rounds), mask_out.data_ptr(), cnt.data_ptr(), head_xcd.data_ptr(),
+                           xcd_load.data_ptr(), ws.data_ptr(), ws.numel(), _stream_ptr(stream)))
+    return mask_out, cnt, head_xcd, xcd_load
 
 
 def dense_attn_ref(q, k, v, scale=None, out=None, stream=None):

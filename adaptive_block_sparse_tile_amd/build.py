@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfva.so")
-SOURCES = ["fva_route.hip", "fva_static.hip", "fva_attn.hip", "fva_api.cpp"]
+SOURCES = ["fva_route.hip", "fva_static.hip", "fva_sasa.hip", "fva_attn.hip", "fva_api.cpp"]
 HEADERS = ["fva_dev.h", "fva_kernels.h"]
 
 HIPCC_FLAGS = [

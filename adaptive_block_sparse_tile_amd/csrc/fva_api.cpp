@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <algorithm>
 #include <map>
 #include <string>
 #include <tuple>
@@ -207,7 +208,8 @@ static fva_status sparse_setup(const void* q, const void* k, const void* v, void
   fva::Geo g;
   if ((st = check_grid(desc, grid, &g)) != FVA_OK) return st;
   if (check_scale_arg && (st = check_scale(desc->D, scale)) != FVA_OK) return st;
-  if (sched != FVA_SCHED_LPT && sched != FVA_SCHED_NAIVE) return fail(FVA_ERR_INVALID_ARG, "unknown schedule %d", sched);
+  if (sched != FVA_SCHED_LPT && sched != FVA_SCHED_NAIVE && sched != FVA_SCHED_XCD)
+    return fail(FVA_ERR_INVALID_ARG, "unknown schedule %d", sched);
   const int64_t items = (int64_t)desc->B * desc->heads * g.N;
   const int64_t slots = items * fva::attn_chunks_per_block(g.bt * g.bh * g.bw);
   if (slots >= ((int64_t)1 << 31)) return fail(FVA_ERR_UNSUPPORTED, "too many work items");
@@ -234,6 +236,56 @@ static fva_status sparse_setup(const void* q, const void* k, const void* v, void
   return FVA_OK;
 }
 
+// SASA workspace: per-row candidates int32 [rows][rounds], per-row costs
+// int64 [rows], heads per XCD int32 [8][BH], head counts int32 [8].
+struct SasaWs {
+  size_t cand, cost, slot, nh, total;
+};
+static SasaWs sasa_ws_layout(const fva_desc* d, const fva::Geo& g, int rounds) {
+  SasaWs w;
+  const size_t BH = (size_t)d->B * d->heads;
+  const size_t rows = BH * g.N;
+  size_t off = 0;
+  w.cand = off; off += align_up(rows * (size_t)std::max(rounds, 1) * sizeof(int32_t));
+  w.cost = off; off += align_up(rows * sizeof(int64_t));
+  w.slot = off; off += align_up(8 * BH * sizeof(int32_t));
+  w.nh = off; off += align_up(8 * sizeof(int32_t));
+  w.total = off;
+  return w;
+}
+
+size_t fva_sasa_workspace_bytes(const fva_desc* desc, const fva_grid* grid, int32_t rounds) {
+  fva::Geo g;
+  if (check_desc(desc) != FVA_OK || check_grid(desc, grid, &g) != FVA_OK || rounds < 0 || rounds > 8) return 0;
+  return sasa_ws_layout(desc, g, rounds).total;
+}
+
+fva_status fva_sasa(const fva_desc* desc, const fva_grid* grid, const uint32_t* mask_in, const void* route_ws,
+                    size_t route_ws_bytes, int32_t rounds, uint32_t* mask_out, int32_t* kv_cnt, int32_t* head_xcd,
+                    int64_t* xcd_load, void* ws, size_t ws_bytes, void* stream) {
+  if (!mask_in || !route_ws || !mask_out || !head_xcd || !xcd_load)
+    return fail(FVA_ERR_INVALID_ARG, "mask_in, route_ws, mask_out, head_xcd and xcd_load must not be null");
+  if (rounds < 0 || rounds > 8) return fail(FVA_ERR_INVALID_ARG, "rounds %d outside 0..8", rounds);
+  fva_status st = check_desc(desc);
+  if (st != FVA_OK) return st;
+  fva::Geo g;
+  if ((st = check_grid(desc, grid, &g)) != FVA_OK) return st;
+  if ((int64_t)desc->B * desc->heads > kMaxHeads)
+    return fail(FVA_ERR_UNSUPPORTED, "B*heads = %lld > %d not supported", (long long)desc->B * desc->heads, kMaxHeads);
+  const RouteWs rl = route_ws_layout(desc, g);
+  if (route_ws_bytes < rl.total)
+    return fail(FVA_ERR_WORKSPACE, "route workspace holds %zu bytes, the router's is %zu", route_ws_bytes, rl.total);
+  const SasaWs lay = sasa_ws_layout(desc, g, rounds);
+  if ((st = check_ws(ws, ws_bytes, lay.total)) != FVA_OK) return st;
+  char* w = (char*)ws;
+  const double* S = (const double*)((const char*)route_ws + rl.s);
+  hipError_t e = fva::launch_sasa(S, mask_in, g, desc->B * desc->heads, rounds, mask_out, kv_cnt, head_xcd, xcd_load,
+                                  (int32_t*)(w + lay.cand), (int64_t*)(w + lay.cost), (int32_t*)(w + lay.slot),
+                                  (int32_t*)(w + lay.nh), (hipStream_t)stream);
+  if (e != hipSuccess) return device_error(e, "sasa launch");
+  return ok();
+}
+
 fva_status fva_static_mask(const fva_desc* desc, const fva_grid* grid, const fva_static_cfg* cfg, uint32_t* mask,
                            int32_t* kv_cnt, void* stream) {
   if (!mask || !cfg) return fail(FVA_ERR_INVALID_ARG, "mask and cfg must not be null");
@@ -258,32 +310,33 @@ fva_status fva_sparse_attn(const void* q, const void* k, const void* v, void* o,
   fva_status st = sparse_setup(q, k, v, o, true, true, desc, grid, mask, scale, true, sched, ws, ws_bytes, &a);
   if (st != FVA_OK) return st;
   a.trace = trace;
-  hipError_t e = fva::launch_sparse_plan(a, sched == FVA_SCHED_LPT, (hipStream_t)stream);
+  hipError_t e = fva::launch_sparse_plan(a, sched, nullptr, (hipStream_t)stream);
   if (e != hipSuccess) return device_error(e, "sparse attention plan launch");
-  e = fva::launch_sparse_exec(a, (hipStream_t)stream);
+  e = fva::launch_sparse_exec(a, sched, (hipStream_t)stream);
   if (e != hipSuccess) return device_error(e, "sparse attention launch");
   return ok();
 }
 
 fva_status fva_attn_plan(const void* k, const void* v, const fva_desc* desc, const fva_grid* grid,
-                         const uint32_t* mask, int32_t sched, void* ws, size_t ws_bytes, void* stream) {
+                         const uint32_t* mask, int32_t sched, const int32_t* head_xcd, void* ws, size_t ws_bytes,
+                         void* stream) {
   fva::AttnLaunch a;
   fva_status st = sparse_setup(nullptr, k, v, nullptr, false, true, desc, grid, mask, 0.f, false, sched, ws, ws_bytes,
                                &a);
   if (st != FVA_OK) return st;
-  hipError_t e = fva::launch_sparse_plan(a, sched == FVA_SCHED_LPT, (hipStream_t)stream);
+  hipError_t e = fva::launch_sparse_plan(a, sched, head_xcd, (hipStream_t)stream);
   if (e != hipSuccess) return device_error(e, "sparse attention plan launch");
   return ok();
 }
 
 fva_status fva_attn_exec(const void* q, void* o, const fva_desc* desc, const fva_grid* grid, const uint32_t* mask,
-                         float scale, uint64_t* trace, void* ws, size_t ws_bytes, void* stream) {
+                         float scale, int32_t sched, uint64_t* trace, void* ws, size_t ws_bytes, void* stream) {
   fva::AttnLaunch a;
-  fva_status st = sparse_setup(q, nullptr, nullptr, o, true, false, desc, grid, mask, scale, true, FVA_SCHED_LPT, ws,
+  fva_status st = sparse_setup(q, nullptr, nullptr, o, true, false, desc, grid, mask, scale, true, sched, ws,
                                ws_bytes, &a);
   if (st != FVA_OK) return st;
   a.trace = trace;
-  hipError_t e = fva::launch_sparse_exec(a, (hipStream_t)stream);
+  hipError_t e = fva::launch_sparse_exec(a, sched, (hipStream_t)stream);
   if (e != hipSuccess) return device_error(e, "sparse attention launch");
   return ok();
 }

@@ -82,6 +82,7 @@ struct AttnParams {
   const int32_t* order;    // item order (sparse)
   const int32_t* qoff;     // [NXCD + 1] queue segments in order (sparse)
   uint32_t* qctr;          // [NXCD] pop counters (sparse)
+  int steal;               // sparse: an idle workgroup takes items from the other XCDs' queues
   int n_items;
   int q_tiles;  // dense: query tiles per (b, h)
   // sparse work items are groups of up to 4 query blocks: a (gt, gh, gw) box
@@ -397,7 +398,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
     } else {
       if (tid == 0) {
         int got = -1;
-        for (int t = 0; t < NXCD && got < 0; ++t) {
+        for (int t = 0; t < (p.steal ? NXCD : 1) && got < 0; ++t) {
           const int x = (my_xcd + t) % NXCD;
           const int n = p.qoff[x + 1] - p.qoff[x];
           if (n <= 0 || __atomic_load_n(&p.qctr[x], __ATOMIC_RELAXED) >= (uint32_t)n) continue;
@@ -955,7 +956,9 @@ __global__ __launch_bounds__(256) void cost_kernel(AttnParams p, const int32_t* 
 // each goes to the XCD with the least assigned cost (ties: lower XCD).
 // Writes each head's first position in the order array and the queue
 // segments qoff[0..NXCD].  NAIVE puts every head on queue 0 in head order.
+// forced (nullable): each head's XCD, given by the caller instead of chosen.
 __global__ __launch_bounds__(256) void head_plan_kernel(const uint64_t* __restrict__ keys, int N, int BH, bool lpt,
+                                                        const int32_t* __restrict__ forced,
                                                         int32_t* __restrict__ head_pos, int32_t* __restrict__ qoff) {
   extern __shared__ uint64_t hsh[];  // [BH] head costs, then [BH] int32 order
   uint64_t* hcost = hsh;
@@ -985,9 +988,12 @@ __global__ __launch_bounds__(256) void head_plan_kernel(const uint64_t* __restri
     for (int r = 0; r < BH; ++r) {
       const int hd = horder[r];
       int best = 0;
-      if (lpt)
+      if (forced) {
+        best = min(max(forced[hd], 0), NXCD - 1);
+      } else if (lpt) {
         for (int x = 1; x < NXCD; ++x)
           if (load[x] < load[best]) best = x;
+      }
       load[best] += hcost[hd];
       nh[best]++;
       head_pos[hd] = best;  // XCD for now
@@ -1119,7 +1125,8 @@ static AttnParams sparse_params(const AttnLaunch& a) {
   return prm;
 }
 
-hipError_t launch_sparse_plan(const AttnLaunch& a, bool lpt, hipStream_t st) {
+hipError_t launch_sparse_plan(const AttnLaunch& a, int sched, const int32_t* head_xcd, hipStream_t st) {
+  const bool lpt = sched != 1;  // LPT order within heads for both the stealing and the per-XCD schedules
   const AttnParams prm = sparse_params(a);
   const int BH = a.B * a.heads;
   const int n_items = prm.n_items, per_head = prm.n_groups, cpb = prm.cpb;
@@ -1134,7 +1141,7 @@ hipError_t launch_sparse_plan(const AttnLaunch& a, bool lpt, hipStream_t st) {
   hipLaunchKernelGGL(cost_kernel, dim3((n_items + 255) / 256), dim3(256), 0, st, prm, a.blk_cnt, a.keys, a.rank,
                      a.qctr);
   hipLaunchKernelGGL(head_plan_kernel, dim3(1), dim3(256), (size_t)BH * 12, st, a.keys, per_head, BH, lpt,
-                     a.head_pos, a.qoff);
+                     sched == 2 ? head_xcd : nullptr, a.head_pos, a.qoff);
   if (lpt)
     hipLaunchKernelGGL(rank_kernel, dim3((n_items + 255) / 256, (n_items + 2047) / 2048), dim3(256), 0, st, a.keys,
                        n_items, per_head, a.rank);
@@ -1143,8 +1150,9 @@ hipError_t launch_sparse_plan(const AttnLaunch& a, bool lpt, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_sparse_exec(const AttnLaunch& a, hipStream_t st) {
+hipError_t launch_sparse_exec(const AttnLaunch& a, int sched, hipStream_t st) {
   AttnParams prm = sparse_params(a);
+  prm.steal = sched != 2;
   const int vol = a.g.bt * a.g.bh * a.g.bw;
   int err = 0;
   const int grid = attn_persistent_workgroups(a.D, vol, &err);

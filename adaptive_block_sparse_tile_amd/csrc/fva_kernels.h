@@ -12,6 +12,11 @@ namespace fva {
 hipError_t launch_pool(const void* q, const void* k, const Geo& g, int B, int L, int heads, int D, double* qbar,
                        double* kbar, uint32_t* status, hipStream_t st);
 hipError_t launch_scores(const double* qbar, const double* kbar, int BH, int N, int D, double* S, hipStream_t st);
+// Slack-aware augmentation over the router's scores S (fp64 [BH, N, N]).
+hipError_t launch_sasa(const double* S, const uint32_t* mask_in, const Geo& g, int BH, int R, uint32_t* mask_out,
+                       int32_t* kv_cnt, int32_t* head_xcd, int64_t* xcd_load, int32_t* cand, int64_t* row_cost,
+                       int32_t* slot_head, int32_t* nh, hipStream_t st);
+
 // Static block mask of every (b, h): rows = B*heads*N.
 hipError_t launch_static_mask(const Geo& g, int64_t rows, int lt, int lh, int lw, int anchor_t, uint32_t* mask,
                               int32_t* kv_cnt, hipStream_t st);
@@ -52,8 +57,10 @@ size_t attn_tile_bytes(int D, int64_t slots);
 int attn_persistent_workgroups(int D, int block_volume, int* err);
 // plan: token table, chunk images, item costs and the LPT (or naive) queues
 // in the workspace; exec: the persistent attention kernel over that plan
-hipError_t launch_sparse_plan(const AttnLaunch& a, bool lpt, hipStream_t st);
-hipError_t launch_sparse_exec(const AttnLaunch& a, hipStream_t st);
+// sched: 0 LPT with stealing, 1 naive, 2 per-XCD without stealing (heads by
+// head_xcd if not null, else by the LPT rule)
+hipError_t launch_sparse_plan(const AttnLaunch& a, int sched, const int32_t* head_xcd, hipStream_t st);
+hipError_t launch_sparse_exec(const AttnLaunch& a, int sched, hipStream_t st);
 hipError_t launch_dense_attn(const void* q, const void* k, const void* v, void* o, int B, int L, int heads, int D,
                              float scale, hipStream_t st);
 

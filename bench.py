@@ -33,11 +33,14 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="wan14b")
-    ap.add_argument("--sched", default="lpt", choices=["lpt", "naive"])
+    ap.add_argument("--sched", default="lpt", choices=["lpt", "naive", "xcd"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--oracle-items", type=int, default=160, help="work items in the CPU oracle sample")
     ap.add_argument("--no-dense", action="store_true", help="skip timing the dense reference")
+    ap.add_argument("--sasa", type=int, default=0, metavar="R",
+                    help="also measure slack-aware augmentation with R rounds on the per-XCD schedule, with its "
+                         "error against the dense oracle on sampled items")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only copy 2 GiB device-to-device three times (reference for rocprofv3 FETCH/WRITE_SIZE)")
     args = ap.parse_args()
@@ -92,7 +95,7 @@ def main():
         # one layer: the mask, then the sparse attention call (plan + attention kernel)
         make_mask()
         fva.attn_plan(k, v, wl.grid, wl.block, mask, sched=args.sched, ws=ws_a, stream=stream)
-        fva.attn_exec(q, wl.grid, wl.block, mask, ws_a, out=o, stream=stream)
+        fva.attn_exec(q, wl.grid, wl.block, mask, ws_a, sched=args.sched, out=o, stream=stream)
 
     print("[bench] workload %s: generated inputs in %.1fs; warmup %d" % (wl.name, gen_s, args.warmup),
           file=sys.stderr, flush=True)
@@ -111,7 +114,7 @@ def main():
         ev[s][1].record(stream)
         fva.attn_plan(k, v, wl.grid, wl.block, mask, sched=args.sched, ws=ws_a, stream=stream)
         ev[s][2].record(stream)
-        fva.attn_exec(q, wl.grid, wl.block, mask, ws_a, out=o, stream=stream)
+        fva.attn_exec(q, wl.grid, wl.block, mask, ws_a, sched=args.sched, out=o, stream=stream)
         ev[s][3].record(stream)
     end.record(stream)
     torch.cuda.synchronize()
@@ -168,6 +171,10 @@ def main():
 
     traffic = _profiled_traffic(wl.name)
 
+    sasa = None
+    if args.sasa > 0 and not wl.static:
+        sasa = _sasa_leg(fva, wl, q, k, v, host, shape, ws_r, ws_a, stream, args)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = _cpu_baseline(wl, host, mask_h, counts, args.oracle_items)
@@ -218,6 +225,7 @@ def main():
             "traffic": traffic,
         },
         "cpu_baseline": cpu,
+        "sasa": sasa,
     }
     print(json.dumps(res), flush=True)
 
@@ -250,6 +258,93 @@ def _block_counts(wl):
     eh = [min(bh, H - i * bh) for i in range(-(-H // bh))]
     ew = [min(bw, W - i * bw) for i in range(-(-W // bw))]
     return np.array([a * b * c for a in et for b in eh for c in ew], dtype=np.int64)
+
+
+def _sasa_leg(fva, wl, q, k, v, host, shape, ws_r, ws_a, stream, args):
+    """Slack-aware augmentation on the per-XCD schedule: ms/layer with and
+    without it (same timing protocol as the main loop), and the mean absolute
+    error of O against dense attention (fp64 oracle) on sampled query blocks,
+    most of them blocks that received extra key blocks."""
+    import torch
+    import oracle
+    B, L, heads, D = shape
+    N = fva.num_blocks(wl.grid, wl.block)
+    o = torch.empty_like(q)
+    mask = torch.empty((B, heads, N, (N + 31) // 32), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((B, heads, N), dtype=torch.int32, device="cuda")
+    mask_s, cnt_s = torch.empty_like(mask), torch.empty_like(cnt)
+    status = torch.empty((1,), dtype=torch.int32, device="cuda")
+    sws = fva.workspace(fva.sasa_workspace_bytes(shape, wl.grid, wl.block, args.sasa), q.device)
+
+    def layer(aug):
+        fva.route(q, k, wl.grid, wl.block, wl.top_p, wl.k_floor, ws=ws_r, out=(mask, cnt, status), stream=stream)
+        m, hx = mask, None
+        if aug:
+            m, _, hx, _ = fva.sasa(shape, wl.grid, wl.block, mask, ws_r, rounds=args.sasa, out=(mask_s, cnt_s),
+                                   ws=sws, stream=stream)
+        fva.attn_plan(k, v, wl.grid, wl.block, m, sched="xcd", head_xcd=hx, ws=ws_a, stream=stream)
+        fva.attn_exec(q, wl.grid, wl.block, m, ws_a, sched="xcd", out=o, stream=stream)
+        return m
+
+    res = {}
+    outs = {}
+    for aug in (False, True):
+        for _ in range(args.warmup):
+            layer(aug)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            m = layer(aug)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res["ms_per_layer_sasa" if aug else "ms_per_layer_xcd"] = round(e0.elapsed_time(e1) / args.steps, 4)
+        outs[aug] = (o.clone(), m.clone())
+    _, _, _, load = fva.sasa(shape, wl.grid, wl.block, mask, ws_r, rounds=args.sasa, out=(mask_s, cnt_s), ws=sws)
+    torch.cuda.synchronize()
+    ld = load.cpu().numpy()
+    kept0 = outs[False][1].cpu().numpy().view(np.uint32)
+    kept1 = outs[True][1].cpu().numpy().view(np.uint32)
+    bits = lambda m: int(np.unpackbits(m.view(np.uint8)).sum())
+    grown = np.nonzero((kept1 != kept0).any(-1).reshape(-1))[0]
+    rng = np.random.default_rng(2)
+    pick = set(rng.choice(grown, size=min(24, grown.size), replace=False).tolist()) if grown.size else set()
+    while len(pick) < min(32, B * heads * N):
+        pick.add(int(rng.integers(B * heads * N)))
+    items = np.array(sorted(pick))
+    print("[bench] sasa: dense oracle on %d sampled items" % len(items), file=sys.stderr, flush=True)
+    qh, kh, vh = host
+    threads = max(1, min(16, os.cpu_count() or 1))
+    dense = oracle.attn(qh, kh, vh, wl.grid, wl.block, oracle.dense_mask(B, heads, N), 1.0 / math.sqrt(D),
+                        items=items, nthreads=threads)
+    tb = oracle.token_block(wl.grid, wl.block)
+    err = {}
+    for aug in (False, True):
+        out = outs[aug][0].view(torch.int16).cpu().numpy().view(np.uint16)
+        import fvgen
+        out = fvgen.bf16_to_f64(out)
+        e_all, e_grown = [], []
+        for it in items:
+            i, h, b = it % N, (it // N) % heads, it // (N * heads)
+            d = np.abs(out[b, tb == i, h] - dense[b, tb == i, h]).mean()
+            e_all.append(d)
+            if it in set(grown.tolist()):
+                e_grown.append(d)
+        err[aug] = (float(np.mean(e_all)), float(np.mean(e_grown)) if e_grown else None)
+    res.update({
+        "rounds": args.sasa,
+        "xcd_load_before": [int(x) for x in ld[:8]],
+        "xcd_added": [int(x) for x in ld[8:]],
+        "kept_blocks_before": bits(kept0),
+        "kept_blocks_after": bits(kept1),
+        "rows_augmented": int(grown.size),
+        "sampled_items": int(items.size),
+        "mean_abs_err_vs_dense": {"xcd": round(err[False][0], 6), "xcd_sasa": round(err[True][0], 6)},
+        "mean_abs_err_vs_dense_on_augmented_rows": {
+            "xcd": None if err[False][1] is None else round(err[False][1], 6),
+            "xcd_sasa": None if err[True][1] is None else round(err[True][1], 6)},
+    })
+    return res
 
 
 def _cpu_baseline(wl, host, mask_h, counts, n_items):

@@ -83,6 +83,11 @@ typedef struct {
  * NAIVE: one queue in (batch, head, query block) order. */
 #define FVA_SCHED_LPT 0
 #define FVA_SCHED_NAIVE 1
+/* XCD: the ranks of the FVAttn abstract's load balancing played by the 8 XCDs:
+ * heads are assigned as for LPT (or as fva_sasa assigned them, see
+ * fva_attn_plan) and each XCD serves only its own queue, without taking
+ * items from the others.  The launch puts 32 workgroups on each XCD. */
+#define FVA_SCHED_XCD 2
 
 /* Number of blocks prod ceil(dim/block) (VSA guide, section 3), or -1 when a
  * dimension is not positive.  Host only. */
@@ -161,7 +166,8 @@ fva_status fva_static_mask(const fva_desc* desc, const fva_grid* grid, const fva
  *            with no bit set is an error the caller must avoid (its O rows
  *            are written as zeros)
  *   scale    softmax scale; must be within 1e-6 of 1/sqrt(D)
- *   sched    FVA_SCHED_LPT or FVA_SCHED_NAIVE; both give bitwise equal O
+ *   sched    FVA_SCHED_LPT, FVA_SCHED_NAIVE or FVA_SCHED_XCD; all give bitwise
+ *            equal O
  *   trace    nullable device uint64 [fva_attn_workgroups()][4]: per
  *            workgroup first-item start, last-item end, summed item time
  *            (100 MHz ticks) and (items << 40 | xcc_id << 32 | hw_id)
@@ -180,11 +186,44 @@ fva_status fva_sparse_attn(const void* q, const void* k, const void* v, void* o,
  * desc, grid, k, v, mask and sched (same stream, or ordered after it), with
  * ws untouched in between; one plan serves one exec (the queue counters are
  * consumed).  Arguments and errors as for fva_sparse_attn; plan does not read
- * q, exec does not read k or v. */
+ * q, exec does not read k or v.  head_xcd (nullable device int32 [B*heads],
+ * used with FVA_SCHED_XCD only): the XCD (0..7) of each (b, h), as fva_sasa
+ * writes it; null assigns heads by the LPT rule.  exec must be given the
+ * same sched as plan. */
 fva_status fva_attn_plan(const void* k, const void* v, const fva_desc* desc, const fva_grid* grid,
-                         const uint32_t* mask, int32_t sched, void* ws, size_t ws_bytes, void* stream);
+                         const uint32_t* mask, int32_t sched, const int32_t* head_xcd, void* ws, size_t ws_bytes,
+                         void* stream);
 fva_status fva_attn_exec(const void* q, void* o, const fva_desc* desc, const fva_grid* grid, const uint32_t* mask,
-                         float scale, uint64_t* trace, void* ws, size_t ws_bytes, void* stream);
+                         float scale, int32_t sched, uint64_t* trace, void* ws, size_t ws_bytes, void* stream);
+
+/* Slack-aware sparse augmentation, one-GPU form (FVAttn abstract and
+ * summary, key modules 2 and 3: after load balancing, the slack left on the
+ * non-critical ranks is filled with extra high-value blocks chosen from the
+ * attention scores, without lengthening the critical path).  The ranks are
+ * the 8 XCDs.  Row cost = c_i * sum_{kept j} c_j real token pairs; head cost
+ * = the sum over its rows; heads go longest first (ties: lower head) to the
+ * least loaded XCD (ties: lower XCD); the heaviest XCD's load is the
+ * makespan M.  Every other XCD x offers, in rounds r = 1..rounds, each of its
+ * rows (heads in the order they were assigned to x, rows in block order) the
+ * r-th block the router dropped from that row, in the router's order (block
+ * score descending, lower index first); the longest prefix of these offers
+ * whose summed cost c_i * c_j fits M - load_x is added.  Run the attention
+ * with FVA_SCHED_XCD and this head_xcd so that each XCD serves its own heads.
+ *   mask_in    uint32 [B, heads, N, ceil(N/32)] from fva_route
+ *   route_ws   the workspace of that fva_route call (it holds the block
+ *              scores), untouched since
+ *   rounds     0..8 (0 copies the mask)
+ *   mask_out   out, same layout (may equal mask_in)
+ *   kv_cnt     out, int32 [B, heads, N] kept counts after augmentation (nullable)
+ *   head_xcd   out, int32 [B*heads]
+ *   xcd_load   out, int64 [16]: load of each XCD before (0..7) and the cost
+ *              added to it (8..15), in real token pairs
+ *   ws         device workspace of at least fva_sasa_workspace_bytes()
+ * Errors: INVALID_ARG, SHAPE, UNSUPPORTED, WORKSPACE, DEVICE. */
+size_t fva_sasa_workspace_bytes(const fva_desc* desc, const fva_grid* grid, int32_t rounds);
+fva_status fva_sasa(const fva_desc* desc, const fva_grid* grid, const uint32_t* mask_in, const void* route_ws,
+                    size_t route_ws_bytes, int32_t rounds, uint32_t* mask_out, int32_t* kv_cnt, int32_t* head_xcd,
+                    int64_t* xcd_load, void* ws, size_t ws_bytes, void* stream);
 
 /* Dense softmax attention over all L tokens (the FlashAttention baseline the
  * FVAttn abstract measures against), same numerics as fva_sparse_attn and

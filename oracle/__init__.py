@@ -235,6 +235,92 @@ def static_mask(grid, block, local=(1, 1, 1), anchor_t=0, B=1, heads=1):
     return mask, counts
 
 
+def sasa(scores: np.ndarray, mask: np.ndarray, grid, block, rounds: int, margin: float = MARGIN):
+    """Slack-aware sparse augmentation, one-GPU form (8 XCDs as the ranks).
+
+    FVAttn abstract and summary, key modules 2 and 3: after load balancing the
+    non-critical ranks have slack, filled with extra high-value blocks chosen
+    from the attention scores without lengthening the critical path.  Steps:
+      1. row cost = c_i * sum of c_j over the row's kept blocks (real token
+         pairs); head cost = sum over its rows;
+      2. heads by cost descending (ties: lower head) each go to the XCD with
+         the least load so far (ties: lower XCD); makespan M = max load;
+      3. on every XCD, offers in rounds r = 0..rounds-1: for each of its heads
+         (in assignment order) and each row (block order), the row's r-th
+         dropped block in the router's order (score descending, lower index
+         first; non-finite scores are never offered); offers are taken in
+         that order until the first one whose cost c_i * c_j no longer fits
+         M - load (rows without an r-th dropped block are passed over).
+    scores: fp64 [B, heads, N, N] (oracle.scores); mask: the routed mask.
+    Returns (mask_out, counts, head_xcd [B*heads], load [8], added [8],
+    flags [B, heads, N]) where a flagged row has two of its first rounds+1
+    dropped candidates within margin * max(1, |s|) of each other without being
+    equal (their order may differ under another fp64 rounding order).
+    """
+    B, heads, N, _ = scores.shape
+    BH = B * heads
+    c = block_table(grid, block)[:, 6].astype(np.int64)
+    keep = mask_to_bool(mask, N).reshape(BH, N, N)
+    S = scores.reshape(BH, N, N)
+    row_cost = c[None, :] * (keep * c[None, None, :]).sum(-1)
+    head_cost = row_cost.sum(1)
+    load = [0] * 8
+    heads_of = [[] for _ in range(8)]
+    head_xcd = np.zeros(BH, dtype=np.int32)
+    for h in sorted(range(BH), key=lambda h: (-int(head_cost[h]), h)):
+        x = min(range(8), key=lambda x: (load[x], x))
+        load[x] += int(head_cost[h])
+        heads_of[x].append(h)
+        head_xcd[h] = x
+    M = max(load)
+
+    # each row's first rounds+1 dropped blocks in the router's order
+    cand = np.full((BH, N, rounds + 1), -1, dtype=np.int64)
+    flags = np.zeros((BH, N), dtype=bool)
+    for h in range(BH):
+        for i in range(N):
+            js = np.nonzero(~keep[h, i] & np.isfinite(S[h, i]))[0]
+            if js.size == 0:
+                continue
+            order = js[np.lexsort((js, -S[h, i, js]))][: rounds + 1]
+            cand[h, i, : order.size] = order
+            sv = S[h, i, order]
+            gap = np.abs(np.diff(sv))
+            flags[h, i] = bool(((gap > 0) & (gap < margin * np.maximum(1.0, np.abs(sv[1:])))).any())
+
+    out = keep.copy()
+    added = [0] * 8
+    for x in range(8):
+        slack = M - load[x]
+        acc = 0
+        stop = False
+        for r in range(rounds):
+            for h in heads_of[x]:
+                for i in range(N):
+                    j = int(cand[h, i, r])
+                    if j < 0:
+                        continue
+                    cost = int(c[i] * c[j])
+                    if acc + cost > slack:
+                        stop = True
+                        break
+                    acc += cost
+                    out[h, i, j] = True
+                if stop:
+                    break
+            if stop:
+                break
+        added[x] = acc
+
+    words = (N + 31) // 32
+    padded = np.zeros((BH, N, words * 32), dtype=np.uint64)
+    padded[..., :N] = out
+    mask_out = (padded.reshape(BH, N, words, 32) << np.arange(32, dtype=np.uint64)).sum(-1).astype(np.uint32)
+    counts = out.sum(-1).astype(np.int32)
+    return (mask_out.reshape(B, heads, N, words), counts.reshape(B, heads, N), head_xcd,
+            np.array(load, dtype=np.int64), np.array(added, dtype=np.int64), flags.reshape(B, heads, N))
+
+
 def dense_mask(B, heads, N) -> np.ndarray:
     words = (N + 31) // 32
     m = np.zeros((B, heads, N, words), dtype=np.uint32)

@@ -295,7 +295,7 @@ def test_plan_exec_equals_sparse_attn(name):
     ws = fva.attn_plan(kd, vd, wl.grid, wl.block, mask_g)
     o2 = fva.attn_exec(qd, wl.grid, wl.block, mask_g, ws)
     ws = fva.attn_plan(kd, vd, wl.grid, wl.block, mask_g, sched="naive", ws=ws)
-    o3 = fva.attn_exec(qd, wl.grid, wl.block, mask_g, ws)
+    o3 = fva.attn_exec(qd, wl.grid, wl.block, mask_g, ws, sched="naive")
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
     assert torch.equal(o1.view(torch.int16), o3.view(torch.int16))

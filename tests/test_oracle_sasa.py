@@ -1,0 +1,95 @@
+"""Pins of the oracle's slack-aware sparse augmentation (one-GPU form).
+
+Checked against things other than the rule's own text: an independent stable
+argsort for each row's candidate order; the partition of head costs over the
+XCDs; that nothing is added to the critical XCD and no XCD passes the
+makespan; that every XCD either exhausts its offers or is left with less slack
+than the largest possible offer; superset of the routed mask; special cases
+with no slack (equal heads, dense rows, zero rounds)."""
+import numpy as np
+import pytest
+
+import fvgen
+import oracle
+
+
+def _routed(wl, q=None, k=None):
+    if q is None:
+        q, k, _ = fvgen.generate_qkv(wl)
+    S = oracle.scores(oracle.pool(q, wl.grid, wl.block), oracle.pool(k, wl.grid, wl.block))
+    mask, cnt, flags, st = oracle.route(q, k, wl.grid, wl.block, wl.top_p, wl.k_floor)
+    return S, mask
+
+
+def _wl(name, heads, grid, block, top_p, k_floor, D=64):
+    taus = tuple(np.linspace(0.4, 5.0, heads))
+    return fvgen.Workload(name, 61, heads, D, grid, block, 8, "list", taus, top_p, k_floor)
+
+
+CASES = [_wl("h12", 12, (9, 17, 23), (4, 8, 8), 0.8, 2), _wl("h11_small", 11, (6, 8, 8), (2, 4, 4), 0.7, 3),
+         fvgen.WORKLOADS["wan14b"]]
+
+
+@pytest.mark.parametrize("wl", CASES, ids=lambda w: w.name)
+def test_invariants(wl):
+    S, mask = _routed(wl)
+    rounds = 4
+    mo, co, hx, load, added, flags = oracle.sasa(S, mask, wl.grid, wl.block, rounds)
+    B, H, N, _ = S.shape
+    keep = oracle.mask_to_bool(mask, N).reshape(B * H, N, N)
+    out = oracle.mask_to_bool(mo, N).reshape(B * H, N, N)
+    assert (out >= keep).all()
+    assert np.array_equal(co.reshape(-1, N), out.sum(-1))
+    c = oracle.block_table(wl.grid, wl.block)[:, 6].astype(np.int64)
+    # head costs partition over the XCDs
+    head_cost = (c[None, :, None] * keep * c[None, None, :]).sum((1, 2))
+    for x in range(8):
+        assert load[x] == head_cost[hx == x].sum()
+    M = load.max()
+    assert added[np.argmax(load)] == 0
+    assert ((load + added) <= M).all()
+    # the added cost is what the new bits cost, per XCD
+    new = out & ~keep
+    per_head = (c[None, :, None] * new * c[None, None, :]).sum((1, 2))
+    for x in range(8):
+        assert added[x] == per_head[hx == x].sum()
+    # per row: the added blocks are the first ones of the dropped order (stable argsort of -score)
+    for h in range(B * H):
+        for i in range(N):
+            a = int(new[h, i].sum())
+            if a == 0:
+                continue
+            key = np.where(keep[h, i], np.inf, -S.reshape(B * H, N, N)[h, i])
+            order = np.argsort(key, kind="stable")
+            assert set(order[:a].tolist()) == set(np.nonzero(new[h, i])[0].tolist())
+            assert a <= rounds
+    # every XCD either ran out of offers or kept less slack than the largest offer
+    biggest = int(c.max()) ** 2
+    for x in range(8):
+        rows_x = [h for h in range(B * H) if hx[h] == x]
+        dropped = sum(int(min(rounds, (~keep[h]).sum(-1)[i])) for h in rows_x for i in range(N))
+        taken = int(sum(new[h].sum() for h in rows_x))
+        if taken < dropped:
+            assert M - (load[x] + added[x]) < biggest
+
+
+def test_no_slack_equal_heads():
+    wl = _wl("eq", 1, (9, 17, 23), (4, 8, 8), 0.8, 2)
+    q, k, _ = fvgen.generate_qkv(wl)
+    q8, k8 = np.repeat(q, 8, axis=2), np.repeat(k, 8, axis=2)
+    wl8 = _wl("eq8", 8, (9, 17, 23), (4, 8, 8), 0.8, 2)
+    S, mask = _routed(wl8, q8, k8)
+    mo, co, hx, load, added, flags = oracle.sasa(S, mask, wl8.grid, wl8.block, 4)
+    assert sorted(hx.tolist()) == list(range(8))
+    assert (load == load[0]).all() and (added == 0).all() and np.array_equal(mo, mask)
+
+
+def test_dense_rows_and_zero_rounds():
+    wl = _wl("dense", 5, (9, 17, 23), (4, 8, 8), 1.0, 1)
+    S, mask = _routed(wl)
+    mo, _, _, _, added, _ = oracle.sasa(S, mask, wl.grid, wl.block, 4)
+    assert np.array_equal(mo, mask) and (added == 0).all()
+    wl = CASES[0]
+    S, mask = _routed(wl)
+    mo, _, _, _, added, _ = oracle.sasa(S, mask, wl.grid, wl.block, 0)
+    assert np.array_equal(mo, mask) and (added == 0).all()
