@@ -38,6 +38,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--oracle-items", type=int, default=160, help="work items in the CPU oracle sample")
     ap.add_argument("--no-dense", action="store_true", help="skip timing the dense reference")
+    ap.add_argument("--overlap", type=int, default=0, metavar="G",
+                    help="also measure the layer split into G head groups (contiguous per-group tensors), run "
+                         "in sequence and with routing/planning of group g+1 on a second stream behind the "
+                         "attention of group g")
     ap.add_argument("--sasa", type=int, default=0, metavar="R",
                     help="also measure slack-aware augmentation with R rounds on the per-XCD schedule, with its "
                          "error against the dense oracle on sampled items")
@@ -171,6 +175,10 @@ def main():
 
     traffic = _profiled_traffic(wl.name)
 
+    overlap = None
+    if args.overlap > 0 and not wl.static:
+        overlap = _overlap_leg(fva, wl, host, args)
+
     sasa = None
     if args.sasa > 0 and not wl.static:
         sasa = _sasa_leg(fva, wl, q, k, v, host, shape, ws_r, ws_a, stream, args)
@@ -226,6 +234,7 @@ def main():
         },
         "cpu_baseline": cpu,
         "sasa": sasa,
+        "overlap": overlap,
     }
     print(json.dumps(res), flush=True)
 
@@ -258,6 +267,76 @@ def _block_counts(wl):
     eh = [min(bh, H - i * bh) for i in range(-(-H // bh))]
     ew = [min(bw, W - i * bw) for i in range(-(-W // bw))]
     return np.array([a * b * c for a in et for b in eh for c in ew], dtype=np.int64)
+
+
+def _overlap_leg(fva, wl, host, args):
+    """Overlap of routing and planning with attention, one-GPU form: the heads
+    split into G groups held as separate contiguous tensors; 'sequential' runs
+    route, plan and attention group after group on one stream; 'overlapped'
+    routes and plans every group on a second stream (default priority) while
+    the main stream runs the attention of the groups already planned.  Both
+    give bitwise equal outputs (checked here)."""
+    import torch
+    G = args.overlap
+    B, L, heads, D = host[0].shape
+    if heads % G:
+        return {"groups": G, "error": "heads %d not divisible by %d" % (heads, G)}
+    hg = heads // G
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    qs, ks, vs = ([dev(x[:, :, g * hg:(g + 1) * hg]) for g in range(G)] for x in host)
+    outs = [torch.empty_like(x) for x in qs]
+    shape = tuple(qs[0].shape)
+    N = fva.num_blocks(wl.grid, wl.block)
+    masks = [torch.empty((B, hg, N, (N + 31) // 32), dtype=torch.int32, device="cuda") for _ in range(G)]
+    cnts = [torch.empty((B, hg, N), dtype=torch.int32, device="cuda") for _ in range(G)]
+    sts = [torch.empty((1,), dtype=torch.int32, device="cuda") for _ in range(G)]
+    wsr = [fva.workspace(fva.route_workspace_bytes(shape, wl.grid, wl.block), "cuda") for _ in range(G)]
+    wsa = [fva.workspace(fva.attn_workspace_bytes(shape, wl.grid, wl.block), "cuda") for _ in range(G)]
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+
+    def prep(g, s):
+        fva.route(qs[g], ks[g], wl.grid, wl.block, wl.top_p, wl.k_floor, ws=wsr[g], out=(masks[g], cnts[g], sts[g]),
+                  stream=s)
+        fva.attn_plan(ks[g], vs[g], wl.grid, wl.block, masks[g], ws=wsa[g], stream=s)
+
+    def sequential():
+        for g in range(G):
+            prep(g, main)
+            fva.attn_exec(qs[g], wl.grid, wl.block, masks[g], wsa[g], out=outs[g], stream=main)
+
+    def overlapped():
+        side.wait_stream(main)
+        ev = []
+        for g in range(G):
+            prep(g, main if g == 0 else side)
+            e = torch.cuda.Event()
+            e.record(main if g == 0 else side)
+            ev.append(e)
+        for g in range(G):
+            main.wait_event(ev[g])
+            fva.attn_exec(qs[g], wl.grid, wl.block, masks[g], wsa[g], out=outs[g], stream=main)
+        side.wait_stream(main)
+
+    res = {"groups": G}
+    ref = None
+    for name, f in (("ms_per_layer_grouped_sequential", sequential), ("ms_per_layer_grouped_overlapped", overlapped)):
+        for _ in range(args.warmup):
+            f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(main)
+        for _ in range(args.steps):
+            f()
+        e1.record(main)
+        torch.cuda.synchronize()
+        res[name] = round(e0.elapsed_time(e1) / args.steps, 4)
+        o = [x.view(torch.int16).clone() for x in outs]
+        if ref is None:
+            ref = o
+        else:
+            res["outputs_bitwise_equal"] = all(torch.equal(a, b) for a, b in zip(ref, o))
+    return res
 
 
 def _sasa_leg(fva, wl, q, k, v, host, shape, ws_r, ws_a, stream, args):
