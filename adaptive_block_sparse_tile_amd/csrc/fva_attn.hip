@@ -12,20 +12,24 @@
 // routing.  The one-GPU share: heads are assigned longest-first to the eight
 // XCDs (each XCD has its own L2, so the keys and values of a head stay in one
 // cache), each XCD's queue runs its heads' (query block) items longest-first,
-// and a workgroup whose queue is empty takes items from the other XCDs.
+// and a workgroup whose queue is empty takes items from the other XCDs (the
+// per-XCD schedule turns that off, so that each XCD plays one rank).
 //
-// Attention kernel (one work item = the real rows of one query block):
+// Attention kernel (one work item = the real rows of one query block, or of a
+// small group of small blocks):
 //   - WAVES wavefronts, each owning QT sub-tiles of 32 query rows held in
 //     registers as B operands of v_mfma_f32_32x32x16_bf16, so each K or V^T
 //     operand read from LDS feeds QT MFMAs;
-//   - chunks of 64 keys stream through a 3-stage LDS ring; a chunk is K
-//     [64][D] followed by V^T [D][64], rows padded so the MFMA operand reads of
-//     16-lane groups hit distinct banks;
+//   - chunks of 64 keys move from HBM straight into a 4-stage LDS ring, three
+//     chunks ahead of the one being computed; a chunk is K [64][D] followed by
+//     V^T [D][64], rows padded so the MFMA operand reads of 16-lane groups hit
+//     distinct banks;
 //   - S^T = K Q^T gives each lane one query column, so the softmax row
-//     statistics need one cross-half lane swap per chunk, and the bf16
+//     statistics need one cross-half lane swap per 32 keys, and the bf16
 //     probabilities feed O^T += V^T P^T from registers;
-//   - Q K^T of chunk c+1 is issued before the softmax of chunk c so the
-//     matrix cores and the vector ALUs work at the same time;
+//   - per 32 keys, Q K^T of the next 32 keys, P V of the current ones and the
+//     exponentials are interleaved so the matrix cores and the vector ALUs
+//     work at the same time;
 //   - the running max is raised lazily (only when it grows by more than 8 in
 //     log2 units), which skips most rescales of the O accumulators.
 #include "fva_dev.h"
