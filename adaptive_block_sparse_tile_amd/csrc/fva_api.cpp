@@ -52,7 +52,7 @@ bool make_geo(const fva_grid* g, fva::Geo* out) {
   return true;
 }
 
-constexpr int kMaxBlocks = 8192;  // largest row the router sorts in one workgroup's LDS
+constexpr int kMaxBlocks = 8192;  // largest row the router selects in one workgroup; the attention kernel's LDS mask
 constexpr int64_t kMaxTokens = 1 << 24;
 constexpr int kMaxHeads = 4096;  // B*heads planned by one workgroup's LDS
 
@@ -210,6 +210,8 @@ static fva_status sparse_setup(const void* q, const void* k, const void* v, void
   if (check_scale_arg && (st = check_scale(desc->D, scale)) != FVA_OK) return st;
   if (sched != FVA_SCHED_LPT && sched != FVA_SCHED_NAIVE && sched != FVA_SCHED_XCD)
     return fail(FVA_ERR_INVALID_ARG, "unknown schedule %d", sched);
+  // an item's mask rows are staged in LDS (kMaxBlocks / 32 words)
+  if (g.N > kMaxBlocks) return fail(FVA_ERR_UNSUPPORTED, "num_blocks %d > %d not supported", g.N, kMaxBlocks);
   const int64_t items = (int64_t)desc->B * desc->heads * g.N;
   const int64_t slots = items * fva::attn_chunks_per_block(g.bt * g.bh * g.bw);
   if (slots >= ((int64_t)1 << 31)) return fail(FVA_ERR_UNSUPPORTED, "too many work items");

@@ -94,6 +94,13 @@ def test_attn_validation_errors():
     assert call(sched=7) == 1
     assert call(ws_bytes=100) == 5
     assert call(desc=fva.make_desc(1, 100, 40, 128)) == 2
+    # more than 8192 blocks: (132, 64, 64) in (4, 4, 4) tiles is 33 * 16 * 16 = 8448
+    big_desc, big_grid = fva.make_desc(1, 132 * 64 * 64, 1, 64), fva.make_grid((132, 64, 64), (4, 4, 4))
+    assert lib.fva_sparse_attn(FAKE, FAKE, FAKE, FAKE, ctypes.byref(big_desc), ctypes.byref(big_grid), FAKE,
+                               64 ** -0.5, 0, None, FAKE, 1 << 40, None) == 6
+    assert "num_blocks 8448 > 8192" in _err()
+    assert lib.fva_attn_plan(FAKE, FAKE, ctypes.byref(big_desc), ctypes.byref(big_grid), FAKE, 0, None, FAKE,
+                             1 << 40, None) == 6
     assert lib.fva_dense_attn_ref(FAKE, FAKE, FAKE, FAKE, ctypes.byref(desc), ctypes.c_float(0.1), None) == 4
     assert lib.fva_dense_attn_ref(FAKE, FAKE, FAKE, None, ctypes.byref(desc), ctypes.c_float(128 ** -0.5),
                                   None) == 1
