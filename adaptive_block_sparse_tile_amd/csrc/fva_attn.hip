@@ -204,14 +204,23 @@ struct ChunkDma {
   static constexpr int PER_WAVE = (PIECES + WAVES - 1) / WAVES;
   static_assert(BYTES % 1024 == 0, "a chunk image is a whole number of 1 KB pieces");
   static_assert(PIECES >= WAVES && PER_WAVE <= 15, "every wavefront has a piece; vmcnt range");
+  // Addresses: a scalar base (the chunk's image plus the piece's offset past
+  // this wavefront's first piece) and a per-lane vector offset; M0 likewise.
+  // The wavefront's own offset passes through an empty asm statement so that
+  // the compiler forms the per-piece scalars here, at each issue, instead of
+  // keeping all of them (4 stages x PER_WAVE) live across the chunk loop.
   __device__ static void issue(const bf16_bits* tiles, int slot, bf16_bits* lds, int wave, int lane) {
-    const char* src = (const char*)tiles + (int64_t)slot * BYTES + lane * 16;
+    uint32_t w1k = (uint32_t)wave * 1024u;
+    asm volatile("" : "+s"(w1k));
+    const uint64_t gbase = (uint64_t)(uintptr_t)tiles + (uint64_t)(uint32_t)slot * (uint64_t)BYTES;
+    const uint32_t lbase = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)((char*)lds) + w1k;
+    const uint32_t voff = w1k + (uint32_t)lane * 16u;
 #pragma unroll
     for (int u = 0; u < PER_WAVE; ++u) {
-      int j = wave + u * WAVES;
-      if (j >= PIECES) j -= WAVES;
-      const uint32_t ldsa = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)((char*)lds + j * 1024);
-      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(ldsa), "v"(src + j * 1024) : "memory", "m0");
+      uint32_t joff = (uint32_t)(u * WAVES * 1024);
+      if (wave + u * WAVES >= PIECES) joff -= WAVES * 1024u;  // repeat the previous piece
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" : : "s"(lbase + joff), "v"(voff),
+                   "s"(gbase + joff) : "memory", "m0");
     }
   }
 };
@@ -421,6 +430,8 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
     int qbase, qcount;  // this wavefront's query block: first position, real rows
     int row0;           // first row of this wavefront inside that block
     int mine = -1;      // groups: this wavefront's member index, or -1
+    int ksel = -1;      // -1: every key of every chunk; 0 / 1: only key half ksel of each chunk
+    bool merge = false;  // some tile of the item is split over two wavefronts (uniform)
     KvIter it;
     it.umask = umask;
     if (DENSE) {
@@ -440,7 +451,23 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
       const Box bx = block_box(p.g, n);
       qbase = bx.start;
       qcount = bx.count;
-      row0 = 32 * QT * wave;
+      // Ragged blocks: the per-chunk work of a 32-row tile is two key halves,
+      // and the four SIMDs of the CU hold wavefronts w and w + 4.  A block of
+      // 5 or 6 tiles gives its tiles 4 and 5 two wavefronts each, one per key
+      // half, and a block of at most 4 tiles does so for all its tiles, so
+      // every SIMD carries at most 3 (resp. 2) halves per chunk instead of 4;
+      // the two partial softmax states of a tile are merged at the end.
+      const int nt = (qcount + 32 * QT - 1) / (32 * QT);
+      merge = QT == 1 && nt <= 6;
+      int tile = wave;
+      if (QT == 1 && nt <= 4) {
+        tile = wave >> 1;
+        ksel = wave & 1;
+      } else if (QT == 1 && nt <= 6 && wave >= 4) {
+        tile = 4 + ((wave - 4) >> 1);
+        ksel = wave & 1;
+      }
+      row0 = 32 * QT * tile;
     } else {
       const int gid = item % p.n_groups;
       bh = item / p.n_groups;
@@ -564,11 +591,14 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
     constexpr int EPS = 8 / DT;   // probabilities per sub-tile per step of A or B
     static_assert(NOPS % AHEAD == 0 && EPS % 2 == 0, "operand ring and probability pairs");
     f32x16 sA[QT], sB[QT];
-    auto kread_at = [&](const bf16_bits* img, int kt, int ds) -> bf16x8 {
-      return *(const bf16x8*)(img + Lds<D>::k_off(32 * kt + lr, 16 * ds + 8 * hi));
+    // operand bases of key half kt of a chunk image: its K rows, its V^T columns
+    auto kbase = [](const bf16_bits* img, int kt) -> const bf16_bits* { return img + 32 * kt * Lds<D>::KROW; };
+    auto vbase = [](const bf16_bits* img, int kt) -> const bf16_bits* { return img + 32 * kt; };
+    auto kread = [&](const bf16_bits* kb, int ds) -> bf16x8 {
+      return *(const bf16x8*)(kb + Lds<D>::k_off(lr, 16 * ds + 8 * hi));
     };
-    auto vread_at = [&](const bf16_bits* img, int kt, int kg, int t) -> bf16x8 {
-      return *(const bf16x8*)(img + Lds<D>::v_off(32 * t + lr, 32 * kt + 16 * kg + 8 * hi));
+    auto vread = [&](const bf16_bits* vb, int kg, int t) -> bf16x8 {
+      return *(const bf16x8*)(vb + Lds<D>::v_off(32 * t + lr, 16 * kg + 8 * hi));
     };
     // operand i of a half: a K d-step (isk, a = d-step) or a V^T tile (a = key
     // group, t = d tile), in the order the MFMAs of A, B and C consume them
@@ -623,10 +653,11 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
       }
     };
 
+    const int kt0 = ksel < 0 ? 0 : ksel;  // first key half this wavefront computes
     if (wave_active && ready > 0) {
 #pragma unroll
       for (int ds = 0; ds < DS; ++ds) {
-        const bf16x8 a = kread_at(ring0, 0, ds);
+        const bf16x8 a = kread(kbase(ring0, kt0), ds);
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) {
           const f32x16 c0 = {};
@@ -634,27 +665,33 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
         }
       }
 #pragma unroll
-      for (int step = 0; step < STAT_STEPS; ++step) stat_step(step, sA, v0, 0);
+      for (int step = 0; step < STAT_STEPS; ++step) stat_step(step, sA, v0, kt0);
     }
-    // the first AHEAD operands of the first half (key half 0 of chunk 0; its
-    // Q K^T computes key half 1 of chunk 0)
+    // the first AHEAD operands of a half: from its V^T (vc) and the K of the
+    // next half (kn)
     bf16x8 opw[AHEAD];
+    auto preload = [&](const bf16_bits* vc, const bf16_bits* kn) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < AHEAD; ++i) {
-      const HalfOp o = half_op(i);
-      opw[i] = o.isk ? kread_at(ring0, 1, o.a) : vread_at(ring0, 0, o.a, o.t);
-    }
+      for (int i = 0; i < AHEAD; ++i) {
+        const HalfOp o = half_op(i);
+        opw[i] = o.isk ? kread(kn, o.a) : vread(vc, o.a, o.t);
+      }
+    };
+    // every wavefront's first half is key half kt0 of chunk 0; a wavefront
+    // that takes both halves computes key half 1 of chunk 0 in it, one that
+    // takes a single half computes its half of chunk 1 (its operands are
+    // loaded before each of its halves)
+    if (ksel < 0) preload(vbase(ring0, 0), kbase(ring0, 1));
 
-    // One half: keys 32*kt_cur .. +31 of the chunk in LDS image imgv, S^T
-    // (masked, statistics in mxc / rc) in sc.  S^T of the next half (key half
-    // kt_nxt of image imgk, valid_nxt real keys in its chunk) goes to sn and
-    // its statistics are taken in C.  The operand ring runs AHEAD operands
-    // into the half after (its V^T from imgk / kt_nxt, its K from imgk2 /
-    // kt_nn).
+    // One half: the 32 keys whose V^T starts at vc, S^T (masked, statistics
+    // in mxc / rc) in sc.  S^T of the next half (K rows from kn; key half
+    // kt_nxt of a chunk with valid_nxt real keys) goes to sn and its
+    // statistics are taken in C.  The operand ring runs AHEAD operands into
+    // the half after (its V^T from vn, its K from knn).
     constexpr int STAT_C0 = 1;  // first step of C followed by statistics (the Q K^T result has landed)
     constexpr int STAT_PER = (STAT_STEPS + DT - STAT_C0 - 1) / (DT - STAT_C0);
-    auto half = [&](f32x16 (&sc)[QT], f32x16 (&sn)[QT], int kt_cur, const bf16_bits* imgv, const bf16_bits* imgk,
-                    int kt_nxt, int valid_nxt, const bf16_bits* imgk2, int kt_nn) __attribute__((always_inline)) {
+    auto half = [&](f32x16 (&sc)[QT], f32x16 (&sn)[QT], const bf16_bits* vc, const bf16_bits* kn, int kt_nxt,
+                    int valid_nxt, const bf16_bits* vn, const bf16_bits* knn) __attribute__((always_inline)) {
       if (rc) {
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) {
@@ -677,10 +714,8 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
       auto refill = [&](int i) __attribute__((always_inline)) {
         const int j = i + AHEAD;
         const HalfOp o = half_op(j % NOPS);
-        bf16x8 x;
-        if (j < NOPS) x = o.isk ? kread_at(imgk, kt_nxt, o.a) : vread_at(imgv, kt_cur, o.a, o.t);
-        else x = o.isk ? kread_at(imgk2, kt_nn, o.a) : vread_at(imgk, kt_nxt, o.a, o.t);
-        opw[i % AHEAD] = x;
+        if (j < NOPS) opw[i % AHEAD] = o.isk ? kread(kn, o.a) : vread(vc, o.a, o.t);
+        else opw[i % AHEAD] = o.isk ? kread(knn, o.a) : vread(vn, o.a, o.t);
       };
       typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
       const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
@@ -753,6 +788,14 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
     // wavefront waits until chunk c+2 has landed (dense: stores chunk c+2)
     // and the workgroup meets at the barrier.  s0 is a compile-time constant
     // in each of the four unrolled copies below.
+    //
+    // A wavefront on one key half (ksel) runs key half ksel of chunk c and
+    // (Q K^T) the same half of chunk c+1, in the first half slot of even
+    // chunks and the second slot of odd ones, so that its S^T alternates
+    // between sA and sB like everyone else's; its operand ring is reloaded
+    // before each of its halves (what the slot before read ahead is not its
+    // own).
+    const bool sp = !DENSE && !GRP && ksel >= 0;
     Stager<D, THREADS, DENSE> st2k;  // dense: chunk c+2, K part
     auto chunk_step = [&](int s0) __attribute__((always_inline)) -> bool {
       const int s1 = (s0 + 1) % STAGES;
@@ -769,8 +812,24 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
         }
       }
       if (wave_active) {
-        half(sA, sB, 0, stage(s0), stage(s0), 1, v0, stage(s1), 0);
-        half(sB, sA, 1, stage(s0), stage(s1), 0, v1, stage(s1), 1);
+        const bf16_bits* S0 = stage(s0);
+        const bf16_bits* S1 = stage(s1);
+        const bool even = (s0 & 1) == 0;
+        // a one-half wavefront's half: V^T of (c, ksel), K of (c+1, ksel)
+        const bf16_bits* vs = vbase(S0, sp ? ksel : 0);
+        const bf16_bits* ks = kbase(S1, sp ? ksel : 0);
+        // first slot, two-half wavefronts: key half 0 of c; Q K^T of half 1 of c
+        if (!sp || even) {
+          if (sp) preload(vs, ks);
+          half(sA, sB, sp ? vs : vbase(S0, 0), sp ? ks : kbase(S0, 1), sp ? ksel : 1, sp ? v1 : v0, vbase(S0, 1),
+               kbase(S1, 0));
+        }
+        // second slot, two-half wavefronts: key half 1 of c; Q K^T of half 0 of c+1
+        if (!sp || !even) {
+          if (sp) preload(vs, ks);
+          half(sB, sA, sp ? vs : vbase(S0, 1), sp ? ks : kbase(S1, 0), sp ? ksel : 0, v1, vbase(S1, 0),
+               kbase(S1, 1));
+        }
       }
       if (more) {
         if (DENSE) {
@@ -803,8 +862,48 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
       if (!chunk_step(3)) break;
     }
 
+    // ---- split tiles: the key-half-1 wavefront hands its running max, partial
+    //      row sums and O^T accumulators to the key-half-0 wavefront through
+    //      LDS (the ring is idle: every chunk load has landed), which rescales
+    //      both to the larger max and adds them.  A side that saw no real key
+    //      has the floor max and zero sums, so it contributes nothing.
+    if (!DENSE && !GRP && QT == 1 && merge) {
+      float* xch = (float*)stage((row0 >> 5) & 3);
+      f32x4* xv = (f32x4*)xch;
+      if (wave_active && ksel == 1) {
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            f32x4 x;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = acc[0][t][4 * g + e];
+            xv[(t * 4 + g) * 64 + lane] = x;
+          }
+        xch[DT * 16 * 64 + lane] = m_run[0];
+        xch[DT * 16 * 64 + 64 + lane] = lsum[0];
+      }
+      __syncthreads();
+      if (wave_active && ksel == 0) {
+        const float mb = xch[DT * 16 * 64 + lane];
+        const float lb = xch[DT * 16 * 64 + 64 + lane];
+        const float m = fmaxf(m_run[0], mb);
+        const float ea = __builtin_amdgcn_exp2f(m_run[0] - m);
+        const float eb = __builtin_amdgcn_exp2f(mb - m);
+        lsum[0] = lsum[0] * ea + lb * eb;
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 x = xv[(t * 4 + g) * 64 + lane];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[0][t][4 * g + e] = acc[0][t][4 * g + e] * ea + x[e] * eb;
+          }
+      }
+    }
+
     // ---- normalise and store the real rows (lane and lane ^ 32 share a row)
-    if (wave_active) {
+    if (wave_active && ksel != 1) {
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
         const float lt = sum_halves(lsum[qt]);
