@@ -27,7 +27,7 @@ SCHEDS = {"lpt": SCHED_LPT, "naive": SCHED_NAIVE, "xcd": SCHED_XCD}
 # every symbol include/fva.h declares
 EXPORTS = ["fva_num_blocks", "fva_route_workspace_bytes", "fva_attn_workspace_bytes", "fva_attn_workgroups",
            "fva_route", "fva_static_mask", "fva_sparse_attn", "fva_attn_plan", "fva_attn_exec", "fva_sasa_workspace_bytes", "fva_sasa",
-           "fva_dense_attn_ref",
+           "fva_dense_workspace_bytes", "fva_dense_attn_ref",
            "fva_trace_imbalance", "fva_last_error", "fva_status_name"]
 
 
@@ -91,8 +91,10 @@ def load():
     lib.fva_sasa_workspace_bytes.argtypes = [D, G, ctypes.c_int32]
     lib.fva_sasa.restype = ctypes.c_int
     lib.fva_sasa.argtypes = [D, G, _P, _P, ctypes.c_size_t, ctypes.c_int32, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.fva_dense_workspace_bytes.restype = ctypes.c_size_t
+    lib.fva_dense_workspace_bytes.argtypes = [D]
     lib.fva_dense_attn_ref.restype = ctypes.c_int
-    lib.fva_dense_attn_ref.argtypes = [_P, _P, _P, _P, D, ctypes.c_float, _P]
+    lib.fva_dense_attn_ref.argtypes = [_P, _P, _P, _P, D, ctypes.c_float, _P, ctypes.c_size_t, _P]
     lib.fva_trace_imbalance.restype = ctypes.c_int
     lib.fva_trace_imbalance.argtypes = [_P, ctypes.c_int32, ctypes.POINTER(ctypes.c_double),
                                         ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32)]
@@ -286,16 +288,24 @@ def sasa(shape, grid, block, mask, route_ws, rounds=4, out=None, ws=None, stream
     return mask_out, cnt, head_xcd, xcd_load
 
 
-def dense_attn_ref(q, k, v, scale=None, out=None, stream=None):
-    """Dense attention over all tokens on the GPU (same core and numerics)."""
+def dense_workspace_bytes(shape):
+    """Workspace bytes of dense_attn_ref for q/k/v of shape [B, L, heads, D]."""
+    return int(load().fva_dense_workspace_bytes(ctypes.byref(make_desc(*shape))))
+
+
+def dense_attn_ref(q, k, v, scale=None, out=None, ws=None, stream=None):
+    """Dense attention over all tokens on the GPU (same kernel and numerics)."""
     torch = _torch()
     shape = _check_qkv(q, k, v)
     D = shape[3]
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     o = torch.empty_like(q) if out is None else out
+    if ws is None:
+        ws = workspace(dense_workspace_bytes(shape), q.device)
     _check(load().fva_dense_attn_ref(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                                     ctypes.byref(make_desc(*shape)), float(scale), _stream_ptr(stream)))
+                                     ctypes.byref(make_desc(*shape)), float(scale), ws.data_ptr(), ws.numel(),
+                                     _stream_ptr(stream)))
     return o
 
 

@@ -343,13 +343,20 @@ fva_status fva_attn_exec(const void* q, void* o, const fva_desc* desc, const fva
   return ok();
 }
 
+size_t fva_dense_workspace_bytes(const fva_desc* desc) {
+  if (check_desc(desc) != FVA_OK) return 0;
+  return align_up(fva::dense_tile_bytes(desc->B, desc->L, desc->heads, desc->D));
+}
+
 fva_status fva_dense_attn_ref(const void* q, const void* k, const void* v, void* o, const fva_desc* desc, float scale,
-                              void* stream) {
+                              void* ws, size_t ws_bytes, void* stream) {
   if (!q || !k || !v || !o) return fail(FVA_ERR_INVALID_ARG, "q, k, v and o must not be null");
   fva_status st = check_desc(desc);
   if (st != FVA_OK) return st;
   if ((st = check_scale(desc->D, scale)) != FVA_OK) return st;
-  hipError_t e = fva::launch_dense_attn(q, k, v, o, desc->B, desc->L, desc->heads, desc->D, scale, (hipStream_t)stream);
+  if ((st = check_ws(ws, ws_bytes, fva_dense_workspace_bytes(desc))) != FVA_OK) return st;
+  hipError_t e = fva::launch_dense_attn(q, k, v, o, desc->B, desc->L, desc->heads, desc->D, scale, ws,
+                                        (hipStream_t)stream);
   if (e != hipSuccess) return device_error(e, "dense attention launch");
   return ok();
 }

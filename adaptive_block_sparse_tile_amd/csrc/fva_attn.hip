@@ -30,6 +30,9 @@
 //   - per 32 keys, Q K^T of the next 32 keys, P V of the current ones and the
 //     exponentials are interleaved so the matrix cores and the vector ALUs
 //     work at the same time;
+//   - Q is pre-multiplied by the score scale in log2 units and the Q K^T
+//     accumulator starts at minus the row's running max, so each exponent
+//     argument comes straight out of the MFMA;
 //   - the running max is raised lazily (only when it grows by more than 8 in
 //     log2 units), which skips most rescales of the O accumulators.
 #include "fva_dev.h"
@@ -108,7 +111,7 @@ __device__ inline int group_member(const AttnParams& p, int gid, int k) {
 
 // One chunk of a work item's key sequence.
 struct Chunk {
-  int slot;   // sparse: chunk image index; dense: first token
+  int slot;   // chunk image index
   int valid;  // real keys in the chunk (1..64)
   int blk;    // sparse: key block of the chunk
 };
@@ -149,7 +152,7 @@ struct KvIter {
     if (DENSE) {
       count = L;
       nch = (L + KCH - 1) / KCH;
-      slot0 = 0;
+      slot0 = bh * cpb;
       return;
     }
     words = nwords;
@@ -174,18 +177,14 @@ struct KvIter {
   template <bool DENSE>
   __device__ Chunk chunk() const {
     Chunk ck;
-    ck.slot = DENSE ? c * KCH : slot0 + c;
+    ck.slot = slot0 + c;
     ck.valid = min(KCH, count - c * KCH);
     ck.blk = blk;
     return ck;
   }
 };
 
-// Register staging of one chunk between its global load and its LDS store.
-template <int D, int THREADS, bool DENSE>
-struct Stager;
-
-// Sparse: a chunk image moves from HBM straight into LDS, 1 KB per wavefront
+// A chunk image moves from HBM straight into LDS, 1 KB per wavefront
 // instruction (global_load_lds_dwordx4: lane l's 16 bytes land at the LDS
 // address in M0 + 16 l).  It is written as inline assembly so that the
 // compiler's wait counting stays blind to these loads: its LDS waits inside
@@ -212,7 +211,9 @@ struct ChunkDma {
   __device__ static void issue(const bf16_bits* tiles, int slot, bf16_bits* lds, int wave, int lane) {
     uint32_t w1k = (uint32_t)wave * 1024u;
     asm volatile("" : "+s"(w1k));
-    const uint64_t gbase = (uint64_t)(uintptr_t)tiles + (uint64_t)(uint32_t)slot * (uint64_t)BYTES;
+    // (the slot is the same in every lane; say so, so that it stays scalar)
+    const uint32_t us = (uint32_t)__builtin_amdgcn_readfirstlane(slot);
+    const uint64_t gbase = (uint64_t)(uintptr_t)tiles + (uint64_t)us * (uint64_t)BYTES;
     const uint32_t lbase = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)((char*)lds) + w1k;
     const uint32_t voff = w1k + (uint32_t)lane * 16u;
 #pragma unroll
@@ -223,13 +224,6 @@ struct ChunkDma {
                    "s"(gbase + joff) : "memory", "m0");
     }
   }
-};
-
-// (sparse chunks need no register staging)
-template <int D, int THREADS>
-struct Stager<D, THREADS, false> {
-  __device__ void load(const AttnParams&, int64_t, int64_t, Chunk, int) {}
-  __device__ void store(bf16_bits*, int) const {}
 };
 
 // Workgroup barrier for LDS data: waits for this wavefront's LDS operations
@@ -252,84 +246,6 @@ __device__ inline void wait_vmem() {
   static_assert(N >= 0 && N <= 15, "vmcnt range");
   __builtin_amdgcn_s_waitcnt(0x0F70 | N);
 }
-
-// Dense: 64 consecutive tokens of BSHD K and V; V is transposed on the way.
-// Part 0 stages K, part 1 stages V.
-template <int D, int THREADS>
-struct Stager<D, THREADS, true> {
-  static constexpr int KP = KCH * D / 8;  // (row, piece) pairs of K
-  static constexpr int KPER = (KP + THREADS - 1) / THREADS;
-  static constexpr int VP = (D / 2) * 8;  // (d pair, 8-key group) pairs of V
-  static constexpr int VPER = (VP + THREADS - 1) / THREADS;
-  u32x4 kr[KPER];
-  uint32_t vr[VPER][8];
-
-  __device__ void load(const AttnParams& p, int64_t head_off, int64_t rs, Chunk ck, int part) {
-    const bf16_bits* kb = p.k + head_off + (int64_t)ck.slot * rs;
-    const bf16_bits* vb = p.v + head_off + (int64_t)ck.slot * rs;
-    const bool full = ck.valid == KCH;
-    if (part == 0) {
-#pragma unroll
-    for (int u = 0; u < KPER; ++u) {
-      const int s = threadIdx.x + u * THREADS;
-      const int row = s / (D / 8), piece = s % (D / 8);
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if ((KP % THREADS == 0 || s < KP) && (full || row < ck.valid)) x = *(const u32x4*)(kb + row * rs + piece * 8);
-      kr[u] = x;
-    }
-      return;
-    }
-#pragma unroll
-    for (int u = 0; u < VPER; ++u) {
-      const int s = threadIdx.x + u * THREADS;
-      const int dp = s % (D / 2), kg = s / (D / 2);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int row = kg * 8 + e;
-        uint32_t x = 0u;
-        if ((VP % THREADS == 0 || s < VP) && (full || row < ck.valid)) x = *(const uint32_t*)(vb + row * rs + dp * 2);
-        vr[u][e] = x;
-      }
-    }
-  }
-  __device__ void store(bf16_bits* img, int part) const {
-    if (part == 0) {
-#pragma unroll
-      for (int u = 0; u < KPER; ++u) {
-        const int s = threadIdx.x + u * THREADS;
-        if (KP % THREADS == 0 || s < KP) {
-          const int row = s / (D / 8), piece = s % (D / 8);
-          *(u32x4*)(img + Lds<D>::k_off(row, piece * 8)) = kr[u];
-        }
-      }
-      return;
-    }
-#pragma unroll
-    for (int u = 0; u < VPER; ++u) {
-      const int s = threadIdx.x + u * THREADS;
-      if (VP % THREADS == 0 || s < VP) {
-        const int dp = s % (D / 2), kg = s / (D / 2);
-        const uint32_t* w = vr[u];
-        // keys 8kg+0..3 -> positions p0+0..3, keys 8kg+4..7 -> p0+8..11
-        const int p0 = 16 * (kg >> 1) + 4 * (kg & 1);
-        u32x2 lo0, lo1, hi0, hi1;
-        lo0[0] = (w[0] & 0xffffu) | (w[1] << 16);
-        lo0[1] = (w[2] & 0xffffu) | (w[3] << 16);
-        lo1[0] = (w[4] & 0xffffu) | (w[5] << 16);
-        lo1[1] = (w[6] & 0xffffu) | (w[7] << 16);
-        hi0[0] = (w[0] >> 16) | (w[1] & 0xffff0000u);
-        hi0[1] = (w[2] >> 16) | (w[3] & 0xffff0000u);
-        hi1[0] = (w[4] >> 16) | (w[5] & 0xffff0000u);
-        hi1[1] = (w[6] >> 16) | (w[7] & 0xffff0000u);
-        const int d0 = 2 * dp, d1 = 2 * dp + 1;
-        *(u32x2*)(img + Lds<D>::v_off(d0, p0)) = lo0;
-        *(u32x2*)(img + Lds<D>::v_off(d0, p0 + 8)) = lo1;
-        *(u32x2*)(img + Lds<D>::v_off(d1, p0)) = hi0;
-        *(u32x2*)(img + Lds<D>::v_off(d1, p0 + 8)) = hi1;
-      }
-    }
-  }
-};
 
 template <bool DENSE>
 __device__ inline int pos_to_token(const AttnParams& p, int pos) {
@@ -394,7 +310,6 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform in the wavefront
   const int lr = lane & 31, hi = lane >> 5;
   const float cl2 = p.scale_log2;
-  const float inv_cl2 = 1.0f / cl2;
 
   uint64_t t_first = 0, t_last = 0, busy = 0, nitems = 0;
   int my_xcd = 0;
@@ -500,8 +415,11 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
     const int64_t rs = (int64_t)p.heads * D;
     const int64_t head_off = (int64_t)b * p.L * rs + (int64_t)h * D;
 
-    // ---- Q fragments: sub-tile qt holds row row0 + 32*qt + lr of the block, d = 16s + 8hi .. +7
+    // ---- Q fragments: sub-tile qt holds row row0 + 32*qt + lr of the block, d = 16s + 8hi .. +7,
+    //      times the score scale in log2 units (rounded to bf16), so that the
+    //      Q K^T MFMA yields exponent arguments directly
     const bool wave_active = row0 < qcount;
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
     bf16x8 qf[QT][DS];
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
@@ -513,21 +431,35 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
       for (int s = 0; s < DS; ++s) {
         u32x4 x = {0u, 0u, 0u, 0u};
         if (ok) x = *(const u32x4*)(p.q + head_off + qtok * rs + 16 * s + 8 * hi);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bf16x2_t pr = {(__bf16)(__uint_as_float(x[e] << 16) * cl2),
+                               (__bf16)(__uint_as_float(x[e] & 0xffff0000u) * cl2)};
+          x[e] = __builtin_bit_cast(uint32_t, pr);
+        }
         qf[qt][s] = __builtin_bit_cast(bf16x8, x);
       }
     }
     wait_vmem<0>();  // Q is in before any chunk load is issued
 
-    f32x16 acc[QT][DT];
-    float m_run[QT], lsum[QT], thr[QT];  // thr: raise threshold on raw scores
+    // Softmax state of each row (log2 units).  m_run: the running max the
+    // O^T accumulators and the row sum are scaled by.  moff: the offset the
+    // Q K^T MFMAs subtract (their accumulator starts at negm = -moff), equal
+    // to m_run once the row has seen a real key and 0 before.  thr: the
+    // raise threshold on those offset scores.
+    f32x16 acc[QT][DT], negm[QT];
+    float m_run[QT], moff[QT], lsum[QT], thr[QT];
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
 #pragma unroll
       for (int t = 0; t < DT; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[qt][t][r] = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) negm[qt][r] = 0.f;
       m_run[qt] = M_NONE;
-      thr[qt] = (M_NONE + RAISE_SLACK) * inv_cl2;
+      moff[qt] = 0.f;
+      thr[qt] = M_NONE + RAISE_SLACK;
       lsum[qt] = 0.f;
     }
 
@@ -536,7 +468,6 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
     //      computed, with real key counts v0, v1, v2 as this wavefront sees them
     if (!DENSE) __syncthreads();  // the item's mask is in LDS
     it.template first<DENSE>(p.g, p.words, p.L, bh, p.cpb);
-    Stager<D, THREADS, DENSE> st;
     // real keys of the chunks in the ring as this wavefront sees them: a key
     // block its own query block did not keep counts as 0 real keys
     auto seen = [&](const Chunk& ck) -> int {
@@ -544,24 +475,15 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
       if (mine < 0) return 0;
       return ((gmask[mine][ck.blk >> 5] >> (ck.blk & 31)) & 1u) ? ck.valid : 0;
     };
-    // sparse chunks arrive by direct loads three chunks ahead of the one
-    // being computed; dense chunks pass through registers two ahead
-    constexpr int LOOK = DENSE ? 2 : 3;
+    // chunks arrive by direct loads three chunks ahead of the one being computed
+    constexpr int LOOK = 3;
     using Dma = ChunkDma<D, WAVES>;
     int ready = 0, v0 = 0, v1 = 0, v2 = 0;
 #pragma unroll
     for (int sidx = 0; sidx < LOOK; ++sidx) {
       if (it.done) break;
       const Chunk ck = it.template chunk<DENSE>();
-      if (DENSE) {
-#pragma unroll
-        for (int part = 0; part < 2; ++part) {
-          st.load(p, head_off, rs, ck, part);
-          st.store(stage(sidx), part);
-        }
-      } else {
-        Dma::issue(p.tiles, ck.slot, stage(sidx), wave, lane);
-      }
+      Dma::issue(p.tiles, ck.slot, stage(sidx), wave, lane);
       const int sv = seen(ck);
       if (sidx == 0) v0 = sv;
       else if (sidx == 1) v1 = sv;
@@ -569,10 +491,9 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
       ++ready;
       it.template advance<DENSE>(p.g, bh, p.cpb);
     }
-    if (!DENSE) {  // chunks 0 and 1 must be in; chunk 2 may still be in flight
-      if (ready == LOOK) wait_vmem<Dma::PER_WAVE>();
-      else wait_vmem<0>();
-    }
+    // chunks 0 and 1 must be in; chunk 2 may still be in flight
+    if (ready == LOOK) wait_vmem<Dma::PER_WAVE>();
+    else wait_vmem<0>();
     barrier_lds();
 
     // The pipeline runs on 32-key halves of the chunks (the online softmax
@@ -616,8 +537,8 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
     };
 
     // Row statistics of a freshly computed S^T half: the tail mask (keys past
-    // the chunk's real count become -inf), the row max in raw score units and
-    // whether some row's running max must move.  Split into STAT_STEPS steps
+    // the chunk's real count become -inf), the row max of the offset scores
+    // and whether some row's running max must move.  Split into STAT_STEPS steps
     // so they sit between the P V MFMAs of the half before the one that uses
     // them, off the critical path.
     constexpr int STAT_STEPS = 7;
@@ -660,8 +581,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
         const bf16x8 a = kread(kbase(ring0, kt0), ds);
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) {
-          const f32x16 c0 = {};
-          sA[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qt][ds], ds == 0 ? c0 : sA[qt], 0, 0, 0);
+          sA[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qt][ds], ds == 0 ? negm[qt] : sA[qt], 0, 0, 0);
         }
       }
 #pragma unroll
@@ -693,22 +613,30 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
     auto half = [&](f32x16 (&sc)[QT], f32x16 (&sn)[QT], const bf16_bits* vc, const bf16_bits* kn, int kt_nxt,
                     int valid_nxt, const bf16_bits* vn, const bf16_bits* knn) __attribute__((always_inline)) {
       if (rc) {
+        // raise: the new max (absolute) of a row is its old one or this
+        // half's; scores of this half move to the new offset, and a row that
+        // has still seen no real key keeps offset 0
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) {
-          const float m_new = fmaxf(m_run[qt], mxc[qt] * cl2);
+          const float m_new = fmaxf(m_run[qt], moff[qt] + mxc[qt]);
+          const float o_new = m_new > 0.5f * M_NONE ? m_new : 0.f;
+          const float shift = o_new - moff[qt];
           const float alpha = __builtin_amdgcn_exp2f(m_run[qt] - m_new);
-          thr[qt] = (m_new + RAISE_SLACK) * inv_cl2;
+          thr[qt] = m_new - o_new + RAISE_SLACK;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            sc[qt][r] -= shift;
+            negm[qt][r] = -o_new;
+          }
 #pragma unroll
           for (int t = 0; t < DT; ++t)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[qt][t][r] *= alpha;
           lsum[qt] *= alpha;
           m_run[qt] = m_new;
+          moff[qt] = o_new;
         }
       }
-      float nm[QT];
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) nm[qt] = -m_run[qt];
 
       // consume operand i from the ring and read operand i + AHEAD into its slot
       auto refill = [&](int i) __attribute__((always_inline)) {
@@ -717,7 +645,6 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
         if (j < NOPS) opw[i % AHEAD] = o.isk ? kread(kn, o.a) : vread(vc, o.a, o.t);
         else opw[i % AHEAD] = o.isk ? kread(knn, o.a) : vread(vn, o.a, o.t);
       };
-      typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
       const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
       u32x4 pw[2][QT];  // bf16 probability pairs: B operands of the P V MFMAs
       // probabilities r0 .. r0+EPS-1 of every sub-tile, rounded to bf16 in
@@ -728,8 +655,8 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
 #pragma unroll
           for (int u = 0; u < EPS; u += 2) {
             const int r = r0 + u;
-            const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[qt][r], cl2, nm[qt]));
-            const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[qt][r + 1], cl2, nm[qt]));
+            const float e0 = __builtin_amdgcn_exp2f(sc[qt][r]);
+            const float e1 = __builtin_amdgcn_exp2f(sc[qt][r + 1]);
             const bf16x2_t pr = {(__bf16)e0, (__bf16)e1};
             pw[r >> 3][qt][(r & 7) >> 1] = __builtin_bit_cast(uint32_t, pr);
             lsum[qt] = __builtin_amdgcn_fdot2_f32_bf16(pr, one, lsum[qt], false);
@@ -745,8 +672,8 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
       auto qk = [&](int i, int ds) __attribute__((always_inline)) {
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) {
-          const f32x16 c0 = {};
-          sn[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opw[i % AHEAD], qf[qt][ds], ds == 0 ? c0 : sn[qt], 0, 0, 0);
+          sn[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opw[i % AHEAD], qf[qt][ds], ds == 0 ? negm[qt] : sn[qt], 0, 0,
+                                                           0);
         }
         refill(i);
       };
@@ -785,8 +712,8 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
 
     // One chunk c (stage s0): the load of chunk c+LOOK is issued, the two
     // halves of c run (the second also reads K of chunk c+1), then every
-    // wavefront waits until chunk c+2 has landed (dense: stores chunk c+2)
-    // and the workgroup meets at the barrier.  s0 is a compile-time constant
+    // wavefront waits until chunk c+2 has landed and the workgroup meets at
+    // the barrier.  s0 is a compile-time constant
     // in each of the four unrolled copies below.
     //
     // A wavefront on one key half (ksel) runs key half ksel of chunk c and
@@ -796,7 +723,6 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
     // before each of its halves (what the slot before read ahead is not its
     // own).
     const bool sp = !DENSE && !GRP && ksel >= 0;
-    Stager<D, THREADS, DENSE> st2k;  // dense: chunk c+2, K part
     auto chunk_step = [&](int s0) __attribute__((always_inline)) -> bool {
       const int s1 = (s0 + 1) % STAGES;
       const int sl = (s0 + LOOK) % STAGES;
@@ -804,55 +730,38 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
       Chunk ckl = {0, 0, -1};
       if (more) {
         ckl = it.template chunk<DENSE>();
-        if (DENSE) {
-          st2k.load(p, head_off, rs, ckl, 0);
-          st.load(p, head_off, rs, ckl, 1);
-        } else {
-          Dma::issue(p.tiles, ckl.slot, stage(sl), wave, lane);
-        }
+        Dma::issue(p.tiles, ckl.slot, stage(sl), wave, lane);
       }
-      if (wave_active) {
-        const bf16_bits* S0 = stage(s0);
-        const bf16_bits* S1 = stage(s1);
-        const bool even = (s0 & 1) == 0;
-        // a one-half wavefront's half: V^T of (c, ksel), K of (c+1, ksel)
-        const bf16_bits* vs = vbase(S0, sp ? ksel : 0);
-        const bf16_bits* ks = kbase(S1, sp ? ksel : 0);
-        // first slot, two-half wavefronts: key half 0 of c; Q K^T of half 1 of c
-        if (!sp || even) {
-          if (sp) preload(vs, ks);
-          half(sA, sB, sp ? vs : vbase(S0, 0), sp ? ks : kbase(S0, 1), sp ? ksel : 1, sp ? v1 : v0, vbase(S0, 1),
-               kbase(S1, 0));
-        }
-        // second slot, two-half wavefronts: key half 1 of c; Q K^T of half 0 of c+1
-        if (!sp || !even) {
-          if (sp) preload(vs, ks);
-          half(sB, sA, sp ? vs : vbase(S0, 1), sp ? ks : kbase(S1, 0), sp ? ksel : 0, v1, vbase(S1, 0),
-               kbase(S1, 1));
-        }
+      const bf16_bits* S0 = stage(s0);
+      const bf16_bits* S1 = stage(s1);
+      const bool even = (s0 & 1) == 0;
+      // a one-half wavefront's half: V^T of (c, ksel), K of (c+1, ksel)
+      const bf16_bits* vs = vbase(S0, sp ? ksel : 0);
+      const bf16_bits* ks = kbase(S1, sp ? ksel : 0);
+      // first slot, two-half wavefronts: key half 0 of c; Q K^T of half 1 of c
+      if (wave_active && (!sp || even)) {
+        if (sp) preload(vs, ks);
+        half(sA, sB, sp ? vs : vbase(S0, 0), sp ? ks : kbase(S0, 1), sp ? ksel : 1, sp ? v1 : v0, vbase(S0, 1),
+             kbase(S1, 0));
+      }
+      // second slot, two-half wavefronts: key half 1 of c; Q K^T of half 0 of c+1
+      if (wave_active && (!sp || !even)) {
+        if (sp) preload(vs, ks);
+        half(sB, sA, sp ? vs : vbase(S0, 1), sp ? ks : kbase(S1, 0), sp ? ksel : 0, v1, vbase(S1, 0),
+             kbase(S1, 1));
       }
       if (more) {
-        if (DENSE) {
-          st2k.store(stage(sl), 0);
-          st.store(stage(sl), 1);
-        }
         ++ready;
         it.template advance<DENSE>(p.g, bh, p.cpb);
       }
-      if (!DENSE) {
-        if (more) wait_vmem<Dma::PER_WAVE>();
-        else wait_vmem<0>();
-      }
+      if (more) wait_vmem<Dma::PER_WAVE>();
+      else wait_vmem<0>();
       barrier_lds();
       --ready;
       const int sv = more ? seen(ckl) : 0;
       v0 = v1;
-      if (DENSE) {
-        v1 = sv;
-      } else {
-        v1 = v2;
-        v2 = sv;
-      }
+      v1 = v2;
+      v2 = sv;
       return ready > 0;
     };
     while (ready > 0) {
@@ -964,7 +873,8 @@ __global__ __launch_bounds__(256) void layout_kernel(Geo g, int32_t* __restrict_
 // Chunk images of K and V in the LDS layout: one workgroup per (b, h,
 // block, chunk) slot.  Rows past the block's real count and the row pads are
 // zero.  The image is assembled in LDS and written out linearly, so every
-// store covers whole cache lines.
+// store covers whole cache lines.  tok = null: the tokens are in their
+// natural order (the dense reference's single block of L tokens).
 template <int D>
 __global__ __launch_bounds__(256) void tile_kernel(const bf16_bits* __restrict__ k, const bf16_bits* __restrict__ v,
                                                    const int32_t* __restrict__ tok, Geo g, int L, int heads, int cpb,
@@ -991,7 +901,8 @@ __global__ __launch_bounds__(256) void tile_kernel(const bf16_bits* __restrict__
     const int row = s / (D / 8), piece = s % (D / 8);
     u32x4 kx = zero, vx = zero;
     if (row < valid) {
-      const int64_t t = tok[bx.start + c * KCH + row];
+      const int pos = bx.start + c * KCH + row;
+      const int64_t t = tok ? tok[pos] : pos;
       kx = *(const u32x4*)(k + head_off + t * rs + piece * 8);
       vx = *(const u32x4*)(v + head_off + t * rs + piece * 8);
     }
@@ -1264,8 +1175,18 @@ hipError_t launch_sparse_exec(const AttnLaunch& a, int sched, hipStream_t st) {
   return hipLaunchKernel(sparse_kernel(a.D, group_shape(vol).wpb < WAVES), dim3(grid), dim3(WAVES * 64), args, 0, st);
 }
 
+// The dense reference: the whole sequence as one block of L tokens, tiled in
+// natural order (chunk c = tokens 64c .. 64c+63), and query tiles of 256
+// consecutive tokens as work items (one workgroup each, consecutive tiles on
+// one XCD), streamed through the same chunk pipeline as the sparse path.
+static Geo dense_geo(int L) { return Geo{L, 1, 1, L, 1, 1, 1, 1, 1, 1}; }
+
+size_t dense_tile_bytes(int B, int L, int heads, int D) {
+  return attn_tile_bytes(D, (int64_t)B * heads * ((L + KCH - 1) / KCH));
+}
+
 hipError_t launch_dense_attn(const void* q, const void* k, const void* v, void* o, int B, int L, int heads, int D,
-                             float scale, hipStream_t st) {
+                             float scale, void* tiles, hipStream_t st) {
   constexpr int QT = 1;
   AttnParams prm = {};
   prm.q = (const bf16_bits*)q;
@@ -1275,10 +1196,20 @@ hipError_t launch_dense_attn(const void* q, const void* k, const void* v, void* 
   prm.B = B;
   prm.L = L;
   prm.heads = heads;
+  prm.g = dense_geo(L);
+  prm.cpb = (L + KCH - 1) / KCH;
+  prm.tiles = (const bf16_bits*)tiles;
   prm.q_tiles = (L + WAVES * QT * 32 - 1) / (WAVES * QT * 32);
   prm.n_items = B * heads * prm.q_tiles;
   prm.scale_log2 = scale * 1.4426950408889634f;
   prm.trace = nullptr;
+  const unsigned slots = (unsigned)(B * heads * prm.cpb);
+  if (D == 128)
+    hipLaunchKernelGGL(tile_kernel<128>, dim3(slots), dim3(256), 0, st, prm.k, prm.v, nullptr, prm.g, L, heads,
+                       prm.cpb, (bf16_bits*)tiles);
+  else
+    hipLaunchKernelGGL(tile_kernel<64>, dim3(slots), dim3(256), 0, st, prm.k, prm.v, nullptr, prm.g, L, heads, prm.cpb,
+                       (bf16_bits*)tiles);
   const int grid = NXCD * ((prm.n_items + NXCD - 1) / NXCD);
   if (D == 128)
     hipLaunchKernelGGL((attn_kernel<128, WAVES, QT, true, false>), dim3(grid), dim3(WAVES * 64), 0, st, prm);

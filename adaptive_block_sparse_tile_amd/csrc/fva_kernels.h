@@ -61,7 +61,10 @@ int attn_persistent_workgroups(int D, int block_volume, int* err);
 // head_xcd if not null, else by the LPT rule)
 hipError_t launch_sparse_plan(const AttnLaunch& a, int sched, const int32_t* head_xcd, hipStream_t st);
 hipError_t launch_sparse_exec(const AttnLaunch& a, int sched, hipStream_t st);
+// dense reference: natural-order chunk images (dense_tile_bytes) in tiles,
+// then query tiles of 256 tokens over every key
+size_t dense_tile_bytes(int B, int L, int heads, int D);
 hipError_t launch_dense_attn(const void* q, const void* k, const void* v, void* o, int B, int L, int heads, int D,
-                             float scale, hipStream_t st);
+                             float scale, void* tiles, hipStream_t st);
 
 }  // namespace fva

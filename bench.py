@@ -151,17 +151,19 @@ def main():
     dense_ms = None
     if not args.no_dense:
         od = torch.empty_like(q)
+        ws_d = fva.workspace(fva.dense_workspace_bytes(shape), q.device)
         for _ in range(2):
-            fva.dense_attn_ref(q, k, v, out=od, stream=stream)
+            fva.dense_attn_ref(q, k, v, out=od, ws=ws_d, stream=stream)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         nd = max(3, args.steps // 4)
         e0.record(stream)
         for _ in range(nd):
-            fva.dense_attn_ref(q, k, v, out=od, stream=stream)
+            fva.dense_attn_ref(q, k, v, out=od, ws=ws_d, stream=stream)
         e1.record(stream)
         torch.cuda.synchronize()
         dense_ms = e0.elapsed_time(e1) / nd
+        del ws_d
 
     # CU imbalance of the persistent kernel (separate, untimed run with a trace)
     nwg = fva.attn_workgroups(shape, wl.grid, wl.block)

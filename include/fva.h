@@ -226,10 +226,16 @@ fva_status fva_sasa(const fva_desc* desc, const fva_grid* grid, const uint32_t* 
                     int64_t* xcd_load, void* ws, size_t ws_bytes, void* stream);
 
 /* Dense softmax attention over all L tokens (the FlashAttention baseline the
- * FVAttn abstract measures against), same numerics as fva_sparse_attn and
- * no workspace.  Errors: INVALID_ARG, SCALE, UNSUPPORTED, DEVICE. */
+ * FVAttn abstract measures against), on the same kernel as fva_sparse_attn:
+ * the sequence is one block of L tokens whose K and V are re-tiled in natural
+ * order into the workspace (64-token chunks), and every 256-token query tile
+ * attends to every chunk.  q, k, v, o as for fva_sparse_attn.
+ *   ws   device workspace of at least fva_dense_workspace_bytes(), 256-byte
+ *        aligned, caller-owned; its contents on return are unspecified
+ * Errors: INVALID_ARG, SCALE, UNSUPPORTED, WORKSPACE, DEVICE. */
+size_t fva_dense_workspace_bytes(const fva_desc* desc);
 fva_status fva_dense_attn_ref(const void* q, const void* k, const void* v, void* o, const fva_desc* desc, float scale,
-                              void* stream);
+                              void* ws, size_t ws_bytes, void* stream);
 
 /* Host helper: CU imbalance from a trace copied to host memory.  Groups the
  * workgroups by compute unit (xcc, shader engine, CU) and returns max/mean of

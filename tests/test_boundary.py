@@ -101,9 +101,19 @@ def test_attn_validation_errors():
     assert "num_blocks 8448 > 8192" in _err()
     assert lib.fva_attn_plan(FAKE, FAKE, ctypes.byref(big_desc), ctypes.byref(big_grid), FAKE, 0, None, FAKE,
                              1 << 40, None) == 6
-    assert lib.fva_dense_attn_ref(FAKE, FAKE, FAKE, FAKE, ctypes.byref(desc), ctypes.c_float(0.1), None) == 4
-    assert lib.fva_dense_attn_ref(FAKE, FAKE, FAKE, None, ctypes.byref(desc), ctypes.c_float(128 ** -0.5),
-                                  None) == 1
+    need = lib.fva_dense_workspace_bytes(ctypes.byref(desc))
+    # 40 heads x ceil(27280 / 64) = 427 chunk images of 35,840 bytes
+    assert need == 40 * 427 * 35840
+    good = 128 ** -0.5
+
+    def dense(o=FAKE, scale=good, ws=FAKE, ws_bytes=need):
+        return lib.fva_dense_attn_ref(FAKE, FAKE, FAKE, o, ctypes.byref(desc), ctypes.c_float(scale), ws, ws_bytes,
+                                      None)
+    assert dense(scale=0.1) == 4
+    assert dense(o=None) == 1
+    assert dense(ws=None) == 5
+    assert dense(ws_bytes=need - 1) == 5
+    assert "workspace" in _err()
 
 
 def test_status_names():
