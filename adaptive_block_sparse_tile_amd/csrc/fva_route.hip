@@ -342,45 +342,107 @@ __device__ inline uint64_t order_key(double d) {
   return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
 }
 
-template <typename T>
-__device__ inline T wave_sum(T v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-  return v;
+// Wavefront reductions for the select kernel: four DPP steps (lane xor 1 and
+// xor 2 inside quads, then the 8- and 16-lane mirrors) leave every lane of a
+// 16-lane row with the row's total; the four row totals are then combined
+// in a fixed order.  Deterministic, and all VALU (no LDS round trips).
+constexpr int DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_MIRROR8 = 0x141, DPP_MIRROR16 = 0x140;
+
+template <int CTRL>
+__device__ inline uint32_t dpp_move(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ inline uint64_t dpp_move(uint64_t x) {
+  return (uint64_t)dpp_move<CTRL>((uint32_t)x) | ((uint64_t)dpp_move<CTRL>((uint32_t)(x >> 32)) << 32);
+}
+template <int CTRL>
+__device__ inline double dpp_move(double x) {
+  return __longlong_as_double((long long)dpp_move<CTRL>((uint64_t)__double_as_longlong(x)));
+}
+__device__ inline uint32_t read_lane(uint32_t x, int l) { return (uint32_t)__builtin_amdgcn_readlane((int)x, l); }
+__device__ inline uint64_t read_lane(uint64_t x, int l) {
+  return (uint64_t)read_lane((uint32_t)x, l) | ((uint64_t)read_lane((uint32_t)(x >> 32), l) << 32);
+}
+__device__ inline double read_lane(double x, int l) {
+  return __longlong_as_double((long long)read_lane((uint64_t)__double_as_longlong(x), l));
 }
 
-// fixed-order workgroup sum (lane tree, then wavefronts in order); all lanes get it
-template <typename T>
-__device__ inline T group_sum(T v, T* red, int nwaves) {
-  v = wave_sum(v);
-  const int wave = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[wave] = v;
-  __syncthreads();
-  T s = red[0];
-  for (int w = 1; w < nwaves; ++w) s += red[w];
-  return s;
+template <typename T, typename Op>
+__device__ inline T wave_reduce(T v, Op op) {
+  v = op(v, dpp_move<DPP_XOR1>(v));
+  v = op(v, dpp_move<DPP_XOR2>(v));
+  v = op(v, dpp_move<DPP_MIRROR8>(v));
+  v = op(v, dpp_move<DPP_MIRROR16>(v));
+  return op(op(read_lane(v, 0), read_lane(v, 16)), op(read_lane(v, 32), read_lane(v, 48)));
 }
+struct AddOp {
+  template <typename T>
+  __device__ T operator()(T a, T b) const { return a + b; }
+};
+struct MaxOp {
+  __device__ double operator()(double a, double b) const { return fmax(a, b); }
+  __device__ uint64_t operator()(uint64_t a, uint64_t b) const { return a > b ? a : b; }
+};
+struct MinOp {
+  __device__ uint64_t operator()(uint64_t a, uint64_t b) const { return a < b ? a : b; }
+};
 
-__device__ inline double group_max(double v, double* red, int nwaves) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = fmax(v, __shfl_xor(v, off));
-  const int wave = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[wave] = v;
-  __syncthreads();
-  double s = red[0];
-  for (int w = 1; w < nwaves; ++w) s = fmax(s, red[w]);
-  return s;
-}
+// Workgroup reductions through a double-buffered slot per wavefront: one
+// barrier per reduction (a slot is rewritten two reductions later, after
+// every wavefront has passed the barrier in between).  The wavefront totals
+// are combined in wavefront order; every lane gets the result.
+struct GroupRed {
+  uint64_t* slot;  // LDS [2][2][4]: two values per wavefront, two buffers
+  int nwaves, flip;
+  template <typename T, typename Op>
+  __device__ T reduce(T v, Op op) {
+    const T w = wave_reduce(v, op);
+    uint64_t* buf = slot + flip * 8;
+    if ((threadIdx.x & 63) == 0) buf[threadIdx.x >> 6] = to_bits(w);
+    __syncthreads();
+    T r = from_bits<T>(buf[0]);
+    for (int i = 1; i < nwaves; ++i) r = op(r, from_bits<T>(buf[i]));
+    flip ^= 1;
+    return r;
+  }
+  // two reductions in one round (a and b of the same width)
+  template <typename T, typename OpA, typename OpB>
+  __device__ void reduce2(T* a, T* b, OpA opa, OpB opb) {
+    const T wa = wave_reduce(*a, opa), wb = wave_reduce(*b, opb);
+    uint64_t* buf = slot + flip * 8;
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) {
+      buf[wave] = to_bits(wa);
+      buf[4 + wave] = to_bits(wb);
+    }
+    __syncthreads();
+    T ra = from_bits<T>(buf[0]), rb = from_bits<T>(buf[4]);
+    for (int w = 1; w < nwaves; ++w) {
+      ra = opa(ra, from_bits<T>(buf[w]));
+      rb = opb(rb, from_bits<T>(buf[4 + w]));
+    }
+    *a = ra;
+    *b = rb;
+    flip ^= 1;
+  }
+  __device__ static uint64_t to_bits(double x) { return (uint64_t)__double_as_longlong(x); }
+  __device__ static uint64_t to_bits(uint64_t x) { return x; }
+  __device__ static uint64_t to_bits(uint32_t x) { return x; }
+  template <typename T>
+  __device__ static T from_bits(uint64_t x) {
+    if constexpr (sizeof(T) == 4) return (T)(uint32_t)x;
+    else return __builtin_bit_cast(T, x);
+  }
+};
 
 __global__ __launch_bounds__(256) void route_select_kernel(const double* __restrict__ S, int N, int words,
                                                            float top_p, int k_floor, uint32_t* __restrict__ mask,
                                                            int32_t* __restrict__ kv_cnt,
                                                            uint32_t* __restrict__ status) {
-  __shared__ double redd[4];
-  __shared__ uint32_t redu[4];
+  __shared__ uint64_t red_slot[16];
   const int nwaves = blockDim.x >> 6;
+  GroupRed gr{red_slot, nwaves, 0};
   const int tid = threadIdx.x;
   const int64_t row = blockIdx.x;
   const double* s = S + row * N;
@@ -412,18 +474,18 @@ __global__ __launch_bounds__(256) void route_select_kernel(const double* __restr
     }
     return;
   }
-  const double M = group_max(lmax, redd, nwaves);
+  const double M = gr.reduce(lmax, MaxOp());
   double lz = 0.0;
-#pragma unroll
-  for (int e = 0; e < 32; ++e)
-    if (j0 + e < N) lz += exp(pr[e] - M);
-  const double Z = group_sum(lz, redd, nwaves);
 #pragma unroll
   for (int e = 0; e < 32; ++e) {
     const bool in = j0 + e < N;
     key[e] = in ? order_key(pr[e]) : 0ull;  // below every finite score
-    pr[e] = in ? exp(pr[e] - M) / Z : 0.0;
+    pr[e] = in ? exp(pr[e] - M) : 0.0;
+    lz += pr[e];
   }
+  const double Z = gr.reduce(lz, AddOp());
+#pragma unroll
+  for (int e = 0; e < 32; ++e) pr[e] = pr[e] / Z;
   uint64_t kmin = ~0ull, kmax = 0ull;
 #pragma unroll
   for (int e = 0; e < 32; ++e)
@@ -431,80 +493,100 @@ __global__ __launch_bounds__(256) void route_select_kernel(const double* __restr
       kmin = key[e] < kmin ? key[e] : kmin;
       kmax = key[e] > kmax ? key[e] : kmax;
     }
-  // workgroup min / max of the keys (as two u32 halves is not order safe: use
-  // the monotone map to double instead: keys of real blocks are > 0)
-  {
-    __shared__ unsigned long long kred[2][4];
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const unsigned long long a = __shfl_xor((unsigned long long)kmin, off);
-      const unsigned long long b = __shfl_xor((unsigned long long)kmax, off);
-      kmin = a < kmin ? a : kmin;
-      kmax = b > kmax ? b : kmax;
-    }
-    __syncthreads();
-    if ((tid & 63) == 0) {
-      kred[0][tid >> 6] = kmin;
-      kred[1][tid >> 6] = kmax;
-    }
-    __syncthreads();
-    kmin = kred[0][0];
-    kmax = kred[1][0];
-    for (int w = 1; w < nwaves; ++w) {
-      kmin = kred[0][w] < kmin ? kred[0][w] : kmin;
-      kmax = kred[1][w] > kmax ? kred[1][w] : kmax;
-    }
-  }
-  auto mass_ge = [&](uint64_t K) -> double {
+  gr.reduce2(&kmin, &kmax, MinOp(), MaxOp());
+  // mass and count of the blocks with key >= K (fixed summation order)
+  auto mass_count_ge = [&](uint64_t K, uint32_t* cnt) -> double {
     double m = 0.0;
-#pragma unroll
-    for (int e = 0; e < 32; ++e) m += key[e] >= K ? pr[e] : 0.0;
-    return group_sum(m, redd, nwaves);
-  };
-  auto count_ge = [&](uint64_t K) -> uint32_t {
     uint32_t c = 0;
 #pragma unroll
-    for (int e = 0; e < 32; ++e) c += (j0 + e < N && key[e] >= K) ? 1u : 0u;
-    return group_sum(c, redu, nwaves);
+    for (int e = 0; e < 32; ++e) {
+      const bool ge = j0 + e < N && key[e] >= K;
+      m += ge ? pr[e] : 0.0;
+      c += ge ? 1u : 0u;
+    }
+    double cd = (double)c;  // counts are exact in double
+    gr.reduce2(&m, &cd, AddOp(), AddOp());
+    *cnt = (uint32_t)cd;
+    return m;
+  };
+  // the only key in [lo, hi) (callers know there is exactly one)
+  auto only_key_in = [&](uint64_t lo, uint64_t hi) -> uint64_t {
+    uint64_t k = 0;
+#pragma unroll
+    for (int e = 0; e < 32; ++e)
+      if (j0 + e < N && key[e] >= lo && key[e] < hi) k = key[e];
+    return gr.reduce(k, MaxOp());
   };
 
+  // Both searches bisect the key range [lo, hi] keeping a predicate true at
+  // lo and false at hi, with the counts of keys >= lo and >= hi at hand:
+  // once a single key lies in [lo, hi), that key is the answer and the
+  // search stops (otherwise it runs until hi = lo + 1).  At the end no key
+  // lies in (lo, hi), so "keys > lo" are exactly "keys >= hi".
   const double p = (double)top_p;
+  uint32_t n_real = 0;
+  const double total = mass_count_ge(kmin, &n_real);
   int nstar;
+  uint64_t cut = 0;        // crossing key of the Top-p search
+  uint32_t cut_above = 0;  // blocks with key > cut
+  bool have_cut = false;
   if (p >= 1.0) {
     nstar = N;
   } else if (p <= 0.0) {
     nstar = 0;
-  } else if (mass_ge(kmin) < p) {
+  } else if (total < p) {
     nstar = N;  // rounding left the total below p: every block
   } else {
     // largest K with mass(key >= K) >= p: the key of the crossing block
     uint64_t lo = kmin, hi = kmax;
-    if (mass_ge(hi) >= p) {
+    uint32_t c_lo = n_real, c_hi = 0;
+    double m_hi = mass_count_ge(hi, &c_hi);
+    double above;
+    uint32_t n_above;
+    if (m_hi >= p) {
       lo = hi;
+      c_lo = c_hi;
+      above = 0.0;  // nothing above the largest key
+      n_above = 0;
     } else {
       while (hi - lo > 1) {
+        if (c_lo - c_hi == 1) {
+          lo = only_key_in(lo, hi);
+          break;
+        }
         const uint64_t mid = lo + (hi - lo) / 2;
-        if (mass_ge(mid) >= p) lo = mid;
-        else hi = mid;
+        uint32_t c_mid;
+        const double m = mass_count_ge(mid, &c_mid);
+        if (m >= p) {
+          lo = mid;
+          c_lo = c_mid;
+        } else {
+          hi = mid;
+          c_hi = c_mid;
+          m_hi = m;
+        }
       }
+      above = m_hi;
+      n_above = c_hi;
     }
     // blocks above the crossing key, then as many tied blocks as needed
-    const double above = lo == ~0ull ? 0.0 : mass_ge(lo + 1);
-    const uint32_t n_above = lo == ~0ull ? 0u : count_ge(lo + 1);
     double ptie = 0.0;
 #pragma unroll
     for (int e = 0; e < 32; ++e)
       if (key[e] == lo) ptie = pr[e];
     // every tied block has the same probability; any holder reports it
-    ptie = group_max(ptie, redd, nwaves);
+    ptie = gr.reduce(ptie, MaxOp());
     int need = 1;
     double c = above + ptie;
-    const int n_tie = (int)(count_ge(lo) - n_above);
+    const int n_tie = (int)(c_lo - n_above);
     while (c < p && need < n_tie) {
       c += ptie;
       ++need;
     }
     nstar = (int)n_above + need;
+    cut = lo;
+    cut_above = n_above;
+    have_cut = true;
   }
   const int keep = min(N, max(k_floor, nstar));
 
@@ -513,18 +595,40 @@ __global__ __launch_bounds__(256) void route_select_kernel(const double* __restr
     const int nb = min(32, N - j0);
     word = nb >= 32 ? 0xffffffffu : (nb > 0 ? ((1u << nb) - 1u) : 0u);
   } else {
-    // largest K with count(key >= K) >= keep
-    uint64_t lo = kmin, hi = kmax;
-    if (count_ge(hi) >= (uint32_t)keep) {
-      lo = hi;
+    // largest K with count(key >= K) >= keep; when the floor does not bind,
+    // that is the Top-p crossing key itself
+    uint64_t lo = kmin;
+    uint32_t n_above;
+    if (have_cut && keep == nstar) {
+      lo = cut;
+      n_above = cut_above;
     } else {
-      while (hi - lo > 1) {
-        const uint64_t mid = lo + (hi - lo) / 2;
-        if (count_ge(mid) >= (uint32_t)keep) lo = mid;
-        else hi = mid;
+      uint64_t hi = kmax;
+      uint32_t c_lo = n_real, c_hi = 0;
+      mass_count_ge(hi, &c_hi);
+      if (c_hi >= (uint32_t)keep) {
+        lo = hi;
+        n_above = 0;
+      } else {
+        while (hi - lo > 1) {
+          if (c_lo - c_hi == 1) {
+            lo = only_key_in(lo, hi);
+            break;
+          }
+          const uint64_t mid = lo + (hi - lo) / 2;
+          uint32_t c_mid;
+          mass_count_ge(mid, &c_mid);
+          if (c_mid >= (uint32_t)keep) {
+            lo = mid;
+            c_lo = c_mid;
+          } else {
+            hi = mid;
+            c_hi = c_mid;
+          }
+        }
+        n_above = c_hi;
       }
     }
-    const uint32_t n_above = lo == ~0ull ? 0u : count_ge(lo + 1);
     const uint32_t need = (uint32_t)keep - n_above;
     // ties at the cut key, in index order: exclusive prefix over lanes
     uint32_t my_ties = 0;
