@@ -574,19 +574,21 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
       }
     };
 
-    const int kt0 = ksel < 0 ? 0 : ksel;  // first key half this wavefront computes
-    if (wave_active && ready > 0) {
+    // S^T of one key half (K rows from kb; key half kt of a chunk with
+    // `valid` real keys for this wavefront) and its statistics, unpipelined
+    auto qk_only = [&](f32x16 (&sx)[QT], const bf16_bits* kb, int kt, int valid) __attribute__((always_inline)) {
 #pragma unroll
       for (int ds = 0; ds < DS; ++ds) {
-        const bf16x8 a = kread(kbase(ring0, kt0), ds);
+        const bf16x8 a = kread(kb, ds);
 #pragma unroll
-        for (int qt = 0; qt < QT; ++qt) {
-          sA[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qt][ds], ds == 0 ? negm[qt] : sA[qt], 0, 0, 0);
-        }
+        for (int qt = 0; qt < QT; ++qt)
+          sx[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qt][ds], ds == 0 ? negm[qt] : sx[qt], 0, 0, 0);
       }
 #pragma unroll
-      for (int step = 0; step < STAT_STEPS; ++step) stat_step(step, sA, v0, kt0);
-    }
+      for (int step = 0; step < STAT_STEPS; ++step) stat_step(step, sx, valid, kt);
+    };
+    const int kt0 = ksel < 0 ? 0 : ksel;  // first key half this wavefront computes
+    if (wave_active && ready > 0) qk_only(sA, kbase(ring0, kt0), kt0, v0);
     // the first AHEAD operands of a half: from its V^T (vc) and the K of the
     // next half (kn)
     bf16x8 opw[AHEAD];
@@ -722,7 +724,13 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
     // between sA and sB like everyone else's; its operand ring is reloaded
     // before each of its halves (what the slot before read ahead is not its
     // own).
+    //
+    // Grouped items: a wavefront whose own query block did not keep chunk c
+    // skips both halves of c; if its block keeps chunk c+1 it computes only
+    // the S^T of key half 0 of c+1 (the one result of c's second half it
+    // needs), and it reloads its operand ring before its next half.
     const bool sp = !DENSE && !GRP && ksel >= 0;
+    bool reload = false;
     auto chunk_step = [&](int s0) __attribute__((always_inline)) -> bool {
       const int s1 = (s0 + 1) % STAGES;
       const int sl = (s0 + LOOK) % STAGES;
@@ -738,14 +746,23 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
       // a one-half wavefront's half: V^T of (c, ksel), K of (c+1, ksel)
       const bf16_bits* vs = vbase(S0, sp ? ksel : 0);
       const bf16_bits* ks = kbase(S1, sp ? ksel : 0);
+      const bool skip = GRP && v0 == 0;
+      if (GRP && wave_active && skip) {
+        if (v1 > 0) qk_only(sA, kbase(S1, 0), 0, v1);
+        reload = true;
+      }
+      if (GRP && wave_active && !skip && reload) {
+        preload(vbase(S0, 0), kbase(S0, 1));
+        reload = false;
+      }
       // first slot, two-half wavefronts: key half 0 of c; Q K^T of half 1 of c
-      if (wave_active && (!sp || even)) {
+      if (wave_active && !skip && (!sp || even)) {
         if (sp) preload(vs, ks);
         half(sA, sB, sp ? vs : vbase(S0, 0), sp ? ks : kbase(S0, 1), sp ? ksel : 1, sp ? v1 : v0, vbase(S0, 1),
              kbase(S1, 0));
       }
       // second slot, two-half wavefronts: key half 1 of c; Q K^T of half 0 of c+1
-      if (wave_active && (!sp || !even)) {
+      if (wave_active && !skip && (!sp || !even)) {
         if (sp) preload(vs, ks);
         half(sB, sA, sp ? vs : vbase(S0, 1), sp ? ks : kbase(S1, 0), sp ? ksel : 0, v1, vbase(S1, 0),
              kbase(S1, 1));
