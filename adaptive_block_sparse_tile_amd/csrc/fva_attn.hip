@@ -542,8 +542,8 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
     // so they sit between the P V MFMAs of the half before the one that uses
     // them, off the critical path.
     constexpr int STAT_STEPS = 7;
-    float mxc[QT];    // row max of the half to be exponentiated next
-    float mpart[QT];  // partial row max
+    float mxc[QT];    // this lane's max over its 16 keys of the half to be exponentiated next
+    float mpart[QT];  // partial lane max
     bool rc = false;  // some row of that half needs its running max raised
     auto stat_step = [&](int step, f32x16 (&sx)[QT], int valid, int kt) __attribute__((always_inline)) {
       if (step == 0) {
@@ -557,16 +557,19 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
               if (8 * (r >> 2) + (r & 3) >= lim) sx[qt][r] = -INFINITY;
         }
       } else if (step <= 4) {
+        // two 3-input maxima per 4 keys
         const int r0 = 4 * (step - 1);
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) {
-          const float m = step == 1 ? sx[qt][0] : fmaxf(mpart[qt], sx[qt][r0]);
-          mpart[qt] = fmaxf(fmaxf(m, sx[qt][r0 + 1]), fmaxf(sx[qt][r0 + 2], sx[qt][r0 + 3]));
+          const float m = step == 1 ? fmaxf(fmaxf(sx[qt][0], sx[qt][1]), sx[qt][2])
+                                    : fmaxf(fmaxf(mpart[qt], sx[qt][r0]), sx[qt][r0 + 1]);
+          mpart[qt] = step == 1 ? fmaxf(m, sx[qt][3]) : fmaxf(fmaxf(m, sx[qt][r0 + 2]), sx[qt][r0 + 3]);
+          if (step == 4) mxc[qt] = mpart[qt];
         }
-      } else if (step == 5) {
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) mxc[qt] = max_halves(mpart[qt]);
-      } else {
+      } else if (step == 6) {
+        // a row's two lanes share its threshold, so the lane maxima decide
+        // whether some row must move without combining the lane pair (the
+        // raise itself takes the row max)
         bool r = false;
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) r = r || (mxc[qt] > thr[qt]);
@@ -620,7 +623,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
         // has still seen no real key keeps offset 0
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) {
-          const float m_new = fmaxf(m_run[qt], moff[qt] + mxc[qt]);
+          const float m_new = fmaxf(m_run[qt], moff[qt] + max_halves(mxc[qt]));
           const float o_new = m_new > 0.5f * M_NONE ? m_new : 0.f;
           const float shift = o_new - moff[qt];
           const float alpha = __builtin_amdgcn_exp2f(m_run[qt] - m_new);
