@@ -104,7 +104,7 @@ RouteWs route_ws_layout(const fva_desc* d, const fva::Geo& g) {
 }
 
 struct AttnWs {
-  size_t tok, cnt, tiles, keys, rank, order, head_pos, qoff, qctr, total;
+  size_t tok, cnt, tiles, keys, rank, order, head_pos, head_cost, qoff, qctr, total;
 };
 
 AttnWs attn_ws_layout(const fva_desc* d, const fva::Geo& g) {
@@ -120,6 +120,7 @@ AttnWs attn_ws_layout(const fva_desc* d, const fva::Geo& g) {
   w.rank = off; off += align_up(items * sizeof(uint32_t));
   w.order = off; off += align_up(items * sizeof(int32_t));
   w.head_pos = off; off += align_up(bh * sizeof(int32_t));
+  w.head_cost = off; off += align_up(bh * sizeof(uint64_t));
   w.qoff = off; off += align_up(16 * sizeof(int32_t));
   w.qctr = off; off += align_up(16 * sizeof(uint32_t));
   w.total = off;
@@ -233,6 +234,7 @@ static fva_status sparse_setup(const void* q, const void* k, const void* v, void
   a->rank = (uint32_t*)(w + lay.rank);
   a->order = (int32_t*)(w + lay.order);
   a->head_pos = (int32_t*)(w + lay.head_pos);
+  a->head_cost = (uint64_t*)(w + lay.head_cost);
   a->qoff = (int32_t*)(w + lay.qoff);
   a->qctr = (uint32_t*)(w + lay.qctr);
   return FVA_OK;

@@ -878,8 +878,11 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
 // ---------------------------------------------------------------------------
 
 // Block-ordered token table and real counts: one workgroup per block.
-__global__ __launch_bounds__(256) void layout_kernel(Geo g, int32_t* __restrict__ tok, int32_t* __restrict__ cnt) {
+__global__ __launch_bounds__(256) void layout_kernel(Geo g, int32_t* __restrict__ tok, int32_t* __restrict__ cnt,
+                                                     uint64_t* __restrict__ head_cost, int BH) {
   const int n = blockIdx.x;
+  if (n == 0)
+    for (int x = threadIdx.x; x < BH; x += blockDim.x) head_cost[x] = 0;  // summed by cost_kernel
   const Box bx = block_box(g, n);
   if (threadIdx.x == 0) cnt[n] = bx.count;
   const int plane = bx.eh * bx.ew;
@@ -954,7 +957,7 @@ __global__ __launch_bounds__(256) void tile_kernel(const bf16_bits* __restrict__
 // descending cost, ties to the lower item id.
 __global__ __launch_bounds__(256) void cost_kernel(AttnParams p, const int32_t* __restrict__ cnt,
                                                    uint64_t* __restrict__ keys, uint32_t* __restrict__ rank,
-                                                   uint32_t* __restrict__ qctr) {
+                                                   uint32_t* __restrict__ qctr, uint64_t* __restrict__ head_cost) {
   const int item = blockIdx.x * blockDim.x + threadIdx.x;
   if (item < NXCD) qctr[item] = 0u;
   if (item >= p.n_items) return;
@@ -983,30 +986,22 @@ __global__ __launch_bounds__(256) void cost_kernel(AttnParams p, const int32_t* 
   const uint32_t cost = qrows * kv;
   keys[item] = ((uint64_t)cost << 32) | (uint64_t)(~(uint32_t)item);
   rank[item] = 0u;
+  atomicAdd((unsigned long long*)&head_cost[bh], (unsigned long long)cost);  // integer sum: any order
 }
 
 // Heads to XCDs, longest first (single workgroup).  Head cost = sum of its
-// items' costs; heads are taken in descending cost (ties: lower head) and
+// items' costs (summed by cost_kernel); heads are taken in descending cost (ties: lower head) and
 // each goes to the XCD with the least assigned cost (ties: lower XCD).
 // Writes each head's first position in the order array and the queue
 // segments qoff[0..NXCD].  NAIVE puts every head on queue 0 in head order.
 // forced (nullable): each head's XCD, given by the caller instead of chosen.
-__global__ __launch_bounds__(256) void head_plan_kernel(const uint64_t* __restrict__ keys, int N, int BH, bool lpt,
-                                                        const int32_t* __restrict__ forced,
+__global__ __launch_bounds__(256) void head_plan_kernel(const uint64_t* __restrict__ head_cost, int N, int BH,
+                                                        bool lpt, const int32_t* __restrict__ forced,
                                                         int32_t* __restrict__ head_pos, int32_t* __restrict__ qoff) {
   extern __shared__ uint64_t hsh[];  // [BH] head costs, then [BH] int32 order
   uint64_t* hcost = hsh;
   int32_t* horder = (int32_t*)(hsh + BH);
-  // one wavefront per head: lanes sum strided items, then a lane reduction
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
-  for (int x = wave; x < BH; x += nwaves) {
-    uint64_t s = 0;
-    if (lpt)
-      for (int i = lane; i < N; i += 64) s += keys[(int64_t)x * N + i] >> 32;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
-    if (lane == 0) hcost[x] = s;
-  }
+  for (int x = threadIdx.x; x < BH; x += blockDim.x) hcost[x] = lpt ? head_cost[x] : 0;
   __syncthreads();
   for (int x = threadIdx.x; x < BH; x += blockDim.x) {
     int r = 0;
@@ -1164,7 +1159,7 @@ hipError_t launch_sparse_plan(const AttnLaunch& a, int sched, const int32_t* hea
   const AttnParams prm = sparse_params(a);
   const int BH = a.B * a.heads;
   const int n_items = prm.n_items, per_head = prm.n_groups, cpb = prm.cpb;
-  hipLaunchKernelGGL(layout_kernel, dim3(a.g.N), dim3(256), 0, st, a.g, a.tok, a.blk_cnt);
+  hipLaunchKernelGGL(layout_kernel, dim3(a.g.N), dim3(256), 0, st, a.g, a.tok, a.blk_cnt, a.head_cost, BH);
   const unsigned slots = (unsigned)(BH * a.g.N * cpb);
   if (a.D == 128)
     hipLaunchKernelGGL(tile_kernel<128>, dim3(slots), dim3(256), 0, st, (const bf16_bits*)a.k, (const bf16_bits*)a.v,
@@ -1173,8 +1168,8 @@ hipError_t launch_sparse_plan(const AttnLaunch& a, int sched, const int32_t* hea
     hipLaunchKernelGGL(tile_kernel<64>, dim3(slots), dim3(256), 0, st, (const bf16_bits*)a.k, (const bf16_bits*)a.v,
                        a.tok, a.g, a.L, a.heads, cpb, a.tiles);
   hipLaunchKernelGGL(cost_kernel, dim3((n_items + 255) / 256), dim3(256), 0, st, prm, a.blk_cnt, a.keys, a.rank,
-                     a.qctr);
-  hipLaunchKernelGGL(head_plan_kernel, dim3(1), dim3(256), (size_t)BH * 12, st, a.keys, per_head, BH, lpt,
+                     a.qctr, a.head_cost);
+  hipLaunchKernelGGL(head_plan_kernel, dim3(1), dim3(256), (size_t)BH * 12, st, a.head_cost, per_head, BH, lpt,
                      sched == 2 ? head_xcd : nullptr, a.head_pos, a.qoff);
   if (lpt)
     hipLaunchKernelGGL(rank_kernel, dim3((n_items + 255) / 256, (n_items + 2047) / 2048), dim3(256), 0, st, a.keys,

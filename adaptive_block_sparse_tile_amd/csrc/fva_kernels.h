@@ -42,6 +42,7 @@ struct AttnLaunch {
   uint32_t* rank;      // [items] rank inside the item's head
   int32_t* order;      // [items] queue contents
   int32_t* head_pos;   // [B*heads] first order slot of each head
+  uint64_t* head_cost; // [B*heads] summed item costs of each head
   int32_t* qoff;       // [9] queue segments (one per XCD)
   uint32_t* qctr;      // [8] queue pop counters
 };

@@ -217,6 +217,8 @@ def _custom(name, heads, D, grid, block, top_p, k_floor, batch=1, modes=8):
     _custom("dense_floor", 2, 128, (9, 17, 23), (4, 8, 8), 0.5, 18),
     # 65..128-token blocks: two query blocks per work item, the last group ragged
     _custom("vol128_ragged", 2, 128, (7, 9, 21), (4, 4, 8), 0.8, 2),
+    # every block at most 32 tokens: each tile's key-half-1 wavefront sees no real key
+    _custom("halfkey_blocks", 2, 128, (1, 3, 40), (4, 8, 8), 0.9, 1),
     # N = 576 > 512 key blocks: the bisection router
     _custom("select_n576", 2, 64, (12, 16, 24), (2, 2, 2), 0.7, 3),
     _custom("select_topk", 1, 128, (12, 16, 24), (2, 2, 2), 0.0, 7),
