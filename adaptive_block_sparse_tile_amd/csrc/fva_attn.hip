@@ -47,27 +47,22 @@ constexpr int NXCD = 8;     // XCDs of an MI355X
 
 // A chunk of 64 keys, in LDS and in the tiled copy in HBM alike (the copy
 // is byte-identical to the LDS image, so it moves by direct global-to-LDS
-// loads): K [64][D] row-major, then V^T [D][64] with key positions permuted
-// by pi, every row padded by 16 bytes (K rows D+8, V^T rows 64+8 elements;
-// the pad is zero).  Rows 16 bytes apart in bank order make the 16-byte operand
-// reads of 16 consecutive rows hit distinct banks (272 = 17*16 and
-// 144 = 9*16, both odd multiples of 16 bytes), and each operand address is a
-// per-lane base plus a compile-time offset.
+// loads), stored as 16-byte pieces (8 bf16) in piece-major order:
+//   K:   piece c (d = 8c .. 8c+7) of key row r at piece index c*64 + r;
+//   V^T: piece g (positions 8g .. 8g+7, key k at position pi(k)) of row d at
+//        index D*8 + g*D + d.
+// An MFMA operand read by 16 consecutive lanes (16 consecutive K rows, or 16
+// consecutive d) then covers 256 contiguous bytes, one piece per bank group,
+// so there are no bank conflicts without any row padding; the image is
+// exactly 2*64*D*2 bytes (a whole number of 1 KB DMA pieces, 4 per
+// wavefront for D = 128), and each operand address is a per-lane base plus
+// a compile-time offset.
 template <int D>
 struct Lds {
-  static constexpr int KROW = D + 8;
-  static constexpr int VROW = KCH + 8;
-  static constexpr int VBASE = KCH * KROW;
-  static constexpr int ELEMS = KCH * KROW + D * VROW;
-  __host__ __device__ static constexpr int k_off(int row, int col) { return row * KROW + col; }
-  __host__ __device__ static constexpr int v_off(int d, int pos) { return VBASE + d * VROW + pos; }
-  // element offset in LDS of the 16-byte piece s of the compact image
-  __host__ __device__ static int piece_off(int s) {
-    constexpr int KP = KCH * D / 8;
-    if (s < KP) return k_off(s / (D / 8), (s % (D / 8)) * 8);
-    s -= KP;
-    return v_off(s / 8, (s % 8) * 8);
-  }
+  static constexpr int VBASE = KCH * D;
+  static constexpr int ELEMS = 2 * KCH * D;
+  __host__ __device__ static constexpr int k_off(int row, int col) { return ((col >> 3) * KCH + row) * 8 + (col & 7); }
+  __host__ __device__ static constexpr int v_off(int d, int pos) { return VBASE + ((pos >> 3) * D + d) * 8 + (pos & 7); }
 };
 
 // Key k of a chunk sits at V^T position pi(k): inside each group of 16 keys,
@@ -513,8 +508,10 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
     static_assert(NOPS % AHEAD == 0 && EPS % 2 == 0, "operand ring and probability pairs");
     f32x16 sA[QT], sB[QT];
     // operand bases of key half kt of a chunk image: its K rows, its V^T columns
-    auto kbase = [](const bf16_bits* img, int kt) -> const bf16_bits* { return img + 32 * kt * Lds<D>::KROW; };
-    auto vbase = [](const bf16_bits* img, int kt) -> const bf16_bits* { return img + 32 * kt; };
+    auto kbase = [](const bf16_bits* img, int kt) -> const bf16_bits* { return img + Lds<D>::k_off(32 * kt, 0); };
+    auto vbase = [](const bf16_bits* img, int kt) -> const bf16_bits* {
+      return img + (Lds<D>::v_off(0, 32 * kt) - Lds<D>::VBASE);
+    };
     auto kread = [&](const bf16_bits* kb, int ds) -> bf16x8 {
       return *(const bf16x8*)(kb + Lds<D>::k_off(lr, 16 * ds + 8 * hi));
     };
@@ -894,15 +891,17 @@ __global__ __launch_bounds__(256) void layout_kernel(Geo g, int32_t* __restrict_
 }
 
 // Chunk images of K and V in the LDS layout: one workgroup per (b, h,
-// block, chunk) slot.  Rows past the block's real count and the row pads are
-// zero.  The image is assembled in LDS and written out linearly, so every
-// store covers whole cache lines.  tok = null: the tokens are in their
-// natural order (the dense reference's single block of L tokens).
+// block, chunk) slot.  Rows past the block's real count are zero.  K and V
+// rows are read as whole token rows (16 lanes per 256-byte row), staged in
+// LDS row-major (rows padded by 16 bytes, so the column reads below hit
+// distinct banks), and written out piece-major, each thread storing the next
+// 16 bytes of the image.  tok = null: the tokens are in their natural order
+// (the dense reference's single block of L tokens).
 template <int D>
 __global__ __launch_bounds__(256) void tile_kernel(const bf16_bits* __restrict__ k, const bf16_bits* __restrict__ v,
                                                    const int32_t* __restrict__ tok, Geo g, int L, int heads, int cpb,
                                                    bf16_bits* __restrict__ tiles) {
-  __shared__ __attribute__((aligned(16))) bf16_bits im[Lds<D>::ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16_bits ks[KCH][D + 8];
   __shared__ __attribute__((aligned(16))) bf16_bits vs[KCH][D + 8];
   const int cs = blockIdx.x;
   const int c = cs % cpb;
@@ -914,12 +913,8 @@ __global__ __launch_bounds__(256) void tile_kernel(const bf16_bits* __restrict__
   if (valid <= 0) return;  // slot past the block's chunks: never read
   const int64_t rs = (int64_t)heads * D;
   const int64_t head_off = (int64_t)b * L * rs + (int64_t)h * D;
-  constexpr int PIECES = KCH * D / 8;
+  constexpr int PIECES = KCH * D / 8;  // 16-byte pieces of K (and of V)
   const u32x4 zero = {0u, 0u, 0u, 0u};
-  for (int s = threadIdx.x; s < KCH + D; s += 256) {  // the 16-byte pad of every K and V^T row
-    if (s < KCH) *(u32x4*)(im + Lds<D>::k_off(s, D)) = zero;
-    else *(u32x4*)(im + Lds<D>::v_off(s - KCH, KCH)) = zero;
-  }
   for (int s = threadIdx.x; s < PIECES; s += 256) {
     const int row = s / (D / 8), piece = s % (D / 8);
     u32x4 kx = zero, vx = zero;
@@ -929,25 +924,26 @@ __global__ __launch_bounds__(256) void tile_kernel(const bf16_bits* __restrict__
       kx = *(const u32x4*)(k + head_off + t * rs + piece * 8);
       vx = *(const u32x4*)(v + head_off + t * rs + piece * 8);
     }
-    *(u32x4*)(im + Lds<D>::k_off(row, piece * 8)) = kx;
+    *(u32x4*)&ks[row][piece * 8] = kx;
     *(u32x4*)&vs[row][piece * 8] = vx;
   }
   __syncthreads();
-  for (int s = threadIdx.x; s < D * 8; s += 256) {
-    const int d = s / 8, piece = s % 8;
+  bf16_bits* dst = tiles + (int64_t)cs * Lds<D>::ELEMS;
+  for (int s = threadIdx.x; s < PIECES; s += 256) {  // K piece s//64 of row s%64
+    const int piece = s / KCH, row = s % KCH;
+    *(u32x4*)(dst + Lds<D>::k_off(row, piece * 8)) = *(const u32x4*)&ks[row][piece * 8];
+  }
+  for (int s = threadIdx.x; s < D * 8; s += 256) {  // V^T piece s//D (positions 8p..8p+7) of row d = s%D
+    const int piece = s / D, d = s % D;
     uint32_t w[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int k0 = pi_key(piece * 8 + 2 * e), k1 = pi_key(piece * 8 + 2 * e + 1);
       w[e] = (uint32_t)vs[k0][d] | ((uint32_t)vs[k1][d] << 16);
     }
-    u32x4 x = {w[0], w[1], w[2], w[3]};
-    *(u32x4*)(im + Lds<D>::v_off(d, piece * 8)) = x;
+    const u32x4 x = {w[0], w[1], w[2], w[3]};
+    *(u32x4*)(dst + Lds<D>::v_off(d, piece * 8)) = x;
   }
-  __syncthreads();
-  u32x4* dst = (u32x4*)(tiles + (int64_t)cs * Lds<D>::ELEMS);
-  const u32x4* src = (const u32x4*)im;
-  for (int s = threadIdx.x; s < Lds<D>::ELEMS / 8; s += 256) dst[s] = src[s];
 }
 
 // Work of every item (query rows x real key tokens of the union of its

@@ -102,8 +102,8 @@ def test_attn_validation_errors():
     assert lib.fva_attn_plan(FAKE, FAKE, ctypes.byref(big_desc), ctypes.byref(big_grid), FAKE, 0, None, FAKE,
                              1 << 40, None) == 6
     need = lib.fva_dense_workspace_bytes(ctypes.byref(desc))
-    # 40 heads x ceil(27280 / 64) = 427 chunk images of 35,840 bytes
-    assert need == 40 * 427 * 35840
+    # 40 heads x ceil(27280 / 64) = 427 chunk images of 32,768 bytes (64 keys x 128 x bf16, K and V)
+    assert need == 40 * 427 * 32768
     good = 128 ** -0.5
 
     def dense(o=FAKE, scale=good, ws=FAKE, ws_bytes=need):
