@@ -26,7 +26,8 @@ SCHEDS = {"lpt": SCHED_LPT, "naive": SCHED_NAIVE, "xcd": SCHED_XCD}
 
 # every symbol include/fva.h declares
 EXPORTS = ["fva_num_blocks", "fva_route_workspace_bytes", "fva_attn_workspace_bytes", "fva_attn_workgroups",
-           "fva_route", "fva_static_mask", "fva_sparse_attn", "fva_attn_plan", "fva_attn_exec", "fva_sasa_workspace_bytes", "fva_sasa",
+           "fva_route", "fva_static_mask", "fva_sparse_attn", "fva_attn_plan", "fva_attn_exec", "fva_attn_items",
+           "fva_attn_schedule", "fva_sasa_workspace_bytes", "fva_sasa",
            "fva_dense_workspace_bytes", "fva_dense_attn_ref",
            "fva_trace_imbalance", "fva_last_error", "fva_status_name"]
 
@@ -87,6 +88,10 @@ def load():
     lib.fva_attn_plan.argtypes = [_P, _P, D, G, _P, ctypes.c_int32, _P, _P, ctypes.c_size_t, _P]
     lib.fva_attn_exec.restype = ctypes.c_int
     lib.fva_attn_exec.argtypes = [_P, _P, D, G, _P, ctypes.c_float, ctypes.c_int32, _P, _P, ctypes.c_size_t, _P]
+    lib.fva_attn_items.restype = ctypes.c_int32
+    lib.fva_attn_items.argtypes = [D, G]
+    lib.fva_attn_schedule.restype = ctypes.c_int
+    lib.fva_attn_schedule.argtypes = [D, G, _P, ctypes.c_size_t, _P, _P, _P, _P]
     lib.fva_sasa_workspace_bytes.restype = ctypes.c_size_t
     lib.fva_sasa_workspace_bytes.argtypes = [D, G, ctypes.c_int32]
     lib.fva_sasa.restype = ctypes.c_int
@@ -258,6 +263,28 @@ def attn_exec(q, grid, block, mask, ws, scale=None, sched: str = "lpt", trace=No
                                 ctypes.byref(make_grid(grid, block)), mask.data_ptr(), float(scale), SCHEDS[sched],
                                 tp, ws.data_ptr(), ws.numel(), _stream_ptr(stream)))
     return o
+
+
+def attn_items(shape, grid, block) -> int:
+    """Number of work items of the sparse attention for q/k/v of shape [B, L, heads, D]."""
+    n = int(load().fva_attn_items(ctypes.byref(make_desc(*shape)), ctypes.byref(make_grid(grid, block))))
+    if n < 0:
+        raise FvaError(1, load().fva_last_error().decode() or "invalid shape or grid")
+    return n
+
+
+def attn_schedule(shape, grid, block, ws, stream=None):
+    """The schedule a plan wrote into ws -> (order int32 [items], qoff int32 [9],
+    cost int32 [items] holding the uint32 item costs), device tensors."""
+    torch = _torch()
+    n = attn_items(shape, grid, block)
+    order = torch.empty(n, dtype=torch.int32, device=ws.device)
+    qoff = torch.empty(9, dtype=torch.int32, device=ws.device)
+    cost = torch.empty(n, dtype=torch.int32, device=ws.device)
+    _check(load().fva_attn_schedule(ctypes.byref(make_desc(*shape)), ctypes.byref(make_grid(grid, block)),
+                                    ws.data_ptr(), ws.numel(), order.data_ptr(), qoff.data_ptr(), cost.data_ptr(),
+                                    _stream_ptr(stream)))
+    return order, qoff, cost
 
 
 def sasa_workspace_bytes(shape, grid, block, rounds) -> int:

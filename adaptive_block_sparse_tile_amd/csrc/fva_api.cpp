@@ -345,6 +345,33 @@ fva_status fva_attn_exec(const void* q, void* o, const fva_desc* desc, const fva
   return ok();
 }
 
+int32_t fva_attn_items(const fva_desc* desc, const fva_grid* grid) {
+  fva::Geo g;
+  if (check_desc(desc) != FVA_OK || check_grid(desc, grid, &g) != FVA_OK) return -1;
+  const int64_t n = (int64_t)desc->B * desc->heads * fva::attn_items_per_head(g);
+  return n > INT32_MAX ? -1 : (int32_t)n;
+}
+
+fva_status fva_attn_schedule(const fva_desc* desc, const fva_grid* grid, const void* ws, size_t ws_bytes,
+                             int32_t* order, int32_t* qoff, uint32_t* cost, void* stream) {
+  if (!order || !qoff) return fail(FVA_ERR_INVALID_ARG, "order and qoff must not be null");
+  fva_status st = check_desc(desc);
+  if (st != FVA_OK) return st;
+  fva::Geo g;
+  if ((st = check_grid(desc, grid, &g)) != FVA_OK) return st;
+  const AttnWs lay = attn_ws_layout(desc, g);
+  if ((st = check_ws(ws, ws_bytes, lay.total)) != FVA_OK) return st;
+  const int64_t items = (int64_t)desc->B * desc->heads * fva::attn_items_per_head(g);
+  const char* w = (const char*)ws;
+  const hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(order, w + lay.order, (size_t)items * sizeof(int32_t), hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(qoff, w + lay.qoff, 9 * sizeof(int32_t), hipMemcpyDeviceToDevice, s);  // 8 queues + end
+  if (e == hipSuccess && cost) e = fva::launch_item_costs((const uint64_t*)(w + lay.keys), items, cost, s);
+  if (e != hipSuccess) return device_error(e, "schedule copy");
+  return ok();
+}
+
 size_t fva_dense_workspace_bytes(const fva_desc* desc) {
   if (check_desc(desc) != FVA_OK) return 0;
   return align_up(fva::dense_tile_bytes(desc->B, desc->L, desc->heads, desc->D));

@@ -950,12 +950,19 @@ __global__ __launch_bounds__(256) void tile_kernel(const bf16_bits* __restrict__
 // members' kept blocks: the time the item takes), its LPT sort key, and the
 // reset of the queue counters.  cost < 2^32: an item holds at most 256 query
 // rows and L < 2^24.  key = cost << 32 | ~item: descending keys give
-// descending cost, ties to the lower item id.
-__global__ __launch_bounds__(256) void cost_kernel(AttnParams p, const int32_t* __restrict__ cnt,
-                                                   uint64_t* __restrict__ keys, uint32_t* __restrict__ rank,
-                                                   uint32_t* __restrict__ qctr, uint64_t* __restrict__ head_cost) {
-  const int item = blockIdx.x * blockDim.x + threadIdx.x;
-  if (item < NXCD) qctr[item] = 0u;
+// descending cost, ties to the lower item id.  One wavefront per item, its
+// lanes over the mask words; the block counts are staged in LDS (N <= 8192).
+constexpr int COST_WAVES = 8;
+__global__ __launch_bounds__(COST_WAVES * 64) void cost_kernel(AttnParams p, const int32_t* __restrict__ cnt,
+                                                               uint64_t* __restrict__ keys, uint32_t* __restrict__ rank,
+                                                               uint32_t* __restrict__ qctr,
+                                                               uint64_t* __restrict__ head_cost) {
+  extern __shared__ int32_t cnt_s[];  // [N]
+  for (int j = threadIdx.x; j < p.g.N; j += COST_WAVES * 64) cnt_s[j] = cnt[j];
+  if (blockIdx.x == 0 && threadIdx.x < NXCD) qctr[threadIdx.x] = 0u;
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int item = blockIdx.x * COST_WAVES + (threadIdx.x >> 6);
   if (item >= p.n_items) return;
   const int gid = item % p.n_groups, bh = item / p.n_groups;
   const uint32_t* rows[4];
@@ -965,24 +972,27 @@ __global__ __launch_bounds__(256) void cost_kernel(AttnParams p, const int32_t* 
     const int n = group_member(p, gid, k);
     if (n < 0) continue;
     rows[nrows++] = p.mask + ((int64_t)bh * p.g.N + n) * p.words;
-    qrows += (uint32_t)cnt[n];
+    qrows += (uint32_t)cnt_s[n];
   }
   uint32_t kv = 0;
-  for (int w = 0; w < p.words; ++w) {
+  for (int w = lane; w < p.words; w += 64) {
     uint32_t bits = 0u;
     for (int r = 0; r < nrows; ++r) bits |= rows[r][w];
     const int rem = p.g.N - w * 32;
     if (rem < 32) bits &= (1u << rem) - 1u;
     while (bits) {
-      const int j = w * 32 + __builtin_ctz(bits);
+      kv += (uint32_t)cnt_s[w * 32 + __builtin_ctz(bits)];
       bits &= bits - 1u;
-      kv += (uint32_t)cnt[j];
     }
   }
-  const uint32_t cost = qrows * kv;
-  keys[item] = ((uint64_t)cost << 32) | (uint64_t)(~(uint32_t)item);
-  rank[item] = 0u;
-  atomicAdd((unsigned long long*)&head_cost[bh], (unsigned long long)cost);  // integer sum: any order
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) kv += (uint32_t)__shfl_xor((int)kv, off);  // integer sum: any order
+  if (lane == 0) {
+    const uint32_t cost = qrows * kv;
+    keys[item] = ((uint64_t)cost << 32) | (uint64_t)(~(uint32_t)item);
+    rank[item] = 0u;
+    atomicAdd((unsigned long long*)&head_cost[bh], (unsigned long long)cost);
+  }
 }
 
 // Heads to XCDs, longest first (single workgroup).  Head cost = sum of its
@@ -994,9 +1004,10 @@ __global__ __launch_bounds__(256) void cost_kernel(AttnParams p, const int32_t* 
 __global__ __launch_bounds__(256) void head_plan_kernel(const uint64_t* __restrict__ head_cost, int N, int BH,
                                                         bool lpt, const int32_t* __restrict__ forced,
                                                         int32_t* __restrict__ head_pos, int32_t* __restrict__ qoff) {
-  extern __shared__ uint64_t hsh[];  // [BH] head costs, then [BH] int32 order
+  extern __shared__ uint64_t hsh[];  // [BH] head costs, then [BH] int32 order, then [BH] int32 XCD of each head
   uint64_t* hcost = hsh;
   int32_t* horder = (int32_t*)(hsh + BH);
+  int32_t* hxcd = horder + BH;
   for (int x = threadIdx.x; x < BH; x += blockDim.x) hcost[x] = lpt ? head_cost[x] : 0;
   __syncthreads();
   for (int x = threadIdx.x; x < BH; x += blockDim.x) {
@@ -1021,7 +1032,7 @@ __global__ __launch_bounds__(256) void head_plan_kernel(const uint64_t* __restri
       }
       load[best] += hcost[hd];
       nh[best]++;
-      head_pos[hd] = best;  // XCD for now
+      hxcd[hd] = best;
     }
     int off = 0;
     for (int x = 0; x < NXCD; ++x) {
@@ -1032,7 +1043,7 @@ __global__ __launch_bounds__(256) void head_plan_kernel(const uint64_t* __restri
     qoff[NXCD] = off;
     for (int r = 0; r < BH; ++r) {
       const int hd = horder[r];
-      const int x = head_pos[hd];
+      const int x = hxcd[hd];
       head_pos[hd] = pos[x];
       pos[x] += N;
     }
@@ -1089,6 +1100,22 @@ static GroupShape group_shape(int vol) {
 }
 
 int attn_chunks_per_block(int vol) { return (vol + KCH - 1) / KCH; }
+
+int attn_items_per_head(const Geo& g) {
+  const GroupShape gs = group_shape(g.bt * g.bh * g.bw);
+  return ((g.nT + gs.gt - 1) / gs.gt) * ((g.nH + gs.gh - 1) / gs.gh) * ((g.nW + gs.gw - 1) / gs.gw);
+}
+
+__global__ __launch_bounds__(256) void item_cost_kernel(const uint64_t* __restrict__ keys, int64_t n,
+                                                        uint32_t* __restrict__ cost) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) cost[i] = (uint32_t)(keys[i] >> 32);
+}
+
+hipError_t launch_item_costs(const uint64_t* keys, int64_t n, uint32_t* cost, hipStream_t st) {
+  if (n > 0) hipLaunchKernelGGL(item_cost_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, keys, n, cost);
+  return hipGetLastError();
+}
 
 size_t attn_tile_bytes(int D, int64_t slots) {
   return (size_t)slots * (D == 128 ? Lds<128>::ELEMS : Lds<64>::ELEMS) * sizeof(bf16_bits);
@@ -1163,9 +1190,9 @@ hipError_t launch_sparse_plan(const AttnLaunch& a, int sched, const int32_t* hea
   else
     hipLaunchKernelGGL(tile_kernel<64>, dim3(slots), dim3(256), 0, st, (const bf16_bits*)a.k, (const bf16_bits*)a.v,
                        a.tok, a.g, a.L, a.heads, cpb, a.tiles);
-  hipLaunchKernelGGL(cost_kernel, dim3((n_items + 255) / 256), dim3(256), 0, st, prm, a.blk_cnt, a.keys, a.rank,
-                     a.qctr, a.head_cost);
-  hipLaunchKernelGGL(head_plan_kernel, dim3(1), dim3(256), (size_t)BH * 12, st, a.head_cost, per_head, BH, lpt,
+  hipLaunchKernelGGL(cost_kernel, dim3((n_items + COST_WAVES - 1) / COST_WAVES), dim3(COST_WAVES * 64),
+                     (size_t)a.g.N * sizeof(int32_t), st, prm, a.blk_cnt, a.keys, a.rank, a.qctr, a.head_cost);
+  hipLaunchKernelGGL(head_plan_kernel, dim3(1), dim3(256), (size_t)BH * 16, st, a.head_cost, per_head, BH, lpt,
                      sched == 2 ? head_xcd : nullptr, a.head_pos, a.qoff);
   if (lpt)
     hipLaunchKernelGGL(rank_kernel, dim3((n_items + 255) / 256, (n_items + 2047) / 2048), dim3(256), 0, st, a.keys,

@@ -56,6 +56,10 @@ size_t attn_tile_bytes(int D, int64_t slots);
 // Persistent workgroups of the sparse kernel for (D, block volume) on the
 // current device.
 int attn_persistent_workgroups(int D, int block_volume, int* err);
+// Work items per (b, h): query blocks, or groups of them for small blocks.
+int attn_items_per_head(const Geo& g);
+// cost[i] = keys[i] >> 32 for i < n (the item costs of a plan)
+hipError_t launch_item_costs(const uint64_t* keys, int64_t n, uint32_t* cost, hipStream_t st);
 // plan: token table, chunk images, item costs and the LPT (or naive) queues
 // in the workspace; exec: the persistent attention kernel over that plan
 // sched: 0 LPT with stealing, 1 naive, 2 per-XCD without stealing (heads by

@@ -196,6 +196,34 @@ fva_status fva_attn_plan(const void* k, const void* v, const fva_desc* desc, con
 fva_status fva_attn_exec(const void* q, void* o, const fva_desc* desc, const fva_grid* grid, const uint32_t* mask,
                          float scale, int32_t sched, uint64_t* trace, void* ws, size_t ws_bytes, void* stream);
 
+/* Number of work items of the sparse attention for this shape, or -1 for
+ * invalid arguments.  A work item is one query block; blocks of at most 64
+ * tokens are grouped 2x1x2 (t, y, x) per item and blocks of 65..128 tokens
+ * 1x1x2, so that an item still fills the kernel's 8 wavefronts.  Item id =
+ * (b*heads + h)*G + g, with G groups per (b, h) numbered in (t, y, x) order
+ * over the grid of groups.  Host only. */
+int32_t fva_attn_items(const fva_desc* desc, const fva_grid* grid);
+
+/* The schedule fva_attn_plan wrote into ws (FVAttn abstract, key module 1:
+ * runtime load balancing of head and block work; here, LPT list scheduling
+ * over the 8 XCD queues).  The cost of an item is its real query rows times
+ * the real key tokens of the union of its members' kept blocks.  Heads go,
+ * in descending summed cost (ties: lower head), to the XCD with the least
+ * assigned cost (ties: lower XCD), or where head_xcd put them; an XCD's
+ * queue holds its heads in that order, each head's items in descending cost
+ * (ties: lower item id; FVA_SCHED_NAIVE: item order, every head on queue 0).
+ * Enqueues copies on the stream:
+ *   order  out, device int32 [fva_attn_items()]: item ids in queue order;
+ *          queue x is order[qoff[x] .. qoff[x+1])
+ *   qoff   out, device int32 [9]
+ *   cost   out, device uint32 [fva_attn_items()] (nullable): each item's
+ *          cost, by item id
+ * ws must hold a plan (fva_attn_plan) for desc and grid; the exec does not
+ * change these arrays.  Errors: FVA_ERR_INVALID_ARG (null order or qoff),
+ * shape errors as for fva_attn_plan, FVA_ERR_WORKSPACE, FVA_ERR_DEVICE. */
+fva_status fva_attn_schedule(const fva_desc* desc, const fva_grid* grid, const void* ws, size_t ws_bytes,
+                             int32_t* order, int32_t* qoff, uint32_t* cost, void* stream);
+
 /* Slack-aware sparse augmentation, one-GPU form (FVAttn abstract and
  * summary, key modules 2 and 3: after load balancing, the slack left on the
  * non-critical ranks is filled with extra high-value blocks chosen from the

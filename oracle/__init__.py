@@ -321,6 +321,84 @@ def sasa(scores: np.ndarray, mask: np.ndarray, grid, block, rounds: int, margin:
             np.array(load, dtype=np.int64), np.array(added, dtype=np.int64), flags.reshape(B, heads, N))
 
 
+def default_group(block) -> tuple:
+    """Blocks per work item (t, y, x) of the sparse attention: an item fills 8
+    wavefronts of 32 query rows, so blocks of at most 64 tokens are taken
+    2 x 1 x 2 per item and blocks of 65..128 tokens 1 x 1 x 2."""
+    vol = int(block[0]) * int(block[1]) * int(block[2])
+    if vol <= 64:
+        return (2, 1, 2)
+    if vol <= 128:
+        return (1, 1, 2)
+    return (1, 1, 1)
+
+
+def work_items(grid, block, group) -> list:
+    """Member block ids of each work item of one (b, h): boxes of group =
+    (gt, gh, gw) blocks tiling the block grid from its origin (cut at the
+    grid's far edges), numbered t-major, then y, then x; members likewise."""
+    nT, nH, nW = (-(-int(d) // int(b)) for d, b in zip(grid, block))
+    gt, gh, gw = (int(x) for x in group)
+    items = []
+    for t0 in range(0, nT, gt):
+        for y0 in range(0, nH, gh):
+            for x0 in range(0, nW, gw):
+                items.append([(t * nH + y) * nW + x
+                              for t in range(t0, min(t0 + gt, nT))
+                              for y in range(y0, min(y0 + gh, nH))
+                              for x in range(x0, min(x0 + gw, nW))])
+    return items
+
+
+def lpt_schedule(grid, block, mask, B, heads, group=None, naive=False, head_xcd=None, queues=8):
+    """Work items, their costs and the queues of the persistent attention kernel.
+
+    FVAttn abstract (key module 1, runtime load balancing) and the workload
+    model of its summary: a unit of work costs the real token pairs it
+    computes.  An item = the query blocks of work_items() for one (b, h); its
+    cost = (sum of its members' real rows) x (real tokens of the union of its
+    members' kept blocks), the work its wavefronts stream.  List scheduling in
+    LPT order over the XCD queues: heads by summed item cost descending (ties:
+    lower head) each go to the queue with the least cost so far (ties: lower
+    queue), or to head_xcd[h] when given; a queue holds its heads in that
+    order, and each head's items by cost descending (ties: lower item id).
+    naive: every head on queue 0 in head order, items in id order.
+    Returns (cost int64 [B*heads*G] by item id, order int64 [B*heads*G],
+    qoff int64 [queues + 1]) with item id = (b*heads + h)*G + g.
+    """
+    if group is None:
+        group = default_group(block)
+    N = num_blocks(grid, block)
+    BH = B * heads
+    c = block_table(grid, block)[:, 6].astype(np.int64)
+    keep = mask_to_bool(np.asarray(mask, dtype=np.uint32), N).reshape(BH, N, N)
+    items = work_items(grid, block, group)
+    G = len(items)
+    cost = np.zeros(BH * G, dtype=np.int64)
+    for h in range(BH):
+        for g, members in enumerate(items):
+            union = keep[h, members].any(0)
+            cost[h * G + g] = int(c[members].sum()) * int(c[union].sum())
+    if naive:
+        order = np.arange(BH * G, dtype=np.int64)
+        qoff = np.array([0] + [BH * G] * queues, dtype=np.int64)
+        return cost, order, qoff
+    head_cost = cost.reshape(BH, G).sum(1)
+    load = [0] * queues
+    heads_of = [[] for _ in range(queues)]
+    for h in sorted(range(BH), key=lambda h: (-int(head_cost[h]), h)):
+        x = int(head_xcd[h]) if head_xcd is not None else min(range(queues), key=lambda x: (load[x], x))
+        load[x] += int(head_cost[h])
+        heads_of[x].append(h)
+    order, qoff = [], [0]
+    for x in range(queues):
+        for h in heads_of[x]:
+            ids = range(h * G, (h + 1) * G)
+            order.extend(sorted(ids, key=lambda a: (-int(cost[a]), a)))
+        qoff.append(len(order))
+    return cost, np.array(order, dtype=np.int64), np.array(qoff, dtype=np.int64)
+
+
 def dense_mask(B, heads, N) -> np.ndarray:
     words = (N + 31) // 32
     m = np.zeros((B, heads, N, words), dtype=np.uint32)
