@@ -22,8 +22,8 @@
 //     operand read from LDS feeds QT MFMAs;
 //   - chunks of 64 keys move from HBM straight into a 4-stage LDS ring, three
 //     chunks ahead of the one being computed; a chunk is K [64][D] followed by
-//     V^T [D][64], rows padded so the MFMA operand reads of 16-lane groups hit
-//     distinct banks;
+//     V^T [D][64], both in 16-byte pieces stored piece-major, so the MFMA
+//     operand reads of 16-lane groups hit distinct banks without padding;
 //   - S^T = K Q^T gives each lane one query column, so the softmax row
 //     statistics need one cross-half lane swap per 32 keys, and the bf16
 //     probabilities feed O^T += V^T P^T from registers;

@@ -131,3 +131,25 @@ def test_trace_imbalance_host_helper():
                  dtype=np.uint64)
     b, f, n = fva.trace_imbalance(t)
     assert n == 2 and abs(b - 1.0) < 1e-12 and abs(f - 20 / 15) < 1e-12
+
+
+def test_attn_items_and_schedule_validation():
+    lib = fva.load()
+    # one item per block for 256-token blocks; 2x1x2 groups of 64-token blocks; 1x1x2 of 128-token blocks
+    assert fva.attn_items((1, 27280, 40, 128), (31, 22, 40), (4, 8, 8)) == 40 * 120
+    assert fva.attn_items((1, 393216, 5, 128), (96, 64, 64), (4, 4, 4)) == 5 * 12 * 16 * 8
+    assert fva.attn_items((2, 3840, 3, 64), (6, 16, 40), (2, 8, 8)) == 2 * 3 * 3 * 2 * 3
+    assert fva.attn_items((1, 7 * 6 * 5, 2, 64), (7, 6, 5), (2, 2, 2)) == 2 * 2 * 3 * 2
+    bad = fva.make_desc(1, 27281, 40, 128)
+    assert lib.fva_attn_items(ctypes.byref(bad), ctypes.byref(fva.make_grid((31, 22, 40), (4, 8, 8)))) == -1
+    desc, grid = fva.make_desc(1, 27280, 40, 128), fva.make_grid((31, 22, 40), (4, 8, 8))
+    need = lib.fva_attn_workspace_bytes(ctypes.byref(desc), ctypes.byref(grid))
+
+    def call(ws=FAKE, ws_bytes=need, order=FAKE, qoff=FAKE, desc=desc):
+        return lib.fva_attn_schedule(ctypes.byref(desc), ctypes.byref(grid), ws, ws_bytes, order, qoff, None, None)
+
+    assert call(order=None) == 1 and "must not be null" in _err()
+    assert call(qoff=None) == 1
+    assert call(ws_bytes=need - 1) == 5 and "needed" in _err()
+    assert call(ws=None) == 5
+    assert call(desc=bad) == 2
