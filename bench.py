@@ -50,8 +50,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print("bench.py measures one GPU: the path has no multi-GPU part in this build "
-              "(it would shard by head; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (across GPUs it would shard the "
+              "heads). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -24,7 +24,7 @@
 // Everything is fp64; bf16 inputs are widened exactly.  Plain loops, no
 // blocking or fusion beyond these definitions.
 //
-// Readings where the pages are silent (each also listed in the design notes):
+// Readings where the pages are silent:
 //   - pooling is the mean over real tokens (divide by the real count);
 //   - blocks are numbered row-major over (block-t, block-h, block-w), and the
 //     tokens of a block are visited row-major over (t, y, x);
