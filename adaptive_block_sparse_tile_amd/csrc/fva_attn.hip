@@ -996,18 +996,24 @@ __global__ __launch_bounds__(COST_WAVES * 64) void cost_kernel(AttnParams p, con
 }
 
 // Heads to XCDs, longest first (single workgroup).  Head cost = sum of its
-// items' costs (summed by cost_kernel); heads are taken in descending cost (ties: lower head) and
-// each goes to the XCD with the least assigned cost (ties: lower XCD).
-// Writes each head's first position in the order array and the queue
-// segments qoff[0..NXCD].  NAIVE puts every head on queue 0 in head order.
-// forced (nullable): each head's XCD, given by the caller instead of chosen.
+// items' costs (summed by cost_kernel); heads are taken in descending cost
+// (ties: lower head) and each goes to the XCD with the least assigned cost
+// (ties: lower XCD).  Writes each head's first position in the order array
+// and the queue segments qoff[0..NXCD].  NAIVE puts every head on queue 0 in
+// head order.  forced (nullable): each head's XCD, given by the caller
+// instead of chosen.  The assignment itself is one thread's sequential walk
+// (each choice depends on the loads before it); the ranking before it and the
+// positions after it are spread over the workgroup.
 __global__ __launch_bounds__(256) void head_plan_kernel(const uint64_t* __restrict__ head_cost, int N, int BH,
                                                         bool lpt, const int32_t* __restrict__ forced,
                                                         int32_t* __restrict__ head_pos, int32_t* __restrict__ qoff) {
-  extern __shared__ uint64_t hsh[];  // [BH] head costs, then [BH] int32 order, then [BH] int32 XCD of each head
+  // [BH] head costs, then [BH] int32 head of each rank, then [BH] int32 place
+  // of each rank (XCD | slot among the XCD's heads << 3)
+  extern __shared__ uint64_t hsh[];
+  __shared__ int32_t qoff_s[NXCD + 1];
   uint64_t* hcost = hsh;
   int32_t* horder = (int32_t*)(hsh + BH);
-  int32_t* hxcd = horder + BH;
+  int32_t* place = horder + BH;
   for (int x = threadIdx.x; x < BH; x += blockDim.x) hcost[x] = lpt ? head_cost[x] : 0;
   __syncthreads();
   for (int x = threadIdx.x; x < BH; x += blockDim.x) {
@@ -1015,39 +1021,44 @@ __global__ __launch_bounds__(256) void head_plan_kernel(const uint64_t* __restri
     for (int y = 0; y < BH; ++y)
       if (hcost[y] > hcost[x] || (hcost[y] == hcost[x] && y < x)) ++r;
     horder[r] = x;
+    place[r] = forced ? min(max(forced[x], 0), NXCD - 1) : 0;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
+    // per-XCD tallies in registers (every index is a constant after unrolling)
     uint64_t load[NXCD];
-    int nh[NXCD], pos[NXCD];
+    int nh[NXCD];
+#pragma unroll
     for (int x = 0; x < NXCD; ++x) load[x] = 0, nh[x] = 0;
+#pragma unroll 4
     for (int r = 0; r < BH; ++r) {
-      const int hd = horder[r];
-      int best = 0;
-      if (forced) {
-        best = min(max(forced[hd], 0), NXCD - 1);
-      } else if (lpt) {
+      const uint64_t c = hcost[horder[r]];
+      int best = place[r];
+      if (!forced && lpt) {
+        uint64_t lb = load[0];
+        best = 0;
+#pragma unroll
         for (int x = 1; x < NXCD; ++x)
-          if (load[x] < load[best]) best = x;
+          if (load[x] < lb) best = x, lb = load[x];
       }
-      load[best] += hcost[hd];
-      nh[best]++;
-      hxcd[hd] = best;
+      int slot = 0;
+#pragma unroll
+      for (int x = 0; x < NXCD; ++x)
+        if (x == best) slot = nh[x], load[x] += c, nh[x]++;
+      place[r] = best | (slot << 3);
     }
     int off = 0;
+#pragma unroll
     for (int x = 0; x < NXCD; ++x) {
       qoff[x] = off;
-      pos[x] = off;
+      qoff_s[x] = off;
       off += nh[x] * N;
     }
     qoff[NXCD] = off;
-    for (int r = 0; r < BH; ++r) {
-      const int hd = horder[r];
-      const int x = hxcd[hd];
-      head_pos[hd] = pos[x];
-      pos[x] += N;
-    }
   }
+  __syncthreads();
+  for (int r = threadIdx.x; r < BH; r += blockDim.x)
+    head_pos[horder[r]] = qoff_s[place[r] & 7] + (place[r] >> 3) * N;
 }
 
 // rank[a] += #{b in this tile of a's head : key[b] > key[a]}  (keys distinct)
