@@ -393,10 +393,23 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
         const int rem = p.g.N - wi * 32;
         umask[wi] = rem < 32 ? u & ((1u << rem) - 1u) : u;
       }
-      const int n_mine = group_member(p, gid, wave / p.wpb);
-      row0 = 32 * QT * (wave % p.wpb);
+      // The member block this wavefront serves.  Wavefronts w and w + 4
+      // share a SIMD, so with 2 wavefronts per member the members pair up on
+      // SIMDs 0-1 (wavefronts 0, 1, 4, 5) and 2-3 (2, 3, 6, 7).  Blocks that
+      // are neighbours in t or in x keep many of the same key blocks, so in
+      // a 2x1x2 group the diagonal members (t0, x0) + (t1, x1) share one SIMD
+      // pair and (t0, x1) + (t1, x0) the other: a chunk that only two
+      // neighbours keep then runs on all four SIMDs.
+      int msel = wave / p.wpb, tsel = wave % p.wpb;
+      if (p.wpb == 2) {
+        const int pair = (wave >> 1) & 1, slot = wave >> 2;
+        msel = pair == 0 ? (slot ? 3 : 0) : (slot ? 2 : 1);
+        tsel = wave & 1;
+      }
+      const int n_mine = group_member(p, gid, msel);
+      row0 = 32 * QT * tsel;
       if (n_mine >= 0) {
-        mine = wave / p.wpb;
+        mine = msel;
         const Box bx = block_box(p.g, n_mine);
         qbase = bx.start;
         qcount = bx.count;
