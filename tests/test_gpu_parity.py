@@ -138,6 +138,24 @@ def test_sparse_attn_parity(name, n_sample):
     assert mx <= MAX_ABS and mean <= MEAN_ABS
 
 
+def test_max_blocks():
+    """The largest supported grid: 8192 blocks of 64 tokens (256 mask words
+    per row, the router's selection kernel with 256 lanes, the attention
+    kernel's largest LDS mask); masks bit-exact, sampled items in tolerance."""
+    wl = _custom("max_blocks_8192", 1, 64, (128, 64, 64), (4, 4, 4), 0.6, 4)
+    assert oracle.num_blocks(wl.grid, wl.block) == 8192
+    (q, k, v), (qd, kd, vd) = _inputs(wl)
+    mask = _check_route(wl, q, k, qd, kd)
+    mask_g = torch.from_numpy(mask.view(np.int32)).cuda()
+    o = fva.sparse_attn(qd, kd, vd, wl.grid, wl.block, mask_g)
+    torch.cuda.synchronize()
+    items = _sample_items(wl, mask, 24)
+    ref = oracle.attn(q, k, v, wl.grid, wl.block, mask, 1.0 / math.sqrt(wl.head_dim), items=items)
+    mx, mean = _attn_errors(wl, _bf16_host(o), ref, items)
+    print("\n[%s] %d items: max-abs %.3e mean-abs %.3e" % (wl.name, len(items), mx, mean), flush=True)
+    assert mx <= MAX_ABS and mean <= MEAN_ABS
+
+
 def test_dense_ref_parity_tiny_and_all_kept_sparse():
     wl = fvgen.WORKLOADS["tiny"]
     (q, k, v), (qd, kd, vd) = _inputs(wl)
