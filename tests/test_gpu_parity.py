@@ -156,6 +156,38 @@ def test_max_blocks():
     assert mx <= MAX_ABS and mean <= MEAN_ABS
 
 
+@pytest.mark.parametrize("grid,block", [((9, 17, 23), (4, 8, 8)), ((8, 12, 12), (4, 4, 4))],
+                         ids=["single_blocks", "grouped_blocks"])
+def test_empty_rows_written_as_zero(grid, block):
+    """A mask row with no bit set (the caller's error) leaves its query
+    block's O rows at zero, in single-block and in grouped work items; the
+    other rows are unaffected."""
+    wl = _custom("empty_rows_%d" % (block[0] * block[1] * block[2]), 2, 64, grid, block, 0.8, 2)
+    (q, k, v), (qd, kd, vd) = _inputs(wl)
+    N = oracle.num_blocks(grid, block)
+    rng = np.random.default_rng(4)
+    keep = rng.random((wl.heads, N, N)) < 0.3
+    keep[:, np.arange(N), np.arange(N)] = True
+    empty = rng.random((wl.heads, N)) < 0.2
+    keep[empty] = False
+    words = (N + 31) // 32
+    padded = np.zeros((wl.heads, N, words * 32), dtype=np.uint64)
+    padded[..., :N] = keep
+    mask = (padded.reshape(wl.heads, N, words, 32) << np.arange(32, dtype=np.uint64)).sum(-1).astype(np.uint32)
+    mask = mask.reshape(1, wl.heads, N, words)
+    o = _bf16_host(fva.sparse_attn(qd, kd, vd, grid, block, torch.from_numpy(mask.view(np.int32)).cuda()))
+    tb = oracle.token_block(grid, block)
+    for h in range(wl.heads):
+        for i in np.nonzero(empty[h])[0]:
+            assert (o[0, tb == i, h, :] == 0).all()
+    items = np.array([h * N + i for h in range(wl.heads) for i in range(N) if not empty[h, i]])
+    ref = oracle.attn(q, k, v, grid, block, mask, 1.0 / math.sqrt(wl.head_dim), items=items)
+    mx, mean = _attn_errors(wl, o, ref, items)
+    print("\n[empty rows %s] %d empty, %d items: max-abs %.3e mean-abs %.3e" % (
+        block, int(empty.sum()), len(items), mx, mean), flush=True)
+    assert mx <= MAX_ABS and mean <= MEAN_ABS
+
+
 def test_dense_ref_parity_tiny_and_all_kept_sparse():
     wl = fvgen.WORKLOADS["tiny"]
     (q, k, v), (qd, kd, vd) = _inputs(wl)
