@@ -8,7 +8,7 @@
 // What it computes, step by step, in the order the method states it:
 //   1. video-aware 3D block organisation of the (T,H,W) token grid
 //      [vLLM-Omni FastVideo VSA guide, sections 1, 3 and 6;
-//       FVAttn abstract: "video-aware block organization"]
+//       FVAttn abstract: video-aware organisation of the blocks]
 //   2. block-mean pooling of Q and K over the real tokens of each block
 //   3. pooled block scores scaled by 1/sqrt(D)          [VSA guide, section 5]
 //   4. row softmax over all N key blocks
