@@ -80,6 +80,7 @@ struct AttnParams {
   int words, cpb;          // mask words per row; chunk slots per block
   const uint32_t* mask;
   const int32_t* tok;      // block-ordered token ids (sparse)
+  const int32_t* cnt;      // real tokens per block (sparse)
   const bf16_bits* tiles;  // chunk images (sparse)
   const int32_t* order;    // item order (sparse)
   const int32_t* qoff;     // [NXCD + 1] queue segments in order (sparse)
@@ -117,6 +118,7 @@ struct Chunk {
 // workgroup holds the same state.
 struct KvIter {
   const uint32_t* umask;  // LDS
+  const uint16_t* cnt;    // LDS: real tokens per block
   int w, words, c, nch, count, slot0, blk;
   uint32_t bits;
   bool done;
@@ -133,7 +135,7 @@ struct KvIter {
     }
     blk = w * 32 + __builtin_ctz(bits);
     bits &= bits - 1u;
-    count = block_box(g, blk).count;
+    count = cnt[blk];
     nch = (count + KCH - 1) / KCH;
     slot0 = (bh * g.N + blk) * cpb;
     c = 0;
@@ -295,6 +297,10 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
   __shared__ uint32_t umask[DENSE ? 1 : MAX_WORDS];
   __shared__ uint32_t gmask[GRP ? 4 : 1][GRP ? MAX_WORDS : 1];
   __shared__ int item_s;
+  // real tokens of every block, read by the chunk walk at each block change
+  // (a table lookup instead of the three integer divisions of the block's
+  // geometry, which cost the walk some 80 scalar instructions per block)
+  __shared__ uint16_t cnt_s[DENSE ? 1 : MAX_WORDS * 32];
   static_assert(STAGES == 4, "four ring stages");
   auto stage = [&](int sidx) -> bf16_bits* {
     return sidx == 0 ? ring0 : (sidx == 1 ? ring1 : (sidx == 2 ? ring2 : ring3));
@@ -306,6 +312,8 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
   const int lr = lane & 31, hi = lane >> 5;
   const float cl2 = p.scale_log2;
 
+  if (!DENSE)  // ordered before any read by the barrier after the first item fetch
+    for (int j = tid; j < p.g.N; j += THREADS) cnt_s[j] = (uint16_t)p.cnt[j];
   uint64_t t_first = 0, t_last = 0, busy = 0, nitems = 0;
   int my_xcd = 0;
   if (!DENSE) my_xcd = (int)(__builtin_amdgcn_s_getreg((15 << 11) | 20) & 7);  // HW_REG_XCC_ID
@@ -344,6 +352,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
     bool merge = false;  // some tile of the item is split over two wavefronts (uniform)
     KvIter it;
     it.umask = umask;
+    it.cnt = cnt_s;
     if (DENSE) {
       const int tile = item % p.q_tiles;
       bh = item / p.q_tiles;
@@ -1183,6 +1192,7 @@ static AttnParams sparse_params(const AttnLaunch& a) {
   prm.cpb = attn_chunks_per_block(vol);
   prm.mask = a.mask;
   prm.tok = a.tok;
+  prm.cnt = a.blk_cnt;
   prm.tiles = a.tiles;
   prm.order = a.order;
   prm.qoff = a.qoff;
