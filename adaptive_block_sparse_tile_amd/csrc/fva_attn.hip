@@ -191,35 +191,47 @@ struct KvIter {
 // every LDS read of a stage after the wait for the loads into it.
 // Every wavefront issues the same number (PER_WAVE) of instructions per
 // chunk, so that a wait for "all but the newest chunk" is one vmcnt
-// immediate: a wavefront with fewer pieces repeats its last one (the same
-// bytes to the same place).
+// immediate.  Wavefront w loads the PER_WAVE consecutive pieces from piece
+// PER_WAVE * w on: one scalar base for the chunk, the wavefront's offset in
+// a VGPR fixed for the kernel, and the piece in the instruction's immediate
+// offset, which moves the global and the LDS address alike (M0 holds the
+// wavefront's first LDS piece).  So a chunk costs a few scalar instructions
+// besides the loads.
 template <int D, int WAVES>
 struct ChunkDma {
   static constexpr int BYTES = Lds<D>::ELEMS * 2;
   static constexpr int PIECES = BYTES / 1024;
-  static constexpr int PER_WAVE = (PIECES + WAVES - 1) / WAVES;
-  static_assert(BYTES % 1024 == 0, "a chunk image is a whole number of 1 KB pieces");
-  static_assert(PIECES >= WAVES && PER_WAVE <= 15, "every wavefront has a piece; vmcnt range");
-  // Addresses: a scalar base (the chunk's image plus the piece's offset past
-  // this wavefront's first piece) and a per-lane vector offset; M0 likewise.
-  // The wavefront's own offset passes through an empty asm statement so that
-  // the compiler forms the per-piece scalars here, at each issue, instead of
-  // keeping all of them (4 stages x PER_WAVE) live across the chunk loop.
-  __device__ static void issue(const bf16_bits* tiles, int slot, bf16_bits* lds, int wave, int lane) {
-    uint32_t w1k = (uint32_t)wave * 1024u;
-    asm volatile("" : "+s"(w1k));
+  static constexpr int PER_WAVE = PIECES / WAVES;
+  static_assert(BYTES % 1024 == 0 && PIECES == PER_WAVE * WAVES, "whole 1 KB pieces, the same count per wavefront");
+  static_assert(PER_WAVE == 2 || PER_WAVE == 4, "pieces per wavefront: immediate offsets below 4 KB");
+  // voff: this lane's byte offset in the chunk image (wavefront's first piece + 16 * lane)
+  __device__ static uint32_t lane_offset(int wave, int lane) {
+    return (uint32_t)wave * (PER_WAVE * 1024u) + (uint32_t)lane * 16u;
+  }
+  __device__ static void issue(const bf16_bits* tiles, int slot, bf16_bits* lds, int wave, uint32_t voff) {
     // (the slot is the same in every lane; say so, so that it stays scalar)
     const uint32_t us = (uint32_t)__builtin_amdgcn_readfirstlane(slot);
     const uint64_t gbase = (uint64_t)(uintptr_t)tiles + (uint64_t)us * (uint64_t)BYTES;
-    const uint32_t lbase = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)((char*)lds) + w1k;
-    const uint32_t voff = w1k + (uint32_t)lane * 16u;
-#pragma unroll
-    for (int u = 0; u < PER_WAVE; ++u) {
-      uint32_t joff = (uint32_t)(u * WAVES * 1024);
-      if (wave + u * WAVES >= PIECES) joff -= WAVES * 1024u;  // repeat the previous piece
-      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" : : "s"(lbase + joff), "v"(voff),
-                   "s"(gbase + joff) : "memory", "m0");
-    }
+    const uint32_t lbase = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)((char*)lds) +
+                           (uint32_t)wave * (PER_WAVE * 1024u);
+    if constexpr (PER_WAVE == 4)
+      asm volatile(
+          "s_mov_b32 m0, %0\n\t"
+          "global_load_lds_dwordx4 %1, %2\n\t"
+          "global_load_lds_dwordx4 %1, %2 offset:1024\n\t"
+          "global_load_lds_dwordx4 %1, %2 offset:2048\n\t"
+          "global_load_lds_dwordx4 %1, %2 offset:3072"
+          :
+          : "s"(lbase), "v"(voff), "s"(gbase)
+          : "memory", "m0");
+    else
+      asm volatile(
+          "s_mov_b32 m0, %0\n\t"
+          "global_load_lds_dwordx4 %1, %2\n\t"
+          "global_load_lds_dwordx4 %1, %2 offset:1024"
+          :
+          : "s"(lbase), "v"(voff), "s"(gbase)
+          : "memory", "m0");
   }
 };
 
@@ -495,12 +507,13 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
     // chunks arrive by direct loads three chunks ahead of the one being computed
     constexpr int LOOK = 3;
     using Dma = ChunkDma<D, WAVES>;
+    const uint32_t dma_voff = Dma::lane_offset(wave, lane);
     int ready = 0, v0 = 0, v1 = 0, v2 = 0;
 #pragma unroll
     for (int sidx = 0; sidx < LOOK; ++sidx) {
       if (it.done) break;
       const Chunk ck = it.template chunk<DENSE>();
-      Dma::issue(p.tiles, ck.slot, stage(sidx), wave, lane);
+      Dma::issue(p.tiles, ck.slot, stage(sidx), wave, dma_voff);
       const int sv = seen(ck);
       if (sidx == 0) v0 = sv;
       else if (sidx == 1) v1 = sv;
@@ -760,7 +773,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
       Chunk ckl = {0, 0, -1};
       if (more) {
         ckl = it.template chunk<DENSE>();
-        Dma::issue(p.tiles, ckl.slot, stage(sl), wave, lane);
+        Dma::issue(p.tiles, ckl.slot, stage(sl), wave, dma_voff);
       }
       const bf16_bits* S0 = stage(s0);
       const bf16_bits* S1 = stage(s1);
