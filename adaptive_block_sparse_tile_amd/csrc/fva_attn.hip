@@ -327,11 +327,71 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
   if (!DENSE)  // ordered before any read by the barrier after the first item fetch
     for (int j = tid; j < p.g.N; j += THREADS) cnt_s[j] = (uint16_t)p.cnt[j];
   uint64_t t_first = 0, t_last = 0, busy = 0, nitems = 0;
-  int my_xcd = 0;
-  if (!DENSE) my_xcd = (int)(__builtin_amdgcn_s_getreg((15 << 11) | 20) & 7);  // HW_REG_XCC_ID
+
+  // Work items come from the XCD queues (thread 0 pops them).  The next item
+  // is popped when the current one's chunk loop ends and its mask rows are
+  // staged in LDS while the current item's output is written, so an item
+  // starts with a single round trip to memory (Q and its first chunks
+  // together).  (Popping it earlier, while the current item runs, reserves
+  // it too soon: the kernel's tail grew and wan14b ran 1.7% slower.)
+  // take a slot of this XCD's queue (thread 0; its queue's segment is read
+  // from memory each time, so that nothing of it stays live in registers
+  // across the chunk loop)
+  auto take_own_slot = [&]() -> uint32_t {
+    const int x = (int)(__builtin_amdgcn_s_getreg((15 << 11) | 20) & 7);  // HW_REG_XCC_ID
+    const int n = p.qoff[x + 1] - p.qoff[x];
+    return n > 0 ? atomicAdd(&p.qctr[x], 1u) : ~0u;
+  };
+  // the item of a taken slot, or (stealing) one from another queue, or -1
+  auto item_of_slot = [&](uint32_t s) -> int {
+    const int my_xcd = (int)(__builtin_amdgcn_s_getreg((15 << 11) | 20) & 7);
+    const int n0 = p.qoff[my_xcd + 1] - p.qoff[my_xcd];
+    if (s < (uint32_t)n0) return p.order[p.qoff[my_xcd] + s];
+    for (int t = 1; t < (p.steal ? NXCD : 1); ++t) {
+      const int x = (my_xcd + t) % NXCD;
+      const int n = p.qoff[x + 1] - p.qoff[x];
+      if (n <= 0 || __atomic_load_n(&p.qctr[x], __ATOMIC_RELAXED) >= (uint32_t)n) continue;
+      const uint32_t u = atomicAdd(&p.qctr[x], 1u);
+      if (u < (uint32_t)n) return p.order[p.qoff[x] + u];
+    }
+    return -1;
+  };
+  // the item's mask rows in LDS: the union of its members' rows (bits >= N
+  // cleared) and, for groups, each member's own row
+  auto stage_mask = [&](int item) {
+    if (!GRP) {
+      const int n = item % p.g.N;
+      const uint32_t* row = p.mask + ((int64_t)(item / p.g.N) * p.g.N + n) * p.words;
+      for (int wi = tid; wi < p.words; wi += THREADS) {
+        const int rem = p.g.N - wi * 32;
+        umask[wi] = rem < 32 ? row[wi] & ((1u << rem) - 1u) : row[wi];
+      }
+    } else {
+      const int gid = item % p.n_groups;
+      const int bhg = item / p.n_groups;
+      const int ng = p.gt * p.gh * p.gw;
+      for (int wi = tid; wi < p.words; wi += THREADS) {
+        uint32_t u = 0u;
+        for (int k = 0; k < 4; ++k) {
+          const int n = k < ng ? group_member(p, gid, k) : -1;
+          const uint32_t x = n >= 0 ? p.mask[((int64_t)bhg * p.g.N + n) * p.words + wi] : 0u;
+          gmask[k][wi] = x;
+          u |= x;
+        }
+        const int rem = p.g.N - wi * 32;
+        umask[wi] = rem < 32 ? u & ((1u << rem) - 1u) : u;
+      }
+    }
+  };
+  if (!DENSE) {
+    if (tid == 0) item_s = item_of_slot(take_own_slot());
+    __syncthreads();
+    if (item_s >= 0) stage_mask(item_s);
+    __syncthreads();
+  }
 
   for (int iter = 0;; ++iter) {
-    // ---- fetch a work item
+    // ---- the work item (its mask rows are already in LDS)
     int item;
     if (DENSE) {
       if (iter > 0) break;
@@ -339,18 +399,6 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
       item = (blockIdx.x % NXCD) * per + blockIdx.x / NXCD;
       if (item >= p.n_items) break;
     } else {
-      if (tid == 0) {
-        int got = -1;
-        for (int t = 0; t < (p.steal ? NXCD : 1) && got < 0; ++t) {
-          const int x = (my_xcd + t) % NXCD;
-          const int n = p.qoff[x + 1] - p.qoff[x];
-          if (n <= 0 || __atomic_load_n(&p.qctr[x], __ATOMIC_RELAXED) >= (uint32_t)n) continue;
-          const uint32_t s = atomicAdd(&p.qctr[x], 1u);
-          if (s < (uint32_t)n) got = p.order[p.qoff[x] + s];
-        }
-        item_s = got;
-      }
-      __syncthreads();
       item = item_s;
       if (item < 0) break;
     }
@@ -374,11 +422,6 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
     } else if (!GRP) {
       const int n = item % p.g.N;
       bh = item / p.g.N;
-      const uint32_t* row = p.mask + ((int64_t)bh * p.g.N + n) * p.words;
-      for (int wi = tid; wi < p.words; wi += THREADS) {
-        const int rem = p.g.N - wi * 32;
-        umask[wi] = rem < 32 ? row[wi] & ((1u << rem) - 1u) : row[wi];
-      }
       const Box bx = block_box(p.g, n);
       qbase = bx.start;
       qcount = bx.count;
@@ -402,18 +445,6 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
     } else {
       const int gid = item % p.n_groups;
       bh = item / p.n_groups;
-      const int ng = p.gt * p.gh * p.gw;
-      for (int wi = tid; wi < p.words; wi += THREADS) {
-        uint32_t u = 0u;
-        for (int k = 0; k < 4; ++k) {
-          const int n = k < ng ? group_member(p, gid, k) : -1;
-          const uint32_t x = n >= 0 ? p.mask[((int64_t)bh * p.g.N + n) * p.words + wi] : 0u;
-          gmask[k][wi] = x;
-          u |= x;
-        }
-        const int rem = p.g.N - wi * 32;
-        umask[wi] = rem < 32 ? u & ((1u << rem) - 1u) : u;
-      }
       // The member block this wavefront serves.  Wavefronts w and w + 4
       // share a SIMD, so with 2 wavefronts per member the members pair up on
       // SIMDs 0-1 (wavefronts 0, 1, 4, 5) and 2-3 (2, 3, 6, 7).  Blocks that
@@ -469,7 +500,6 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
         qf[qt][s] = __builtin_bit_cast(bf16x8, x);
       }
     }
-    wait_vmem<0>();  // Q is in before any chunk load is issued
 
     // Softmax state of each row (log2 units).  m_run: the running max the
     // O^T accumulators and the row sum are scaled by.  moff: the offset the
@@ -495,7 +525,6 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
     // ---- pipeline: `it` is the next chunk to load; the ring holds `ready`
     //      chunks (loaded or in flight) starting with the one being
     //      computed, with real key counts v0, v1, v2 as this wavefront sees them
-    if (!DENSE) __syncthreads();  // the item's mask is in LDS
     it.template first<DENSE>(p.g, p.words, p.L, bh, p.cpb);
     // real keys of the chunks in the ring as this wavefront sees them: a key
     // block its own query block did not keep counts as 0 real keys
@@ -521,9 +550,8 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
       ++ready;
       it.template advance<DENSE>(p.g, bh, p.cpb);
     }
-    // chunks 0 and 1 must be in; chunk 2 may still be in flight
-    if (ready == LOOK) wait_vmem<Dma::PER_WAVE>();
-    else wait_vmem<0>();
+    // Q and the first chunks were issued together: wait for all of them
+    wait_vmem<0>();
     barrier_lds();
 
     // The pipeline runs on 32-key halves of the chunks (the online softmax
@@ -823,6 +851,16 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
       if (!chunk_step(3)) break;
     }
 
+    // ---- the next item: pop it, publish its id and stage its mask rows
+    //      (every wavefront is done with this item's masks) while this
+    //      item's output is written; the barrier that ends the item orders
+    //      both before the next item's first read
+    if (!DENSE) {
+      if (tid == 0) item_s = item_of_slot(take_own_slot());
+      __syncthreads();
+      if (item_s >= 0) stage_mask(item_s);
+    }
+
     // ---- split tiles: the key-half-1 wavefront hands its running max, partial
     //      row sums and O^T accumulators to the key-half-0 wavefront through
     //      LDS (the ring is idle: every chunk load has landed), which rescales
@@ -891,7 +929,10 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
     t_last = t_end;
     busy += t_end - t_start;
     ++nitems;
-    __syncthreads();
+    // the next item depends on this one only through LDS (its mask rows and
+    // id, the ring); the output stores stay in flight and are waited for
+    // with the next item's first loads
+    barrier_lds();
   }
 
   if (p.trace && tid == 0) {
