@@ -272,6 +272,10 @@ def _custom(name, heads, D, grid, block, top_p, k_floor, batch=1, modes=8):
     # N = 576 > 512 key blocks: the bisection router
     _custom("select_n576", 2, 64, (12, 16, 24), (2, 2, 2), 0.7, 3),
     _custom("select_topk", 1, 128, (12, 16, 24), (2, 2, 2), 0.0, 7),
+    # grouped 64-token blocks with B = 2 (items of both batches in one queue) and D = 64
+    _custom("batch2_grouped", 2, 64, (7, 10, 9), (4, 4, 4), 0.8, 2, batch=2),
+    # 128-token blocks with D = 64, ragged in every dimension
+    _custom("vol128_d64", 3, 64, (5, 11, 13), (2, 8, 8), 0.85, 2),
 ], ids=lambda w: w.name)
 def test_edge_cases(wl):
     (q, k, v), (qd, kd, vd) = _inputs(wl)
