@@ -123,15 +123,13 @@ struct KvIter {
   uint32_t bits;
   bool done;
 
-  __device__ uint32_t load_word(const Geo&, int wi) const { return umask[wi]; }
-
   __device__ void next_block(const Geo& g, int bh, int cpb) {
     while (bits == 0u) {
       if (++w >= words) {
         done = true;
         return;
       }
-      bits = load_word(g, w);
+      bits = umask[w];
     }
     blk = w * 32 + __builtin_ctz(bits);
     bits &= bits - 1u;
@@ -154,7 +152,7 @@ struct KvIter {
     }
     words = nwords;
     w = 0;
-    bits = load_word(g, 0);
+    bits = umask[0];
     next_block(g, bh, cpb);
   }
 
@@ -171,7 +169,6 @@ struct KvIter {
     next_block(g, bh, cpb);
   }
 
-  template <bool DENSE>
   __device__ Chunk chunk() const {
     Chunk ck;
     ck.slot = slot0 + c;
@@ -541,7 +538,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
 #pragma unroll
     for (int sidx = 0; sidx < LOOK; ++sidx) {
       if (it.done) break;
-      const Chunk ck = it.template chunk<DENSE>();
+      const Chunk ck = it.chunk();
       Dma::issue(p.tiles, ck.slot, stage(sidx), wave, dma_voff);
       const int sv = seen(ck);
       if (sidx == 0) v0 = sv;
@@ -800,7 +797,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
       const bool more = !it.done;
       Chunk ckl = {0, 0, -1};
       if (more) {
-        ckl = it.template chunk<DENSE>();
+        ckl = it.chunk();
         Dma::issue(p.tiles, ckl.slot, stage(sl), wave, dma_voff);
       }
       const bf16_bits* S0 = stage(s0);
@@ -1175,8 +1172,6 @@ __global__ __launch_bounds__(256) void scatter_kernel(const uint32_t* __restrict
 // A group walks the union of its blocks' kept key blocks; each wavefront
 // masks the key blocks its own query block did not keep.
 constexpr int WAVES = 8;
-int attn_waves_for_block(int) { return WAVES; }
-
 struct GroupShape {
   int gt, gh, gw, wpb;
 };

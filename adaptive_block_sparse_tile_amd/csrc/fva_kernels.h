@@ -47,8 +47,6 @@ struct AttnLaunch {
   uint32_t* qctr;      // [8] queue pop counters
 };
 
-// Wavefronts per work item (8 for every block volume; small blocks are grouped).
-int attn_waves_for_block(int block_volume);
 // 64-key chunk slots reserved per block.
 int attn_chunks_per_block(int block_volume);
 // Bytes of the chunk images for a number of slots.
