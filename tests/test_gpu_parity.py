@@ -252,6 +252,37 @@ def test_nonfinite_rows_repaired_dense():
     assert cnt_g.cpu().numpy()[0, 0, 0] == 8
 
 
+
+def test_select_router_nonfinite_and_all_kept():
+    # N = 576 > 512: the bisection router.  A NaN in one query token of head 1
+    # makes that query block's row non-finite; a +inf in one key token of
+    # head 0 makes every row of head 0 non-finite.  Both are repaired to all
+    # blocks with status bit 0 set; top_p = 1 keeps every block of every row.
+    wl = _custom("select_nonfinite", 2, 64, (12, 16, 24), (2, 2, 2), 0.7, 3)
+    N = oracle.num_blocks(wl.grid, wl.block)
+    assert N == 576
+    q0, k0, _ = fvgen.generate_qkv(wl)
+    q, k = q0.copy(), k0.copy()
+    tb = oracle.token_block(wl.grid, wl.block)
+    q[0, int(np.nonzero(tb == 100)[0][0]), 1, 5] = 0x7FC0   # NaN (bf16 bits)
+    k[0, int(np.nonzero(tb == 300)[0][2]), 0, 9] = 0x7F80   # +inf (bf16 bits)
+    qd, kd = _dev(q), _dev(k)
+    (mg, cg, sg), (mo, co, flags, so) = _route_both(wl, q, k, qd, kd)
+    print("\n[select_nonfinite] status gpu %d oracle %d, flagged rows %d" % (sg, so, int((flags != 0).sum())),
+          flush=True)
+    assert sg == so == 1
+    bad = (flags & oracle.FLAG_NONFINITE) != 0
+    assert bad[0, 0].all() and bad[0, 1, 100] and bad[0, 1].sum() == 1
+    assert (cg[bad] == N).all() and np.array_equal(mg[bad], mo[bad])
+    ok = flags == 0
+    assert ok[0, 1].sum() > 0.9 * N
+    assert not ((mg != mo).any(-1) & ok).any()
+    assert np.array_equal(cg[ok], co[ok])
+    mask_all, cnt_all, st_all = fva.route(_dev(q0), _dev(k0), wl.grid, wl.block, 1.0, 3)
+    m_all = _u32(mask_all)
+    assert int(st_all.cpu()[0]) == 0 and (cnt_all.cpu().numpy() == N).all()
+    assert np.array_equal(m_all, oracle.dense_mask(1, wl.heads, N))
+
 def _custom(name, heads, D, grid, block, top_p, k_floor, batch=1, modes=8):
     return fvgen.Workload(name, 77, heads, D, grid, block, modes, "list", tuple([0.7, 2.5, 5.0][:heads]) if heads <= 3
                           else tuple(np.linspace(0.5, 5, heads)), top_p, k_floor, batch=batch)
