@@ -288,6 +288,26 @@ def _custom(name, heads, D, grid, block, top_p, k_floor, batch=1, modes=8):
                           else tuple(np.linspace(0.5, 5, heads)), top_p, k_floor, batch=batch)
 
 
+def test_many_reruns_bitwise_equal():
+    # the persistent kernel relaunched on fixed inputs, LPT and naive queues
+    # alternating: every output equals the first bit for bit (one-block items
+    # on wan14b; 2x1x2-grouped 64-token items with B = 2 and D = 64)
+    cases = [(fvgen.WORKLOADS["wan14b"], 60),
+             (_custom("rerun_grouped", 3, 64, (12, 20, 24), (4, 4, 4), 0.8, 2, batch=2), 60)]
+    for wl, reps in cases:
+        (q, k, v), (qd, kd, vd) = _inputs(wl)
+        mask_g, _, _ = fva.route(qd, kd, wl.grid, wl.block, wl.top_p, wl.k_floor)
+        ws = fva.workspace(fva.attn_workspace_bytes(tuple(qd.shape), wl.grid, wl.block), "cuda")
+        o0 = fva.sparse_attn(qd, kd, vd, wl.grid, wl.block, mask_g, ws=ws).view(torch.int16).clone()
+        o = torch.empty_like(qd)
+        bad = 0
+        for r in range(reps):
+            fva.sparse_attn(qd, kd, vd, wl.grid, wl.block, mask_g, sched=("lpt", "naive")[r % 2], ws=ws, out=o)
+            bad += int(not torch.equal(o.view(torch.int16), o0))
+        print("\n[%s] %d relaunches, %d differ from the first" % (wl.name, reps, bad), flush=True)
+        assert bad == 0
+
+
 @pytest.mark.parametrize("wl", [
     _custom("ragged_d64", 2, 64, (5, 9, 7), (4, 8, 8), 0.7, 1),
     _custom("h3_ragged", 3, 128, (6, 10, 13), (4, 4, 4), 0.8, 2),
