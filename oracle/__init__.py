@@ -66,10 +66,36 @@ def _load():
     return _lib
 
 
+def host_threads() -> int:
+    """Threads the oracle runs on by default: every CPU this process may run
+    on (its affinity mask), capped by OMP_NUM_THREADS when the environment
+    sets it (the CPU share of a shared host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, n)
+
+
+def cpu_model() -> str:
+    """The host CPU's model name from /proc/cpuinfo ("" if unknown)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
+
+
 def _threads(n):
     if n:
         return n
-    return max(1, min(16, os.cpu_count() or 1))
+    return host_threads()
 
 
 def _grid6(grid, block):
@@ -192,6 +218,74 @@ def attn(q, k, v, grid, block, mask, scale, items=None, nthreads=None, out=None)
                           mask.ctypes.data, float(scale), ip, n, out.ctypes.data, _threads(nthreads))
     if rc < 0:
         raise ValueError("fvo_attn rejected its arguments (%d)" % rc)
+    return out
+
+
+def _block_order(grid, block):
+    """(perm, start, count): the token ids of every block, blocks in index
+    order and each block's tokens in ascending id (row-major over t, y, x),
+    concatenated; block n's tokens are perm[start[n] : start[n] + count[n]]."""
+    tb = token_block(grid, block)
+    perm = np.argsort(tb, kind="stable")
+    count = np.bincount(tb, minlength=num_blocks(grid, block)).astype(np.int64)
+    start = np.concatenate(([0], np.cumsum(count)[:-1]))
+    return perm, start, count
+
+
+def attn_matmul(q, k, v, grid, block, mask, scale, items=None, nthreads=None, out=None) -> np.ndarray:
+    """Block-sparse attention in fp64, the two products by a library matmul.
+
+    The definition attn() follows (VSA guide, sections 1 and 6: a query
+    block attends to the real tokens of its selected key blocks only), with
+    the per-token loops replaced by matrix products over one query block:
+    for item (b, h, i), Q = the real rows of block i, K and V = the real rows
+    of the kept key blocks in ascending block order, all widened exactly to
+    fp64; S = (Q K^T) * scale; P = exp(S - rowmax(S)); O = (P V) / rowsum(P).
+    Only the order of the sums inside the two products differs from attn();
+    it is the same function up to fp64 rounding, and is used where attn()'s
+    plain loops would take too long.  Items run on a pool of host threads,
+    each calling the matmul single-threaded.  Returns [B, L, heads, D] fp64
+    (NaN where not computed; a row with no kept block gives NaN, as attn()).
+    """
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+
+    q = _c(q, np.uint16)
+    k = _c(k, np.uint16)
+    v = _c(v, np.uint16)
+    mask = _c(mask, np.uint32)
+    B, L, heads, D = q.shape
+    N = num_blocks(grid, block)
+    if out is None:
+        out = np.full((B, L, heads, D), np.nan, dtype=np.float64)
+    items = np.arange(B * heads * N, dtype=np.int64) if items is None else np.asarray(items, dtype=np.int64)
+    perm, start, count = _block_order(grid, block)
+    keep = mask_to_bool(mask.reshape(B * heads * N, -1), N)
+
+    def widen(x, b, h):
+        return (x[b, :, h, :].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+    def one(b, h, i, Qh, Kb, Vb):
+        rows = perm[start[i]:start[i] + count[i]]
+        sel = np.repeat(keep[(b * heads + h) * N + i], count)   # block-ordered key positions kept
+        Ks, Vs = Kb[sel], Vb[sel]
+        S = Qh[rows] @ Ks.T
+        S *= scale
+        S -= S.max(axis=1, keepdims=True) if Ks.shape[0] else 0.0
+        np.exp(S, out=S)
+        with np.errstate(invalid="ignore", divide="ignore"):
+            out[b, rows, h, :] = (S @ Vs) / S.sum(axis=1, keepdims=True)
+
+    by_head = {}
+    for it in items.tolist():
+        by_head.setdefault(it // N, []).append(it % N)
+    with threadpool_limits(limits=1, user_api="blas"), ThreadPoolExecutor(max_workers=_threads(nthreads)) as ex:
+        for bh, blocks in sorted(by_head.items()):
+            b, h = divmod(bh, heads)
+            Qh = widen(q, b, h)
+            Kb = widen(k, b, h)[perm]    # keys and values in block order
+            Vb = widen(v, b, h)[perm]
+            list(ex.map(lambda i: one(b, h, i, Qh, Kb, Vb), blocks))
     return out
 
 

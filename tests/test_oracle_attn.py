@@ -169,3 +169,53 @@ def test_real_pairs_counts():
     N = 120
     dense = oracle.dense_mask(1, 2, N)
     assert oracle.real_pairs(grid, block, dense) == 2 * 27280 * 27280
+
+
+@pytest.mark.parametrize("case", ["tiny_routed", "ragged_b2_d128", "tiles64_d64", "empty_rows"])
+def test_attn_matmul_equals_loops(case):
+    """oracle.attn_matmul (the same definition with library matrix products,
+    used for whole-workload parity) equals oracle.attn (plain loops) up to
+    fp64 rounding, NaN (a row with no kept block) in the same places."""
+    rng = np.random.default_rng(5)
+    if case == "tiny_routed":
+        wl = fvgen.WORKLOADS["tiny"]
+        q, k, v = fvgen.generate_qkv(wl)
+        grid, block, D = wl.grid, wl.block, wl.head_dim
+        mask = oracle.route(q, k, grid, block, wl.top_p, wl.k_floor)[0]
+    else:
+        grid, block, B, heads, D = {"ragged_b2_d128": ((5, 9, 7), (4, 8, 8), 2, 2, 128),
+                                    "tiles64_d64": ((6, 10, 13), (4, 4, 4), 1, 2, 64),
+                                    "empty_rows": ((6, 10, 13), (4, 4, 4), 1, 1, 64)}[case]
+        L = grid[0] * grid[1] * grid[2]
+        q, k, v = (_bf16(rng.normal(scale=s, size=(B, L, heads, D))) for s in (2.0, 1.0, 1.0))
+        N = oracle.num_blocks(grid, block)
+        mask = _random_mask(rng, B, heads, N, 0.4)
+        if case == "empty_rows":
+            mask[0, 0, [0, 7, N - 1]] = 0
+    scale = 1.0 / math.sqrt(D)
+    a = oracle.attn(q, k, v, grid, block, mask, scale)
+    b = oracle.attn_matmul(q, k, v, grid, block, mask, scale, nthreads=3)
+    assert np.array_equal(np.isnan(a), np.isnan(b))
+    assert (case == "empty_rows") == bool(np.isnan(a).any())
+    ok = ~np.isnan(a)
+    assert np.abs(a[ok] - b[ok]).max() <= 1e-12
+
+
+def test_attn_matmul_item_subset_and_constant_v():
+    """Only the listed items are written; V constant over the kept keys gives O = that constant (up to the rounding of sum(w v) / sum(w))."""
+    grid, block, heads, D = (5, 9, 7), (4, 8, 8), 2, 32
+    L = 5 * 9 * 7
+    rng = np.random.default_rng(9)
+    q, k = (_bf16(rng.normal(size=(1, L, heads, D))) for _ in range(2))
+    v = _bf16(np.broadcast_to(np.linspace(-2, 2, D), (1, L, heads, D)))
+    N = oracle.num_blocks(grid, block)
+    mask = _random_mask(rng, 1, heads, N, 0.5)
+    items = np.array([1, N + 3])
+    o = oracle.attn_matmul(q, k, v, grid, block, mask, 1.0 / math.sqrt(D), items=items)
+    tb = oracle.token_block(grid, block)
+    written = np.zeros((L, heads), dtype=bool)
+    written[tb == 1, 0] = True
+    written[tb == 3, 1] = True
+    assert np.array_equal(~np.isnan(o[0, :, :, 0]), written)
+    np.testing.assert_allclose(o[0][written], np.broadcast_to(fvgen.bf16_to_f64(v[0, 0, 0]), (int(written.sum()), D)),
+                               rtol=0, atol=1e-13)

@@ -56,6 +56,64 @@ def test_pool_random_vs_longdouble():
         np.testing.assert_allclose(m[0, :, n, :], ref.astype(np.float64), rtol=0, atol=1e-15)
 
 
+def _blockwise_constant(grid, block, B, heads, D, seed):
+    """bf16 tokens equal to one vector per (b, block, h): entries are small
+    multiples of 1/8, so every block mean, product and dot product is exact
+    in fp64.  Returns (bf16 bits [B, L, heads, D], values [B, heads, N, D])."""
+    N = oracle.num_blocks(grid, block)
+    tb = oracle.token_block(grid, block)
+    rng = np.random.default_rng(seed)
+    vals = rng.integers(-24, 25, size=(B, heads, N, D)) / 8.0
+    x = np.transpose(vals[:, :, tb, :], (0, 2, 1, 3))      # [B, L, heads, D]
+    return _bf16(x), vals
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_scores_closed_form_and_scale_rule(D):
+    """Q constant over each query block and K over each key block: the block
+    means are those constants exactly, so s[b,h,i,j] = (a_bhi . c_bhj) /
+    sqrt(D) with an exact dot product: head_dim^-0.5 scaling (VSA guide,
+    section 5), i indexing query blocks and j key blocks, separately per
+    batch entry and head.  For D = 64 the scale is exactly 1/8."""
+    grid, block, B, heads = (5, 9, 7), (4, 8, 8), 2, 3    # ragged blocks: 224, 28, 56, 7 tokens
+    q, a = _blockwise_constant(grid, block, B, heads, D, seed=D)
+    k, c = _blockwise_constant(grid, block, B, heads, D, seed=D + 1)
+    s = oracle.scores(oracle.pool(q, grid, block), oracle.pool(k, grid, block))
+    N = oracle.num_blocks(grid, block)
+    for b in range(B):
+        for h in range(heads):
+            for i in range(N):
+                for j in range(N):
+                    dot = sum((Fraction(float(x)) * Fraction(float(y)) for x, y in zip(a[b, h, i], c[b, h, j])),
+                              Fraction(0))
+                    assert s[b, h, i, j] == float(dot) / math.sqrt(D)
+                    if D == 64:
+                        assert s[b, h, i, j] == float(dot / 8)
+    # not symmetric in (i, j) and not shared across heads: an index slip shows
+    assert not np.array_equal(s, np.swapaxes(s, -1, -2))
+    assert not np.array_equal(s[:, 0], s[:, 1])
+
+
+@pytest.mark.parametrize("top_p,k_floor,expect", [(0.3, 5, 29), (0.05, 9, 9), (0.777, 3, 75)])
+def test_identical_keys_keep_lowest_indices_end_to_end(top_p, k_floor, expect):
+    """Every key token the same bf16 vector: all key blocks pool to it, every
+    row's scores tie, P = 1/N, so the router keeps max(k_floor, ceil(p N))
+    blocks, the lowest indices first.  Runs the whole oracle router (pooling,
+    scores, softmax, order, cumulative mass, floor) on bf16 inputs with p N
+    not an integer (N = 96: p N = 28.8, 4.8, 74.59)."""
+    grid, block, heads, D = (8, 16, 24), (2, 4, 4), 2, 64
+    N = oracle.num_blocks(grid, block)
+    assert N == 96 and expect == max(k_floor, math.ceil(np.float32(top_p) * N))
+    L = 8 * 16 * 24
+    rng = np.random.default_rng(11)
+    q = _bf16(rng.normal(scale=2.0, size=(1, L, heads, D)))
+    k = np.broadcast_to(_bf16(rng.normal(size=D)), (1, L, heads, D))
+    mask, cnt, flags, status = oracle.route(q, k, grid, block, top_p, k_floor)
+    assert status == 0 and (flags == 0).all()
+    assert (cnt == expect).all()
+    assert all(g == set(range(expect)) for g in _mask_sets(mask, N))
+
+
 def test_scores_vs_matmul():
     wl = fvgen.WORKLOADS["tiny"]
     q, k, _ = fvgen.generate_qkv(wl)
