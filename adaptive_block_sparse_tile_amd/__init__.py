@@ -7,7 +7,10 @@ built, every call raises.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
+import functools
+import inspect
 import math
 import os
 
@@ -149,6 +152,23 @@ def _torch():
     return torch
 
 
+def _on_stream(fn):
+    """Run fn with its `stream` argument (when given) as torch's current
+    stream, so that every tensor fn allocates -- outputs and the temporary
+    workspace freed on return -- belongs to the stream the kernels are
+    enqueued on: the caching allocator then hands a freed block only to work
+    ordered after those kernels."""
+    sig = inspect.signature(fn)
+
+    @functools.wraps(fn)
+    def wrapped(*args, **kwargs):
+        stream = sig.bind(*args, **kwargs).arguments.get("stream")
+        ctx = _torch().cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+        with ctx:
+            return fn(*args, **kwargs)
+    return wrapped
+
+
 def _stream_ptr(stream):
     torch = _torch()
     s = stream if stream is not None else torch.cuda.current_stream()
@@ -170,6 +190,7 @@ def workspace(nbytes: int, device):
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
+@_on_stream
 def route(q, k, grid, block, top_p: float, k_floor: int, ws=None, out=None, stream=None):
     """Block router on the GPU -> (mask u32 [B, heads, N, W] as int32 bits, kv_cnt int32 [B, heads, N],
     status int32 [1])."""
@@ -194,6 +215,7 @@ def route(q, k, grid, block, top_p: float, k_floor: int, ws=None, out=None, stre
     return mask, cnt, status
 
 
+@_on_stream
 def sparse_attn(q, k, v, grid, block, mask, scale=None, sched: str = "lpt", trace=None, ws=None, out=None,
                 stream=None):
     """Block-sparse attention on the GPU -> O bf16 [B, L, heads, D].
@@ -217,6 +239,7 @@ def sparse_attn(q, k, v, grid, block, mask, scale=None, sched: str = "lpt", trac
     return o
 
 
+@_on_stream
 def static_mask(shape, grid, block, local=(1, 1, 1), anchor_t=0, out=None, device="cuda", stream=None):
     """Static local-box + anchor-slab block mask of every (b, h) on the GPU -> (mask, kv_cnt)."""
     torch = _torch()
@@ -234,6 +257,7 @@ def static_mask(shape, grid, block, local=(1, 1, 1), anchor_t=0, out=None, devic
     return mask, cnt
 
 
+@_on_stream
 def attn_plan(k, v, grid, block, mask, sched: str = "lpt", head_xcd=None, ws=None, stream=None):
     """First half of sparse_attn: chunk images, item costs and the schedule,
     written into ws (allocated if None and returned).  head_xcd: optional
@@ -249,6 +273,7 @@ def attn_plan(k, v, grid, block, mask, sched: str = "lpt", head_xcd=None, ws=Non
     return ws
 
 
+@_on_stream
 def attn_exec(q, grid, block, mask, ws, scale=None, sched: str = "lpt", trace=None, out=None, stream=None):
     """Second half of sparse_attn: the attention kernel over the plan in ws
     (sched as given to attn_plan)."""
@@ -273,6 +298,7 @@ def attn_items(shape, grid, block) -> int:
     return n
 
 
+@_on_stream
 def attn_schedule(shape, grid, block, ws, stream=None):
     """The schedule a plan wrote into ws -> (order int32 [items], qoff int32 [9],
     cost int32 [items] holding the uint32 item costs), device tensors."""
@@ -292,6 +318,7 @@ def sasa_workspace_bytes(shape, grid, block, rounds) -> int:
                                            int(rounds))
 
 
+@_on_stream
 def sasa(shape, grid, block, mask, route_ws, rounds=4, out=None, ws=None, stream=None):
     """Slack-aware augmentation of a routed mask on the GPU (8 XCDs as ranks).
 
@@ -320,6 +347,7 @@ def dense_workspace_bytes(shape):
     return int(load().fva_dense_workspace_bytes(ctypes.byref(make_desc(*shape))))
 
 
+@_on_stream
 def dense_attn_ref(q, k, v, scale=None, out=None, ws=None, stream=None):
     """Dense attention over all tokens on the GPU (same kernel and numerics)."""
     torch = _torch()

@@ -88,23 +88,35 @@ fva_status check_scale(int D, float scale) {
   return FVA_OK;
 }
 
+// The router's workspace: pooled means (fp64 [B*heads, N, D], Q and K) and
+// one slab of fp64 scores.  The scores are produced and consumed tile by
+// tile (64 query blocks of one head per tile), so the slab holds at most
+// kScoreSlabBytes of them, never the whole [B*heads, N, N] matrix.
+constexpr size_t kScoreSlabBytes = (size_t)128 << 20;
+constexpr int64_t kMaxSlabTiles = 65535;  // grid.y of the scores kernel
+
 struct RouteWs {
   size_t qbar, kbar, s, total;
+  int64_t slab_tiles;
 };
 
-RouteWs route_ws_layout(const fva_desc* d, const fva::Geo& g) {
+RouteWs route_ws_layout(const fva_desc* d, const fva::Geo& g, size_t slab_bytes = kScoreSlabBytes) {
   RouteWs w;
   const size_t rows = (size_t)d->B * d->heads * g.N;
+  const int64_t tiles = (int64_t)d->B * d->heads * ((g.N + 63) / 64);
+  const size_t tile_bytes = (size_t)64 * g.N * sizeof(double);
+  w.slab_tiles = std::min<int64_t>(std::min<int64_t>(tiles, kMaxSlabTiles),
+                                   std::max<int64_t>(1, (int64_t)(slab_bytes / tile_bytes)));
   size_t off = 0;
   w.qbar = off; off += align_up(rows * d->D * sizeof(double));
   w.kbar = off; off += align_up(rows * d->D * sizeof(double));
-  w.s = off; off += align_up(rows * (size_t)g.N * sizeof(double));
+  w.s = off; off += align_up((size_t)w.slab_tiles * tile_bytes);
   w.total = off;
   return w;
 }
 
 struct AttnWs {
-  size_t tok, cnt, tiles, keys, rank, order, head_pos, head_cost, qoff, qctr, total;
+  size_t tok, cnt, tiles, keys, rank, order, head_pos, head_cost, qoff, qctr, tag, total;
 };
 
 AttnWs attn_ws_layout(const fva_desc* d, const fva::Geo& g) {
@@ -123,6 +135,7 @@ AttnWs attn_ws_layout(const fva_desc* d, const fva::Geo& g) {
   w.head_cost = off; off += align_up(bh * sizeof(uint64_t));
   w.qoff = off; off += align_up(16 * sizeof(int32_t));
   w.qctr = off; off += align_up(16 * sizeof(uint32_t));
+  w.tag = off; off += align_up(sizeof(uint64_t));
   w.total = off;
   return w;
 }
@@ -136,6 +149,32 @@ fva_status check_ws(const void* ws, size_t have, size_t need) {
 
 fva_status device_error(hipError_t e, const char* what) {
   return fail(FVA_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+// A launch's grid must fit one dispatch: fewer than 2^32 work-items along x.
+fva_status check_launch(int64_t workgroups, int threads, const char* what) {
+  if (workgroups < 1 || workgroups * threads < ((int64_t)1 << 32)) return FVA_OK;
+  return fail(FVA_ERR_UNSUPPORTED, "%s needs %lld workgroups of %d threads, more than one launch holds (2^32 threads)",
+              what, (long long)workgroups, threads);
+}
+
+// B*heads is bounded for every entry point (the schedule's per-head LDS
+// tables and the per-head grid dimension of its ranking kernel).
+fva_status check_heads(const fva_desc* d) {
+  if ((int64_t)d->B * d->heads > kMaxHeads)
+    return fail(FVA_ERR_UNSUPPORTED, "B*heads = %lld > %d not supported", (long long)d->B * d->heads, kMaxHeads);
+  return FVA_OK;
+}
+
+// Launch sizes of the router for this shape (rows are routed one slab of
+// score tiles per launch).
+fva_status check_route_launches(const fva_desc* d, const fva::Geo& g, int64_t slab_tiles) {
+  const int64_t chunks = ((int64_t)d->heads * d->D / 8 + 63) / 64;
+  const int words = (g.N + 31) / 32;
+  const int threads = g.N <= 512 ? 64 : 64 * ((words + 63) / 64);
+  fva_status st = check_launch((int64_t)g.N * chunks, 256, "pooling");
+  if (st == FVA_OK) st = check_launch(slab_tiles * 64, threads, "row routing");
+  return st;
 }
 
 }  // namespace
@@ -168,21 +207,29 @@ int32_t fva_attn_workgroups(const fva_desc* desc, const fva_grid* grid) {
   return err ? -1 : n;
 }
 
-fva_status fva_route(const void* q, const void* k, const fva_desc* desc, const fva_grid* grid,
-                     const fva_route_cfg* cfg, uint32_t* mask, int32_t* kv_cnt, uint32_t* status, void* ws,
-                     size_t ws_bytes, void* stream) {
+// Host validation of a router call whose score slab may hold slab_bytes;
+// on success *lay is its workspace layout.
+static fva_status route_check(const void* q, const void* k, const fva_desc* desc, const fva_grid* grid,
+                              const fva_route_cfg* cfg, const uint32_t* mask, size_t slab_bytes, fva::Geo* g,
+                              RouteWs* lay) {
   if (!q || !k || !mask || !cfg) return fail(FVA_ERR_INVALID_ARG, "q, k, mask and cfg must not be null");
   fva_status st = check_desc(desc);
   if (st != FVA_OK) return st;
-  fva::Geo g;
-  if ((st = check_grid(desc, grid, &g)) != FVA_OK) return st;
+  if ((st = check_grid(desc, grid, g)) != FVA_OK) return st;
   if (std::isnan(cfg->top_p)) return fail(FVA_ERR_INVALID_ARG, "top_p is NaN");
   if (cfg->k_floor < 1) return fail(FVA_ERR_TOPK, "k_floor %d must be a positive integer", cfg->k_floor);
-  if (cfg->k_floor > g.N) return fail(FVA_ERR_TOPK, "k_floor %d > num_blocks %d", cfg->k_floor, g.N);
-  if (g.N > kMaxBlocks) return fail(FVA_ERR_UNSUPPORTED, "num_blocks %d > %d not supported", g.N, kMaxBlocks);
-  const RouteWs lay = route_ws_layout(desc, g);
-  if ((st = check_ws(ws, ws_bytes, lay.total)) != FVA_OK) return st;
+  if (cfg->k_floor > g->N) return fail(FVA_ERR_TOPK, "k_floor %d > num_blocks %d", cfg->k_floor, g->N);
+  if (g->N > kMaxBlocks) return fail(FVA_ERR_UNSUPPORTED, "num_blocks %d > %d not supported", g->N, kMaxBlocks);
+  *lay = route_ws_layout(desc, *g, slab_bytes);
+  if ((st = check_heads(desc)) != FVA_OK || (st = check_route_launches(desc, *g, lay->slab_tiles)) != FVA_OK)
+    return st;
+  return FVA_OK;
+}
 
+// The router's launches on a validated call, its workspace at ws.
+static fva_status route_launch(const void* q, const void* k, const fva_desc* desc, const fva::Geo& g,
+                               const fva_route_cfg* cfg, const RouteWs& lay, uint32_t* mask, int32_t* kv_cnt,
+                               uint32_t* status, void* ws, void* stream) {
   hipStream_t s = (hipStream_t)stream;
   char* w = (char*)ws;
   double* qbar = (double*)(w + lay.qbar);
@@ -190,12 +237,21 @@ fva_status fva_route(const void* q, const void* k, const fva_desc* desc, const f
   double* S = (double*)(w + lay.s);
   hipError_t e = fva::launch_pool(q, k, g, desc->B, desc->L, desc->heads, desc->D, qbar, kbar, status, s);
   if (e != hipSuccess) return device_error(e, "pool kernel launch");
-  e = fva::launch_scores(qbar, kbar, desc->B * desc->heads, g.N, desc->D, S, s);
-  if (e != hipSuccess) return device_error(e, "scores kernel launch");
-  e = fva::launch_route_rows(S, (int64_t)desc->B * desc->heads * g.N, g.N, cfg->top_p, cfg->k_floor, mask, kv_cnt,
-                             status, s);
-  if (e != hipSuccess) return device_error(e, "route kernel launch");
+  e = fva::launch_route_slabs(qbar, kbar, desc->B * desc->heads, g.N, desc->D, cfg->top_p, cfg->k_floor, S,
+                              lay.slab_tiles, mask, kv_cnt, status, s);
+  if (e != hipSuccess) return device_error(e, "router launch");
   return ok();
+}
+
+fva_status fva_route(const void* q, const void* k, const fva_desc* desc, const fva_grid* grid,
+                     const fva_route_cfg* cfg, uint32_t* mask, int32_t* kv_cnt, uint32_t* status, void* ws,
+                     size_t ws_bytes, void* stream) {
+  fva::Geo g;
+  RouteWs lay;
+  fva_status st = route_check(q, k, desc, grid, cfg, mask, kScoreSlabBytes, &g, &lay);
+  if (st != FVA_OK) return st;
+  if ((st = check_ws(ws, ws_bytes, lay.total)) != FVA_OK) return st;
+  return route_launch(q, k, desc, g, cfg, lay, mask, kv_cnt, status, ws, stream);
 }
 
 // Shared validation and workspace views of the sparse attention calls.
@@ -216,8 +272,8 @@ static fva_status sparse_setup(const void* q, const void* k, const void* v, void
   const int64_t items = (int64_t)desc->B * desc->heads * g.N;
   const int64_t slots = items * fva::attn_chunks_per_block(g.bt * g.bh * g.bw);
   if (slots >= ((int64_t)1 << 31)) return fail(FVA_ERR_UNSUPPORTED, "too many work items");
-  if ((int64_t)desc->B * desc->heads > kMaxHeads)
-    return fail(FVA_ERR_UNSUPPORTED, "B*heads = %lld > %d not supported", (long long)desc->B * desc->heads, kMaxHeads);
+  if ((st = check_heads(desc)) != FVA_OK) return st;
+  if ((st = check_launch(slots, 256, "chunk tiling")) != FVA_OK) return st;
   const AttnWs lay = attn_ws_layout(desc, g);
   if ((st = check_ws(ws, ws_bytes, lay.total)) != FVA_OK) return st;
   char* w = (char*)ws;
@@ -237,6 +293,7 @@ static fva_status sparse_setup(const void* q, const void* k, const void* v, void
   a->head_cost = (uint64_t*)(w + lay.head_cost);
   a->qoff = (int32_t*)(w + lay.qoff);
   a->qctr = (uint32_t*)(w + lay.qctr);
+  a->plan_tag = (uint64_t*)(w + lay.tag);
   return FVA_OK;
 }
 
@@ -274,16 +331,19 @@ fva_status fva_sasa(const fva_desc* desc, const fva_grid* grid, const uint32_t* 
   if (st != FVA_OK) return st;
   fva::Geo g;
   if ((st = check_grid(desc, grid, &g)) != FVA_OK) return st;
-  if ((int64_t)desc->B * desc->heads > kMaxHeads)
-    return fail(FVA_ERR_UNSUPPORTED, "B*heads = %lld > %d not supported", (long long)desc->B * desc->heads, kMaxHeads);
+  if ((st = check_heads(desc)) != FVA_OK) return st;
+  if (g.N > kMaxBlocks) return fail(FVA_ERR_UNSUPPORTED, "num_blocks %d > %d not supported", g.N, kMaxBlocks);
+  if ((st = check_launch((int64_t)desc->B * desc->heads * g.N, 64, "augmentation candidates")) != FVA_OK) return st;
   const RouteWs rl = route_ws_layout(desc, g);
   if (route_ws_bytes < rl.total)
     return fail(FVA_ERR_WORKSPACE, "route workspace holds %zu bytes, the router's is %zu", route_ws_bytes, rl.total);
   const SasaWs lay = sasa_ws_layout(desc, g, rounds);
   if ((st = check_ws(ws, ws_bytes, lay.total)) != FVA_OK) return st;
   char* w = (char*)ws;
-  const double* S = (const double*)((const char*)route_ws + rl.s);
-  hipError_t e = fva::launch_sasa(S, mask_in, g, desc->B * desc->heads, rounds, mask_out, kv_cnt, head_xcd, xcd_load,
+  const double* qbar = (const double*)((const char*)route_ws + rl.qbar);
+  const double* kbar = (const double*)((const char*)route_ws + rl.kbar);
+  hipError_t e = fva::launch_sasa(qbar, kbar, desc->D, mask_in, g, desc->B * desc->heads, rounds, mask_out, kv_cnt,
+                                  head_xcd, xcd_load,
                                   (int32_t*)(w + lay.cand), (int64_t*)(w + lay.cost), (int32_t*)(w + lay.slot),
                                   (int32_t*)(w + lay.nh), (hipStream_t)stream);
   if (e != hipSuccess) return device_error(e, "sasa launch");
@@ -300,7 +360,10 @@ fva_status fva_static_mask(const fva_desc* desc, const fva_grid* grid, const fva
   if (st != FVA_OK) return st;
   fva::Geo g;
   if ((st = check_grid(desc, grid, &g)) != FVA_OK) return st;
+  if (g.N > kMaxBlocks) return fail(FVA_ERR_UNSUPPORTED, "num_blocks %d > %d not supported", g.N, kMaxBlocks);
+  if ((st = check_heads(desc)) != FVA_OK) return st;
   const int64_t rows = (int64_t)desc->B * desc->heads * g.N;
+  if ((st = check_launch(rows, 64, "static mask")) != FVA_OK) return st;
   hipError_t e = fva::launch_static_mask(g, rows, cfg->lt, cfg->lh, cfg->lw, cfg->anchor_t, mask, kv_cnt,
                                          (hipStream_t)stream);
   if (e != hipSuccess) return device_error(e, "static mask launch");
@@ -383,6 +446,11 @@ fva_status fva_dense_attn_ref(const void* q, const void* k, const void* v, void*
   fva_status st = check_desc(desc);
   if (st != FVA_OK) return st;
   if ((st = check_scale(desc->D, scale)) != FVA_OK) return st;
+  if ((st = check_heads(desc)) != FVA_OK) return st;
+  const int64_t bh = (int64_t)desc->B * desc->heads;
+  if ((st = check_launch(bh * ((desc->L + 63) / 64), 256, "chunk tiling")) != FVA_OK ||
+      (st = check_launch(8 * ((bh * ((desc->L + 255) / 256) + 7) / 8), 512, "dense attention")) != FVA_OK)
+    return st;
   if ((st = check_ws(ws, ws_bytes, fva_dense_workspace_bytes(desc))) != FVA_OK) return st;
   hipError_t e = fva::launch_dense_attn(q, k, v, o, desc->B, desc->L, desc->heads, desc->D, scale, ws,
                                         (hipStream_t)stream);

@@ -94,6 +94,11 @@ struct AttnParams {
   int gt, gh, gw, gT, gH, gW, n_groups, wpb;
   float scale_log2;
   uint64_t* trace;
+  // sparse: the shape tag the plan wrote into the workspace, and the value
+  // this launch expects there (a mismatch: the workspace holds no plan for
+  // this shape, and O is filled with NaN instead)
+  const uint64_t* plan_tag;
+  uint64_t want_tag;
 };
 
 // Block index of member k of group gid, or -1 past the grid's edge.
@@ -321,6 +326,15 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
   const int lr = lane & 31, hi = lane >> 5;
   const float cl2 = p.scale_log2;
 
+  if (!DENSE && *p.plan_tag != p.want_tag) {
+    // no plan for this shape in the workspace: every element of O becomes
+    // NaN (grid-stride over the persistent workgroups) rather than output
+    // computed from mismatched tables
+    const int64_t n = (int64_t)p.B * p.L * p.heads * D;
+    for (int64_t e = (int64_t)blockIdx.x * THREADS + tid; e < n; e += (int64_t)gridDim.x * THREADS)
+      p.o[e] = (bf16_bits)0x7FC0;
+    return;
+  }
   if (!DENSE)  // ordered before any read by the barrier after the first item fetch
     for (int j = tid; j < p.g.N; j += THREADS) cnt_s[j] = (uint16_t)p.cnt[j];
   uint64_t t_first = 0, t_last = 0, busy = 0, nitems = 0;
@@ -1029,10 +1043,12 @@ constexpr int COST_WAVES = 8;
 __global__ __launch_bounds__(COST_WAVES * 64) void cost_kernel(AttnParams p, const int32_t* __restrict__ cnt,
                                                                uint64_t* __restrict__ keys, uint32_t* __restrict__ rank,
                                                                uint32_t* __restrict__ qctr,
-                                                               uint64_t* __restrict__ head_cost) {
+                                                               uint64_t* __restrict__ head_cost,
+                                                               uint64_t* __restrict__ tag) {
   extern __shared__ int32_t cnt_s[];  // [N]
   for (int j = threadIdx.x; j < p.g.N; j += COST_WAVES * 64) cnt_s[j] = cnt[j];
   if (blockIdx.x == 0 && threadIdx.x < NXCD) qctr[threadIdx.x] = 0u;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *tag = p.want_tag;
   __syncthreads();
   const int lane = threadIdx.x & 63;
   const int item = blockIdx.x * COST_WAVES + (threadIdx.x >> 6);
@@ -1134,22 +1150,28 @@ __global__ __launch_bounds__(256) void head_plan_kernel(const uint64_t* __restri
     head_pos[horder[r]] = qoff_s[place[r] & 7] + (place[r] >> 3) * N;
 }
 
-// rank[a] += #{b in this tile of a's head : key[b] > key[a]}  (keys distinct)
-__global__ __launch_bounds__(256) void rank_kernel(const uint64_t* __restrict__ keys, int n_items, int N,
+// rank[a] += #{b in this tile of a's head : key[b] > key[a]}  (keys distinct).
+// grid = (ceil(G / 256), ceil(G / 2048), heads): item tiles of one head only.
+__global__ __launch_bounds__(256) void rank_kernel(const uint64_t* __restrict__ keys, int G,
                                                    uint32_t* __restrict__ rank) {
   __shared__ uint64_t tile[2048];
+  const uint64_t* hk = keys + (int64_t)blockIdx.z * G;
   const int a = blockIdx.x * 256 + threadIdx.x;
   const int b0 = blockIdx.y * 2048;
-  const int nb = min(2048, n_items - b0);
-  for (int t = threadIdx.x; t < nb; t += 256) tile[t] = keys[b0 + t];
+  const int nb = min(2048, G - b0);
+  for (int t = threadIdx.x; t < nb; t += 256) tile[t] = hk[b0 + t];
   __syncthreads();
-  if (a >= n_items) return;
-  const uint64_t ka = keys[a];
-  const int head = a / N;
-  const int lo = max(0, head * N - b0), hi_ = min(nb, (head + 1) * N - b0);
+  if (a >= G) return;
+  const uint64_t ka = hk[a];
   uint32_t c = 0;
-  for (int t = lo; t < hi_; ++t) c += tile[t] > ka ? 1u : 0u;
-  if (c) atomicAdd(&rank[a], c);
+  for (int t = 0; t < nb; ++t) c += tile[t] > ka ? 1u : 0u;
+  if (c) atomicAdd(&rank[(int64_t)blockIdx.z * G + a], c);
+}
+
+// The pop counters of the queues start at zero in every launch of the
+// persistent kernel, so that one plan serves any number of execs.
+__global__ __launch_bounds__(64) void queue_reset_kernel(uint32_t* __restrict__ qctr) {
+  if (threadIdx.x < NXCD) qctr[threadIdx.x] = 0u;
 }
 
 __global__ __launch_bounds__(256) void scatter_kernel(const uint32_t* __restrict__ rank,
@@ -1225,6 +1247,16 @@ int attn_persistent_workgroups(int D, int block_volume, int* err) {
   return cus * occ;
 }
 
+// The tag a plan leaves in its workspace: a hash of the tensor shape and the
+// token and block grid (never 0, the value of cleared memory).
+uint64_t plan_tag_of(int B, int L, int heads, int D, const Geo& g) {
+  const int64_t f[10] = {B, L, heads, D, g.T, g.H, g.W, g.bt, g.bh, g.bw};
+  uint64_t h = 0xcbf29ce484222325ull;  // FNV-1a, 64 bit
+  for (int64_t x : f)
+    for (int b = 0; b < 8; ++b) h = (h ^ (uint64_t)((x >> (8 * b)) & 0xff)) * 0x100000001b3ull;
+  return h | 1ull;
+}
+
 static AttnParams sparse_params(const AttnLaunch& a) {
   const int vol = a.g.bt * a.g.bh * a.g.bw;
   const GroupShape gs = group_shape(vol);
@@ -1257,6 +1289,8 @@ static AttnParams sparse_params(const AttnLaunch& a) {
   prm.n_items = a.B * a.heads * prm.n_groups;
   prm.scale_log2 = a.scale * 1.4426950408889634f;
   prm.trace = a.trace;
+  prm.plan_tag = a.plan_tag;
+  prm.want_tag = plan_tag_of(a.B, a.L, a.heads, a.D, a.g);
   return prm;
 }
 
@@ -1274,12 +1308,13 @@ hipError_t launch_sparse_plan(const AttnLaunch& a, int sched, const int32_t* hea
     hipLaunchKernelGGL(tile_kernel<64>, dim3(slots), dim3(256), 0, st, (const bf16_bits*)a.k, (const bf16_bits*)a.v,
                        a.tok, a.g, a.L, a.heads, cpb, a.tiles);
   hipLaunchKernelGGL(cost_kernel, dim3((n_items + COST_WAVES - 1) / COST_WAVES), dim3(COST_WAVES * 64),
-                     (size_t)a.g.N * sizeof(int32_t), st, prm, a.blk_cnt, a.keys, a.rank, a.qctr, a.head_cost);
+                     (size_t)a.g.N * sizeof(int32_t), st, prm, a.blk_cnt, a.keys, a.rank, a.qctr, a.head_cost,
+                     a.plan_tag);
   hipLaunchKernelGGL(head_plan_kernel, dim3(1), dim3(256), (size_t)BH * 16, st, a.head_cost, per_head, BH, lpt,
                      sched == 2 ? head_xcd : nullptr, a.head_pos, a.qoff);
   if (lpt)
-    hipLaunchKernelGGL(rank_kernel, dim3((n_items + 255) / 256, (n_items + 2047) / 2048), dim3(256), 0, st, a.keys,
-                       n_items, per_head, a.rank);
+    hipLaunchKernelGGL(rank_kernel, dim3((per_head + 255) / 256, (per_head + 2047) / 2048, BH), dim3(256), 0, st,
+                       a.keys, per_head, a.rank);
   hipLaunchKernelGGL(scatter_kernel, dim3((n_items + 255) / 256), dim3(256), 0, st, a.rank, a.head_pos, n_items,
                      per_head, lpt, a.order);
   return hipGetLastError();
@@ -1292,6 +1327,7 @@ hipError_t launch_sparse_exec(const AttnLaunch& a, int sched, hipStream_t st) {
   int err = 0;
   const int grid = attn_persistent_workgroups(a.D, vol, &err);
   if (err) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(queue_reset_kernel, dim3(1), dim3(64), 0, st, a.qctr);
   void* args[] = {&prm};
   return hipLaunchKernel(sparse_kernel(a.D, group_shape(vol).wpb < WAVES), dim3(grid), dim3(WAVES * 64), args, 0, st);
 }

@@ -11,17 +11,23 @@ namespace fva {
 // Router (fva_route.hip)
 hipError_t launch_pool(const void* q, const void* k, const Geo& g, int B, int L, int heads, int D, double* qbar,
                        double* kbar, uint32_t* status, hipStream_t st);
-hipError_t launch_scores(const double* qbar, const double* kbar, int BH, int N, int D, double* S, hipStream_t st);
-// Slack-aware augmentation over the router's scores S (fp64 [BH, N, N]).
-hipError_t launch_sasa(const double* S, const uint32_t* mask_in, const Geo& g, int BH, int R, uint32_t* mask_out,
+// Scores and row routing slab by slab: the query rows of every head are cut
+// into tiles of 64 query blocks, and slab_tiles tiles at a time get their
+// fp64 scores in S ([slab_tiles * 64][N]) and are routed from there.
+hipError_t launch_route_slabs(const double* qbar, const double* kbar, int BH, int N, int D, float top_p, int k_floor,
+                              double* S, int64_t slab_tiles, uint32_t* mask, int32_t* kv_cnt, uint32_t* status,
+                              hipStream_t st);
+// Slack-aware augmentation; each row's scores are recomputed from the
+// router's pooled means (fp64 [BH, N, D]) exactly as the router computed them.
+hipError_t launch_sasa(const double* qbar, const double* kbar, int D, const uint32_t* mask_in, const Geo& g, int BH,
+                       int R, uint32_t* mask_out,
                        int32_t* kv_cnt, int32_t* head_xcd, int64_t* xcd_load, int32_t* cand, int64_t* row_cost,
                        int32_t* slot_head, int32_t* nh, hipStream_t st);
 
 // Static block mask of every (b, h): rows = B*heads*N.
 hipError_t launch_static_mask(const Geo& g, int64_t rows, int lt, int lh, int lw, int anchor_t, uint32_t* mask,
                               int32_t* kv_cnt, hipStream_t st);
-hipError_t launch_route_rows(const double* S, int64_t rows, int N, float top_p, int k_floor, uint32_t* mask,
-                             int32_t* kv_cnt, uint32_t* status, hipStream_t st);
+
 
 // Attention (fva_attn.hip)
 struct AttnLaunch {
@@ -45,7 +51,11 @@ struct AttnLaunch {
   uint64_t* head_cost; // [B*heads] summed item costs of each head
   int32_t* qoff;       // [9] queue segments (one per XCD)
   uint32_t* qctr;      // [8] queue pop counters
+  uint64_t* plan_tag;  // [1] shape tag written by the plan, checked by the exec
 };
+
+// Shape tag of a plan (nonzero hash of the tensor shape and the grid).
+uint64_t plan_tag_of(int B, int L, int heads, int D, const Geo& g);
 
 // 64-key chunk slots reserved per block.
 int attn_chunks_per_block(int block_volume);

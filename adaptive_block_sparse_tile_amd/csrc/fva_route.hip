@@ -16,6 +16,8 @@
 //                      floor, mask words and kept count
 //   route_select_kernel N > 512: the same decisions by bisection on
 //                      order-preserving keys (no full sort)
+#include <algorithm>
+
 #include "fva_dev.h"
 #include "fva_kernels.h"
 
@@ -103,18 +105,23 @@ __global__ __launch_bounds__(256) void pool_kernel(const bf16_bits* __restrict__
 }
 
 // ---------------------------------------------------------------------------
-// Block scores.  grid = (ceil(N/64), ceil(N/64), B*heads), 256 threads, each
-// thread a 4x4 set of outputs i = i0 + ty + 16a, j = j0 + tx + 16c.  The dot
-// product runs over d in increasing order for every (i, j), so equal key
-// blocks get bit-equal scores (exact ties stay exact).
+// Block scores of one slab.  The rows of all heads are cut into tiles of 64
+// query blocks (tile t = bh * nIT + i / 64, nIT = ceil(N / 64) tiles per
+// head); a slab is the tiles t0 .. t0 + gridDim.y - 1, and its scores go to
+// S[(tile - t0) * 64 + i % 64][j] (rows past N in a head's last tile are
+// left unwritten).  grid = (ceil(N/64) key tiles, tiles in the slab), 256
+// threads, each a 4x4 set of outputs i = i0 + ty + 16a, j = j0 + tx + 16c.
+// The dot product runs over d in increasing order for every (i, j), so equal
+// key blocks get bit-equal scores (exact ties stay exact).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void scores_kernel(const double* __restrict__ qbar, const double* __restrict__ kbar,
-                                                     int N, int D, double* __restrict__ S) {
+                                                     int N, int D, int t0, int nIT, double* __restrict__ S) {
   __shared__ double As[64][33];
   __shared__ double Bs[64][33];
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-  const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
-  const int64_t bh = blockIdx.z;
+  const int tile = t0 + blockIdx.y;
+  const int64_t bh = tile / nIT;
+  const int i0 = (tile % nIT) * 64, j0 = blockIdx.x * 64;
   const double* qa = qbar + bh * N * D;
   const double* kb = kbar + bh * N * D;
   double acc[4][4];
@@ -147,16 +154,31 @@ __global__ __launch_bounds__(256) void scores_kernel(const double* __restrict__ 
     __syncthreads();
   }
   const double rs = sqrt((double)D);
+  double* out = S + (int64_t)blockIdx.y * 64 * N;
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
-    const int i = i0 + ty + 16 * a;
-    if (i >= N) continue;
+    const int r = ty + 16 * a;
+    if (i0 + r >= N) continue;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int j = j0 + tx + 16 * c;
-      if (j < N) S[(bh * N + i) * N + j] = acc[a][c] / rs;
+      if (j < N) out[(int64_t)r * N + j] = acc[a][c] / rs;
     }
   }
+}
+
+// Slab row r of a router launch: its (b*heads + h) and query block i, from
+// the slab's first tile t0 (i >= N: a padding row of a head's last tile).
+struct SlabRow {
+  int64_t out;  // (b*heads + h)*N + i, the row of the mask and the counts
+  int i;
+};
+__device__ inline SlabRow slab_row(int64_t r, int t0, int nIT, int N) {
+  const int64_t tile = t0 + r / 64;
+  SlabRow x;
+  x.i = (int)((tile % nIT) * 64 + r % 64);
+  x.out = (tile / nIT) * N + x.i;
+  return x;
 }
 
 // ---------------------------------------------------------------------------
@@ -194,8 +216,9 @@ __device__ inline double block_max(double v, double* red) {
 }
 
 template <int SLOTS, int THREADS>
-__global__ __launch_bounds__(THREADS) void route_rows_kernel(const double* __restrict__ S, int N, int words,
-                                                             float top_p, int k_floor, uint32_t* __restrict__ mask,
+__global__ __launch_bounds__(THREADS) void route_rows_kernel(const double* __restrict__ S, int N, int words, int t0,
+                                                             int nIT, float top_p, int k_floor,
+                                                             uint32_t* __restrict__ mask,
                                                              int32_t* __restrict__ kv_cnt,
                                                              uint32_t* __restrict__ status) {
   constexpr int E = SLOTS / THREADS;
@@ -207,8 +230,10 @@ __global__ __launch_bounds__(THREADS) void route_rows_kernel(const double* __res
   __shared__ int nstar_s;
 
   const int tid = threadIdx.x;
-  const int64_t row = blockIdx.x;
-  const double* s = S + row * N;
+  const SlabRow sr = slab_row(blockIdx.x, t0, nIT, N);
+  if (sr.i >= N) return;  // padding row of a head's last tile
+  const int64_t row = sr.out;
+  const double* s = S + (int64_t)blockIdx.x * N;
 
   bool bad = false;
   double lmax = -INFINITY;
@@ -436,16 +461,19 @@ struct GroupRed {
   }
 };
 
-__global__ __launch_bounds__(256) void route_select_kernel(const double* __restrict__ S, int N, int words,
-                                                           float top_p, int k_floor, uint32_t* __restrict__ mask,
+__global__ __launch_bounds__(256) void route_select_kernel(const double* __restrict__ S, int N, int words, int t0,
+                                                           int nIT, float top_p, int k_floor,
+                                                           uint32_t* __restrict__ mask,
                                                            int32_t* __restrict__ kv_cnt,
                                                            uint32_t* __restrict__ status) {
   __shared__ uint64_t red_slot[16];
   const int nwaves = blockDim.x >> 6;
   GroupRed gr{red_slot, nwaves, 0};
   const int tid = threadIdx.x;
-  const int64_t row = blockIdx.x;
-  const double* s = S + row * N;
+  const SlabRow sr = slab_row(blockIdx.x, t0, nIT, N);
+  if (sr.i >= N) return;  // padding row of a head's last tile (uniform over the workgroup)
+  const int64_t row = sr.out;
+  const double* s = S + (int64_t)blockIdx.x * N;
   const int j0 = tid * 32;
 
   double pr[32];
@@ -676,34 +704,33 @@ hipError_t launch_pool(const void* q, const void* k, const Geo& g, int B, int L,
   return hipGetLastError();
 }
 
-hipError_t launch_scores(const double* qbar, const double* kbar, int BH, int N, int D, double* S, hipStream_t st) {
-  dim3 grid((N + 63) / 64, (N + 63) / 64, BH);
-  hipLaunchKernelGGL(scores_kernel, grid, dim3(256), 0, st, qbar, kbar, N, D, S);
-  return hipGetLastError();
-}
-
-hipError_t launch_route_rows(const double* S, int64_t rows, int N, float top_p, int k_floor, uint32_t* mask,
-                             int32_t* kv_cnt, uint32_t* status, hipStream_t st) {
+hipError_t launch_route_slabs(const double* qbar, const double* kbar, int BH, int N, int D, float top_p, int k_floor,
+                              double* S, int64_t slab_tiles, uint32_t* mask, int32_t* kv_cnt, uint32_t* status,
+                              hipStream_t st) {
   const int words = (N + 31) / 32;
-  dim3 grid((unsigned)rows);
-#define FVA_ROUTE_CASE(SL, TH)                                                                                 \
-  if (N <= SL) {                                                                                               \
-    hipLaunchKernelGGL((route_rows_kernel<SL, TH>), grid, dim3(TH), 0, st, S, N, words, top_p, k_floor, mask, \
-                       kv_cnt, status);                                                                        \
-    return hipGetLastError();                                                                                  \
-  }
-  FVA_ROUTE_CASE(64, 64)
-  FVA_ROUTE_CASE(128, 64)
-  FVA_ROUTE_CASE(256, 64)
-  FVA_ROUTE_CASE(512, 64)
+  const int nIT = (N + 63) / 64;
+  const int64_t tiles = (int64_t)BH * nIT;
+  for (int64_t t0 = 0; t0 < tiles; t0 += slab_tiles) {
+    const int nt = (int)std::min<int64_t>(slab_tiles, tiles - t0);
+    hipLaunchKernelGGL(scores_kernel, dim3((N + 63) / 64, nt), dim3(256), 0, st, qbar, kbar, N, D, (int)t0, nIT, S);
+    const dim3 grid((unsigned)nt * 64);
+#define FVA_ROUTE_CASE(SL, TH)                                                                                  \
+    if (N <= SL) {                                                                                              \
+      hipLaunchKernelGGL((route_rows_kernel<SL, TH>), grid, dim3(TH), 0, st, S, N, words, (int)t0, nIT, top_p, \
+                         k_floor, mask, kv_cnt, status);                                                        \
+      continue;                                                                                                 \
+    }
+    FVA_ROUTE_CASE(64, 64)
+    FVA_ROUTE_CASE(128, 64)
+    FVA_ROUTE_CASE(256, 64)
+    FVA_ROUTE_CASE(512, 64)
 #undef FVA_ROUTE_CASE
-  if (N <= 8192) {
+    if (N > 8192) return hipErrorInvalidValue;
     const int threads = 64 * ((words + 63) / 64);
-    hipLaunchKernelGGL(route_select_kernel, grid, dim3(threads), 0, st, S, N, words, top_p, k_floor, mask, kv_cnt,
-                       status);
-    return hipGetLastError();
+    hipLaunchKernelGGL(route_select_kernel, grid, dim3(threads), 0, st, S, N, words, (int)t0, nIT, top_p, k_floor,
+                       mask, kv_cnt, status);
   }
-  return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 }  // namespace fva

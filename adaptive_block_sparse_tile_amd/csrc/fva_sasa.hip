@@ -26,17 +26,33 @@ __device__ inline bool mask_bit(const uint32_t* row, int j) { return (row[j >> 5
 
 __device__ inline int block_count(const Geo& g, int j) { return block_box(g, j).count; }
 
-// Per row (one wavefront): the row cost, the kept count, and the first R
-// dropped blocks in the router's order (-1 past the last one).
-__global__ __launch_bounds__(64) void sasa_cand_kernel(const double* __restrict__ S, const uint32_t* __restrict__ mask,
-                                                       Geo g, int words, int R, int32_t* __restrict__ cand,
+// Per row (one wavefront): the row's block scores, recomputed from the
+// router's pooled means with the router's arithmetic (an fma chain over d
+// in increasing order, then division by sqrt(D): bit-equal to the scores it
+// routed on) into LDS; the row cost, the kept count, and the first R dropped
+// blocks in the router's order (-1 past the last one).
+__global__ __launch_bounds__(64) void sasa_cand_kernel(const double* __restrict__ qbar, const double* __restrict__ kbar,
+                                                       int D, const uint32_t* __restrict__ mask, Geo g, int words,
+                                                       int R, int32_t* __restrict__ cand,
                                                        int64_t* __restrict__ row_cost,
                                                        int32_t* __restrict__ kv_cnt) {
+  extern __shared__ double s[];  // [N]
   const int64_t row = blockIdx.x;
   const int lane = threadIdx.x;
   const int N = g.N;
   const uint32_t* m = mask + row * words;
-  const double* s = S + row * N;
+  {
+    const double* qi = qbar + row * D;
+    const double* kb = kbar + (row / N) * N * D;
+    const double rs = sqrt((double)D);
+    for (int j = lane; j < N; j += 64) {
+      const double* kj = kb + (int64_t)j * D;
+      double acc = 0.0;
+      for (int d = 0; d < D; ++d) acc = fma(qi[d], kj[d], acc);
+      s[j] = acc / rs;
+    }
+    __syncthreads();
+  }
   int64_t kept_tok = 0;
   int kept = 0;
   for (int j = lane; j < N; j += 64)
@@ -198,9 +214,9 @@ __global__ __launch_bounds__(1024) void sasa_take_kernel(Geo g, int words, int R
   if (tid == 0) added[x] = taken_s;
 }
 
-hipError_t launch_sasa(const double* S, const uint32_t* mask_in, const Geo& g, int BH, int R, uint32_t* mask_out,
-                       int32_t* kv_cnt, int32_t* head_xcd, int64_t* xcd_load, int32_t* cand, int64_t* row_cost,
-                       int32_t* slot_head, int32_t* nh, hipStream_t st) {
+hipError_t launch_sasa(const double* qbar, const double* kbar, int D, const uint32_t* mask_in, const Geo& g, int BH,
+                       int R, uint32_t* mask_out, int32_t* kv_cnt, int32_t* head_xcd, int64_t* xcd_load, int32_t* cand,
+                       int64_t* row_cost, int32_t* slot_head, int32_t* nh, hipStream_t st) {
   const int words = (g.N + 31) / 32;
   const int64_t rows = (int64_t)BH * g.N;
   if (mask_out != mask_in) {
@@ -208,8 +224,8 @@ hipError_t launch_sasa(const double* S, const uint32_t* mask_in, const Geo& g, i
                                   hipMemcpyDeviceToDevice, st);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(sasa_cand_kernel, dim3((unsigned)rows), dim3(64), 0, st, S, mask_in, g, words, R, cand, row_cost,
-                     kv_cnt);
+  hipLaunchKernelGGL(sasa_cand_kernel, dim3((unsigned)rows), dim3(64), (size_t)g.N * sizeof(double), st, qbar, kbar, D,
+                     mask_in, g, words, R, cand, row_cost, kv_cnt);
   hipLaunchKernelGGL(sasa_lpt_kernel, dim3(1), dim3(256), (size_t)BH * 12, st, row_cost, g.N, BH, head_xcd, slot_head,
                      nh, xcd_load);
   hipLaunchKernelGGL(sasa_take_kernel, dim3(SASA_NXCD), dim3(1024), 0, st, g, words, R, BH, cand, slot_head, nh,

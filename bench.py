@@ -124,9 +124,15 @@ def main():
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     ms_step = total_ms / args.steps
-    route_ms = float(np.median([e[0].elapsed_time(e[1]) for e in ev]))
-    plan_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
-    kern_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+    per_stage = {"mask" if wl.static else "route": [e[0].elapsed_time(e[1]) for e in ev],
+                 "plan": [e[1].elapsed_time(e[2]) for e in ev],
+                 "kernel": [e[2].elapsed_time(e[3]) for e in ev],
+                 "layer": [e[0].elapsed_time(e[3]) for e in ev]}
+    stages = {name: {"mean": round(float(np.mean(x)), 4), "median": round(float(np.median(x)), 4),
+                     "min": round(float(np.min(x)), 4)} for name, x in per_stage.items()}
+    route_ms = float(np.median(per_stage["mask" if wl.static else "route"]))
+    plan_ms = float(np.mean(per_stage["plan"]))
+    kern_ms = float(np.mean(per_stage["kernel"]))   # the roofline uses the mean launch duration
     attn_ms = plan_ms + kern_ms
     print("[bench] timed %d steps: %.3f ms/step (route %.3f ms, attention plan %.3f ms, attention kernel %.3f ms)"
           % (args.steps, ms_step, route_ms, plan_ms, kern_ms), file=sys.stderr, flush=True)
@@ -217,6 +223,7 @@ def main():
         "attn_call_ms": round(attn_ms, 4),
         "attn_plan_ms": round(plan_ms, 4),
         "attn_kernel_ms": round(kern_ms, 4),
+        "stage_ms": stages,
         "effective_flop": eff_flop,
         "dense_equiv_tflops": round(dense_flop / (ms_step * 1e-3) / 1e12, 2),
         "kept_fraction_per_head": {"min": round(float(frac_per_head.min()), 4),
@@ -395,7 +402,7 @@ def _sasa_leg(fva, wl, q, k, v, host, shape, ws_r, ws_a, stream, args):
     items = np.array(sorted(pick))
     print("[bench] sasa: dense oracle on %d sampled items" % len(items), file=sys.stderr, flush=True)
     qh, kh, vh = host
-    threads = max(1, min(16, os.cpu_count() or 1))
+    threads = oracle.host_threads()
     dense = oracle.attn(qh, kh, vh, wl.grid, wl.block, oracle.dense_mask(B, heads, N), 1.0 / math.sqrt(D),
                         items=items, nthreads=threads)
     tb = oracle.token_block(wl.grid, wl.block)
@@ -429,16 +436,19 @@ def _sasa_leg(fva, wl, q, k, v, host, shape, ws_r, ws_a, stream, args):
 
 
 def _cpu_baseline(wl, host, mask_h, counts, n_items):
-    """The fp64 oracle, as it stands, on the host cores: the full router, plus
-    attention on a seeded sample of work items (including the heaviest and the
-    lightest).  Reported as effective TFLOP/s on that sample."""
+    """The fp64 oracle, as it stands, on the host cores this process may use
+    (its CPU affinity, capped by OMP_NUM_THREADS when set: the host's share
+    for one GPU): the full router, plus attention on a seeded sample of work
+    items (including the heaviest and the lightest).  Reported as effective
+    TFLOP/s on that sample, with the thread count, the host's hardware
+    threads and the CPU model."""
     import oracle
     q, k, v = host
     N = len(counts)
     B, heads = mask_h.shape[0], mask_h.shape[1]
-    threads = max(1, min(16, os.cpu_count() or 1))
-    print("[bench] cpu baseline: oracle router + %d attention items on %d threads" % (n_items, threads),
-          file=sys.stderr, flush=True)
+    threads = oracle.host_threads()
+    print("[bench] cpu baseline: oracle router + %d attention items on %d threads (%s, %d hardware threads)"
+          % (n_items, threads, oracle.cpu_model(), oracle.hardware_threads()), file=sys.stderr, flush=True)
     t0 = time.time()
     if wl.static:
         oracle.static_mask(wl.grid, wl.block, wl.static[0], wl.static[1], B=B, heads=heads)
@@ -461,6 +471,8 @@ def _cpu_baseline(wl, host, mask_h, counts, n_items):
         "value": round(flop / attn_s / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": threads,
+        "host_hardware_threads": oracle.hardware_threads(),
+        "cpu_model": oracle.cpu_model(),
         "kind": "oracle",
         "sample": "%d of %d work items (heaviest, lightest, seeded random), %.2f%% of the layer's effective FLOPs; "
                   "attention %.1fs, full %s %.2fs; whole layer extrapolated %.0fs"

@@ -52,7 +52,8 @@ typedef enum {
   FVA_ERR_TOPK = 3,        /* k_floor < 1 or k_floor > num_blocks */
   FVA_ERR_SCALE = 4,       /* |scale - 1/sqrt(D)| > 1e-6 */
   FVA_ERR_WORKSPACE = 5,   /* workspace null, smaller than required or not 256-byte aligned */
-  FVA_ERR_UNSUPPORTED = 6, /* D not in {64,128}; block volume > 256; num_blocks > 8192 */
+  FVA_ERR_UNSUPPORTED = 6, /* D not in {64,128}; block volume > 256; num_blocks > 8192; B*heads > 4096;
+                              a kernel grid past 2^32 threads for this shape */
   FVA_ERR_DEVICE = 7       /* a HIP runtime call failed */
 } fva_status;
 
@@ -93,8 +94,11 @@ typedef struct {
  * dimension is not positive.  Host only. */
 int32_t fva_num_blocks(const fva_grid* grid);
 
-/* Device workspace fva_route needs (pooled Q and K and the block scores,
- * fp64), or 0 for invalid arguments.  Host only. */
+/* Device workspace fva_route needs, or 0 for invalid arguments: the pooled
+ * Q and K (fp64 [B*heads, N, D] each) and one slab of fp64 block scores.
+ * The scores are computed and routed in tiles of 64 query blocks of one
+ * head, as many tiles at a time as fit 128 MiB (at least one), so the whole
+ * [B*heads, N, N] score matrix is never held.  Host only. */
 size_t fva_route_workspace_bytes(const fva_desc* desc, const fva_grid* grid);
 
 /* Device workspace fva_sparse_attn needs, or 0 for invalid arguments: the
@@ -172,8 +176,7 @@ fva_status fva_static_mask(const fva_desc* desc, const fva_grid* grid, const fva
  *            workgroup first-item start, last-item end, summed item time
  *            (100 MHz ticks) and (items << 40 | xcc_id << 32 | hw_id)
  *   ws       device workspace of at least fva_attn_workspace_bytes()
- * Errors: INVALID_ARG, SHAPE, SCALE, UNSUPPORTED (also B*heads > 4096),
- * WORKSPACE, DEVICE. */
+ * Errors: INVALID_ARG, SHAPE, SCALE, UNSUPPORTED, WORKSPACE, DEVICE. */
 fva_status fva_sparse_attn(const void* q, const void* k, const void* v, void* o, const fva_desc* desc,
                            const fva_grid* grid, const uint32_t* mask, float scale, int32_t sched, uint64_t* trace,
                            void* ws, size_t ws_bytes, void* stream);
@@ -182,11 +185,15 @@ fva_status fva_sparse_attn(const void* q, const void* k, const void* v, void* o,
  * parts.  fva_attn_plan enqueues the preparation: the block-ordered token
  * table, the 64-key chunk images of K and V, the work item costs (from mask)
  * and the schedule, all written into ws.  fva_attn_exec enqueues the
- * attention kernel that reads them.  exec must run after a plan with the same
- * desc, grid, k, v, mask and sched (same stream, or ordered after it), with
- * ws untouched in between; one plan serves one exec (the queue counters are
- * consumed).  Arguments and errors as for fva_sparse_attn; plan does not read
- * q, exec does not read k or v.  head_xcd (nullable device int32 [B*heads],
+ * attention kernel that reads them (the K and V the plan read, the Q it is
+ * given), and may run any number of times on one plan.  exec must run after
+ * the plan (same stream, or ordered after it), with ws untouched in between
+ * and with the same desc and grid; it attends over the kept blocks of the
+ * mask it is given, and the plan's mask only orders the work, so any mask
+ * gives the same O.  The plan leaves a tag of desc and grid in ws: an exec
+ * whose ws holds no plan for its desc and grid writes NaN (bf16 0x7FC0) to
+ * every element of O instead of computing it.  Arguments and errors as for
+ * fva_sparse_attn; plan does not read q, exec does not read k or v.  head_xcd (nullable device int32 [B*heads],
  * used with FVA_SCHED_XCD only): the XCD (0..7) of each (b, h), as fva_sasa
  * writes it; null assigns heads by the LPT rule.  exec must be given the
  * same sched as plan. */
@@ -238,8 +245,9 @@ fva_status fva_attn_schedule(const fva_desc* desc, const fva_grid* grid, const v
  * whose summed cost c_i * c_j fits M - load_x is added.  Run the attention
  * with FVA_SCHED_XCD and this head_xcd so that each XCD serves its own heads.
  *   mask_in    uint32 [B, heads, N, ceil(N/32)] from fva_route
- *   route_ws   the workspace of that fva_route call (it holds the block
- *              scores), untouched since
+ *   route_ws   the workspace of that fva_route call, untouched since (its
+ *              pooled Q and K; each row's scores are recomputed from them
+ *              with the router's arithmetic, bit-equal to what it routed on)
  *   rounds     0..8 (0 copies the mask)
  *   mask_out   out, same layout (may equal mask_in)
  *   kv_cnt     out, int32 [B, heads, N] kept counts after augmentation (nullable)

@@ -46,6 +46,9 @@ def test_workspace_sizes():
     r = fva.route_workspace_bytes(shape, (31, 22, 40), (4, 8, 8))
     rows = 40 * 120
     assert r >= 2 * rows * 128 * 8 + rows * 120 * 8
+    # long video: pooled means plus one score slab of 128 MiB (42 tiles of 64 x 6144 fp64), not 30720 x 6144
+    rl = fva.route_workspace_bytes((1, 393216, 5, 128), (96, 64, 64), (4, 4, 4))
+    assert rl == 2 * 5 * 6144 * 128 * 8 + 42 * 64 * 6144 * 8
     a = fva.attn_workspace_bytes(shape, (31, 22, 40), (4, 8, 8))
     assert a >= 27280 * 4 + rows * (8 + 4 + 4)
     assert fva.route_workspace_bytes((1, 27281, 40, 128), (31, 22, 40), (4, 8, 8)) == 0   # T*H*W != L
@@ -153,3 +156,62 @@ def test_attn_items_and_schedule_validation():
     assert call(ws_bytes=need - 1) == 5 and "needed" in _err()
     assert call(ws=None) == 5
     assert call(desc=bad) == 2
+
+
+def test_launch_size_limits():
+    """Shapes inside the accepted ranges whose kernel grids would pass 2^32
+    threads, or whose B*heads passes 4096, are rejected on the host."""
+    lib = fva.load()
+    grid8k = fva.make_grid((128, 64, 64), (4, 4, 4))      # 8192 blocks of 64 tokens
+    L8k = 128 * 64 * 64
+    # B*heads > 4096, for every entry point that takes a shape
+    many = fva.make_desc(1, L8k, 4097, 64)
+    assert _route(many, grid8k, fva.RouteCfg(0.9, 8), ws_bytes=1 << 62) == 6 and "B*heads = 4097" in _err()
+    assert lib.fva_static_mask(ctypes.byref(many), ctypes.byref(grid8k), ctypes.byref(fva.StaticCfg(1, 1, 1, 0)),
+                               FAKE, None, None) == 6
+    assert lib.fva_dense_attn_ref(FAKE, FAKE, FAKE, FAKE, ctypes.byref(many), ctypes.c_float(0.125), FAKE,
+                                  1 << 62, None) == 6
+    # 2048 heads of 8192 blocks: 16.7M chunk images of 256 threads; the router
+    # routes one slab of rows per launch, so it only runs out of workspace
+    wide = fva.make_desc(1, L8k, 2048, 64)
+    assert lib.fva_sparse_attn(FAKE, FAKE, FAKE, FAKE, ctypes.byref(wide), ctypes.byref(grid8k), FAKE, 0.125, 0,
+                               None, FAKE, 1 << 62, None) == 6 and "chunk tiling" in _err()
+    assert _route(wide, grid8k, fva.RouteCfg(0.9, 8), ws_bytes=16) == 5
+    # one fewer head fits the tiling launch (it then fails only on the workspace size)
+    ok = fva.make_desc(1, L8k, 2047, 64)
+    assert lib.fva_sparse_attn(FAKE, FAKE, FAKE, FAKE, ctypes.byref(ok), ctypes.byref(grid8k), FAKE, 0.125, 0,
+                               None, FAKE, 16, None) == 5
+    # dense reference: 4096 heads of 2^24 - 1 tokens is 1.07e9 chunk images
+    long_desc = fva.make_desc(1, (1 << 24) - 1, 4096, 64)
+    assert lib.fva_dense_attn_ref(FAKE, FAKE, FAKE, FAKE, ctypes.byref(long_desc), ctypes.c_float(0.125), FAKE,
+                                  1 << 62, None) == 6
+
+
+def test_binding_allocates_on_the_call_stream(monkeypatch):
+    """The binding runs each call with its `stream` as torch's current stream
+    (so outputs and the temporary workspace belong to the stream the kernels
+    use); without a stream it leaves the current stream alone."""
+    import contextlib
+    import types
+
+    entered = []
+
+    @contextlib.contextmanager
+    def fake_stream(s):
+        entered.append(s)
+        yield
+
+    fake = types.SimpleNamespace(cuda=types.SimpleNamespace(stream=fake_stream))
+    monkeypatch.setattr(fva, "_torch", lambda: fake)
+
+    @fva._on_stream
+    def call(a, b=None, stream=None):
+        return (a, b, list(entered))
+
+    assert call(1) == (1, None, [])
+    assert call(1, 2, "side") == (1, 2, ["side"])
+    assert call(1, stream="other") == (1, None, ["side", "other"])
+    for name in ("route", "sparse_attn", "static_mask", "attn_plan", "attn_exec", "attn_schedule", "sasa",
+                 "dense_attn_ref"):
+        assert getattr(fva, name).__wrapped__ is not None, name
+
