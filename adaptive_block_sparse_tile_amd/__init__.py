@@ -22,6 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libfva.so")
 FVA_OK = 0
 STATUS_NAMES = ["FVA_OK", "FVA_ERR_INVALID_ARG", "FVA_ERR_SHAPE", "FVA_ERR_TOPK", "FVA_ERR_SCALE",
                 "FVA_ERR_WORKSPACE", "FVA_ERR_UNSUPPORTED", "FVA_ERR_DEVICE"]
+ROUTE_SCRATCH_BYTES = 128 << 20   # FVA_ROUTE_SCRATCH_BYTES: the static scratch of fva_route_noalloc per GPU
 SCHED_LPT = 0
 SCHED_NAIVE = 1
 SCHED_XCD = 2
@@ -29,7 +30,7 @@ SCHEDS = {"lpt": SCHED_LPT, "naive": SCHED_NAIVE, "xcd": SCHED_XCD}
 
 # every symbol include/fva.h declares
 EXPORTS = ["fva_num_blocks", "fva_route_workspace_bytes", "fva_attn_workspace_bytes", "fva_attn_workgroups",
-           "fva_route", "fva_static_mask", "fva_sparse_attn", "fva_attn_plan", "fva_attn_exec", "fva_attn_items",
+           "fva_route", "fva_route_noalloc", "fva_static_mask", "fva_sparse_attn", "fva_attn_plan", "fva_attn_exec", "fva_attn_items",
            "fva_attn_schedule", "fva_sasa_workspace_bytes", "fva_sasa",
            "fva_dense_workspace_bytes", "fva_dense_attn_ref",
            "fva_trace_imbalance", "fva_last_error", "fva_status_name"]
@@ -82,6 +83,8 @@ def load():
     lib.fva_attn_workgroups.argtypes = [D, G]
     lib.fva_route.restype = ctypes.c_int
     lib.fva_route.argtypes = [_P, _P, D, G, C, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.fva_route_noalloc.restype = ctypes.c_int
+    lib.fva_route_noalloc.argtypes = [_P, _P, D, G, C, _P, _P, _P, _P]
     lib.fva_static_mask.restype = ctypes.c_int
     lib.fva_static_mask.argtypes = [D, G, ctypes.POINTER(StaticCfg), _P, _P, _P]
     lib.fva_sparse_attn.restype = ctypes.c_int
@@ -212,6 +215,27 @@ def route(q, k, grid, block, top_p: float, k_floor: int, ws=None, out=None, stre
                             ctypes.byref(make_grid(grid, block)), ctypes.byref(RouteCfg(float(top_p), int(k_floor))),
                             mask.data_ptr(), cnt.data_ptr(), status.data_ptr(), ws.data_ptr(), ws.numel(),
                             _stream_ptr(stream)))
+    return mask, cnt, status
+
+
+@_on_stream
+def route_noalloc(q, k, grid, block, top_p: float, k_floor: int, out=None, stream=None):
+    """The router on the library's static scratch (fva_route_noalloc: no
+    workspace, no device allocation inside the call; outputs are allocated
+    here unless `out` gives them) -> (mask, kv_cnt, status) as route()."""
+    torch = _torch()
+    shape = _check_qkv(q, k)
+    B, L, heads, D = shape
+    N = num_blocks(grid, block)
+    if out is None:
+        out = (torch.empty((B, heads, N, (N + 31) // 32), dtype=torch.int32, device=q.device),
+               torch.empty((B, heads, N), dtype=torch.int32, device=q.device),
+               torch.empty((1,), dtype=torch.int32, device=q.device))
+    mask, cnt, status = out
+    _check(load().fva_route_noalloc(q.data_ptr(), k.data_ptr(), ctypes.byref(make_desc(*shape)),
+                                    ctypes.byref(make_grid(grid, block)),
+                                    ctypes.byref(RouteCfg(float(top_p), int(k_floor))), mask.data_ptr(),
+                                    cnt.data_ptr(), status.data_ptr(), _stream_ptr(stream)))
     return mask, cnt, status
 
 

@@ -254,6 +254,25 @@ fva_status fva_route(const void* q, const void* k, const fva_desc* desc, const f
   return route_launch(q, k, desc, g, cfg, lay, mask, kv_cnt, status, ws, stream);
 }
 
+fva_status fva_route_noalloc(const void* q, const void* k, const fva_desc* desc, const fva_grid* grid,
+                             const fva_route_cfg* cfg, uint32_t* mask, int32_t* kv_cnt, uint32_t* status,
+                             void* stream) {
+  fva::Geo g;
+  RouteWs one;
+  fva_status st = route_check(q, k, desc, grid, cfg, mask, 0, &g, &one);
+  if (st != FVA_OK) return st;
+  // the pooled means must fit with room for at least one tile of scores
+  if (one.total > fva::kRouteScratchBytes)
+    return fail(FVA_ERR_UNSUPPORTED, "the router needs %zu bytes of scratch for this shape, more than the %zu of "
+                "the static scratch (use fva_route with a workspace)", one.total, fva::kRouteScratchBytes);
+  RouteWs lay;
+  if ((st = route_check(q, k, desc, grid, cfg, mask, fva::kRouteScratchBytes - one.s, &g, &lay)) != FVA_OK) return st;
+  void* scratch = nullptr;
+  const hipError_t e = fva::route_scratch(&scratch);
+  if (e != hipSuccess) return device_error(e, "static scratch lookup");
+  return route_launch(q, k, desc, g, cfg, lay, mask, kv_cnt, status, scratch, stream);
+}
+
 // Shared validation and workspace views of the sparse attention calls.
 static fva_status sparse_setup(const void* q, const void* k, const void* v, void* o, bool need_q, bool need_kv,
                                const fva_desc* desc, const fva_grid* grid, const uint32_t* mask, float scale,

@@ -11,6 +11,10 @@ namespace fva {
 // Router (fva_route.hip)
 hipError_t launch_pool(const void* q, const void* k, const Geo& g, int B, int L, int heads, int D, double* qbar,
                        double* kbar, uint32_t* status, hipStream_t st);
+// Bytes of the router's static scratch on each GPU, and its device address
+// on the current device (looked up on the first call per device).
+constexpr size_t kRouteScratchBytes = (size_t)128 << 20;
+hipError_t route_scratch(void** ptr);
 // Scores and row routing slab by slab: the query rows of every head are cut
 // into tiles of 64 query blocks, and slab_tiles tiles at a time get their
 // fp64 scores in S ([slab_tiles * 64][N]) and are routed from there.

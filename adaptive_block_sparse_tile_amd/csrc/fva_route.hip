@@ -17,6 +17,7 @@
 //   route_select_kernel N > 512: the same decisions by bisection on
 //                      order-preserving keys (no full sort)
 #include <algorithm>
+#include <mutex>
 
 #include "fva_dev.h"
 #include "fva_kernels.h"
@@ -702,6 +703,36 @@ hipError_t launch_pool(const void* q, const void* k, const Geo& g, int B, int L,
   hipLaunchKernelGGL(pool_kernel, grid, dim3(256), 0, st, (const bf16_bits*)q, (const bf16_bits*)k, g, L, heads, D,
                      chunks, qbar, kbar, status);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Static scratch of the allocation-free router entry point: the pooled means
+// and one score slab live in this file-scope array (one copy per GPU, held
+// until the process ends) instead of in a caller's workspace.  Host code
+// never passes the array's name to a kernel or a copy: it uses the device
+// address hipGetSymbolAddress returns for the current device, looked up once
+// per device on its first use and kept.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[kRouteScratchBytes];
+
+hipError_t route_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_route_slabs(const double* qbar, const double* kbar, int BH, int N, int D, float top_p, int k_floor,

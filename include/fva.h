@@ -131,6 +131,26 @@ fva_status fva_route(const void* q, const void* k, const fva_desc* desc, const f
                      const fva_route_cfg* cfg, uint32_t* mask, int32_t* kv_cnt, uint32_t* status, void* ws,
                      size_t ws_bytes, void* stream);
 
+/* fva_route for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.  It
+ * takes no workspace: the pooled Q and K and the score slab live in a static
+ * scratch array of FVA_ROUTE_SCRATCH_BYTES that the library holds on every
+ * GPU it runs on until the process ends; the call makes no allocation (the
+ * scratch's device address is looked up once per device, on the first call
+ * there).  Same arguments, results and errors as fva_route, plus
+ * FVA_ERR_UNSUPPORTED when the pooled means of this shape,
+ * 2 * B*heads*N*D*8 bytes, leave no room in the scratch for one tile of 64
+ * score rows (64*N*8 bytes); the long-video shape (5 heads, 6144 blocks,
+ * D = 128) takes 60 MiB of pooled means.  Calls on one GPU share its
+ * scratch: calls that overlap in time on one GPU (other streams, other host
+ * threads) race and must be serialised by the caller.  Nothing in the
+ * scratch needs clearing between calls: every value read is written first
+ * by the same call. */
+#define FVA_ROUTE_SCRATCH_BYTES ((size_t)128 << 20)
+fva_status fva_route_noalloc(const void* q, const void* k, const fva_desc* desc, const fva_grid* grid,
+                             const fva_route_cfg* cfg, uint32_t* mask, int32_t* kv_cnt, uint32_t* status,
+                             void* stream);
+
 /* Static block mask: a second source of masks for fva_sparse_attn besides
  * the router (Sol-Attn article, section 3: tokens attend in full inside
  * their local window, and anchors link every window; here both rules act on

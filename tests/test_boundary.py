@@ -215,3 +215,23 @@ def test_binding_allocates_on_the_call_stream(monkeypatch):
                  "dense_attn_ref"):
         assert getattr(fva, name).__wrapped__ is not None, name
 
+
+def test_route_noalloc_host_validation():
+    """The allocation-free router rejects on the host, before any device call,
+    what fva_route rejects, and shapes whose pooled means leave no room for
+    one tile of scores in its static scratch."""
+    lib = fva.load()
+
+    def call(desc, grid, cfg, mask=FAKE):
+        return lib.fva_route_noalloc(FAKE, FAKE, ctypes.byref(desc), ctypes.byref(grid), ctypes.byref(cfg), mask,
+                                     None, None, None)
+    desc = fva.make_desc(1, 27280, 40, 128)
+    grid = fva.make_grid((31, 22, 40), (4, 8, 8))
+    assert call(desc, grid, fva.RouteCfg(0.9, 130)) == 3 and _err() == "k_floor 130 > num_blocks 120"
+    assert call(desc, grid, fva.RouteCfg(0.9, 8), mask=None) == 1
+    assert call(fva.make_desc(1, 27281, 40, 128), grid, fva.RouteCfg(0.9, 8)) == 2
+    # 40 heads of 6144 blocks: 2 * 40 * 6144 * 128 * 8 bytes of pooled means > 128 MiB
+    big = fva.make_desc(1, 393216, 40, 128)
+    assert call(big, fva.make_grid((96, 64, 64), (4, 4, 4)), fva.RouteCfg(0.85, 32)) == 6
+    assert "static scratch" in _err()
+    assert fva.ROUTE_SCRATCH_BYTES == 128 << 20
