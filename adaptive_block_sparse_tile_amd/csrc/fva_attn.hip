@@ -42,7 +42,6 @@ namespace fva {
 
 constexpr int KCH = 64;     // keys per chunk
 constexpr int STAGES = 4;   // LDS ring depth
-constexpr int MAX_WORDS = 256;  // mask words per row (8192 blocks)
 constexpr int NXCD = 8;     // XCDs of an MI355X
 
 // A chunk of 64 keys, in LDS and in the tiled copy in HBM alike (the copy
@@ -306,15 +305,19 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) bf16_bits ring1[Lds<D>::ELEMS];
   __shared__ __attribute__((aligned(16))) bf16_bits ring2[Lds<D>::ELEMS];
   __shared__ __attribute__((aligned(16))) bf16_bits ring3[Lds<D>::ELEMS];
-  // the item's mask: the union of its members' rows, and (groups) each
-  // member's own row
-  __shared__ uint32_t umask[DENSE ? 1 : MAX_WORDS];
-  __shared__ uint32_t gmask[GRP ? 4 : 1][GRP ? MAX_WORDS : 1];
   __shared__ int item_s;
-  // real tokens of every block, read by the chunk walk at each block change
-  // (a table lookup instead of the three integer divisions of the block's
-  // geometry, which cost the walk some 80 scalar instructions per block)
-  __shared__ uint16_t cnt_s[DENSE ? 1 : MAX_WORDS * 32];
+  // Tables sized by the launch (dynamic LDS, sparse_lds_bytes): the item's
+  // mask, i.e. the union of its members' rows (umask, `words` words) and,
+  // for groups, each member's own row (gmask, 4 x `words`), and the real
+  // tokens of every block (cnt_s, N entries), read by the chunk walk at each
+  // block change (a table lookup instead of the three integer divisions of
+  // the block's geometry, which cost the walk some 80 scalar instructions
+  // per block).  Sized by N rather than by the largest grid, they leave the
+  // rest of the CU's LDS to kernels of other streams.
+  extern __shared__ __attribute__((aligned(16))) uint32_t dyn_lds[];
+  uint32_t* umask = dyn_lds;
+  uint32_t* gmask = dyn_lds + p.words;  // member k's row at gmask + k * words
+  uint16_t* cnt_s = (uint16_t*)(dyn_lds + (GRP ? 5 : 1) * p.words);
   static_assert(STAGES == 4, "four ring stages");
   auto stage = [&](int sidx) -> bf16_bits* {
     return sidx == 0 ? ring0 : (sidx == 1 ? ring1 : (sidx == 2 ? ring2 : ring3));
@@ -386,7 +389,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
         for (int k = 0; k < 4; ++k) {
           const int n = k < ng ? group_member(p, gid, k) : -1;
           const uint32_t x = n >= 0 ? p.mask[((int64_t)bhg * p.g.N + n) * p.words + wi] : 0u;
-          gmask[k][wi] = x;
+          gmask[k * p.words + wi] = x;
           u |= x;
         }
         const int rem = p.g.N - wi * 32;
@@ -542,7 +545,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
     auto seen = [&](const Chunk& ck) -> int {
       if (!GRP) return ck.valid;  // a single member: the union is its own row
       if (mine < 0) return 0;
-      return ((gmask[mine][ck.blk >> 5] >> (ck.blk & 31)) & 1u) ? ck.valid : 0;
+      return ((gmask[mine * p.words + (ck.blk >> 5)] >> (ck.blk & 31)) & 1u) ? ck.valid : 0;
     };
     // chunks arrive by direct loads three chunks ahead of the one being computed
     constexpr int LOOK = 3;
@@ -1233,6 +1236,13 @@ static const void* sparse_kernel(int D, bool grouped) {
                  : reinterpret_cast<const void*>(&attn_kernel<64, WAVES, 1, false, false>);
 }
 
+// Dynamic LDS of the sparse kernel: mask words of the item's union (and of
+// its 4 members for groups), then the real token count of every block.
+static size_t sparse_lds_bytes(int N, bool grouped) {
+  const size_t words = (size_t)(N + 31) / 32;
+  return ((grouped ? 5 : 1) * words * 4 + (size_t)N * 2 + 15) / 16 * 16;
+}
+
 int attn_persistent_workgroups(int D, int block_volume, int* err) {
   int dev = 0, cus = 0, occ = 0;
   *err = 0;
@@ -1329,7 +1339,9 @@ hipError_t launch_sparse_exec(const AttnLaunch& a, int sched, hipStream_t st) {
   if (err) return hipErrorInvalidValue;
   hipLaunchKernelGGL(queue_reset_kernel, dim3(1), dim3(64), 0, st, a.qctr);
   void* args[] = {&prm};
-  return hipLaunchKernel(sparse_kernel(a.D, group_shape(vol).wpb < WAVES), dim3(grid), dim3(WAVES * 64), args, 0, st);
+  const bool grouped = group_shape(vol).wpb < WAVES;
+  return hipLaunchKernel(sparse_kernel(a.D, grouped), dim3(grid), dim3(WAVES * 64), args,
+                         sparse_lds_bytes(a.g.N, grouped), st);
 }
 
 // The dense reference: the whole sequence as one block of L tokens, tiled in
