@@ -17,7 +17,8 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libfva.so")
+# FVA_LIB: another build of the same sources (the host-sanitizer build of the tests)
+LIB_PATH = os.environ.get("FVA_LIB") or os.path.join(_HERE, "libfva.so")
 
 FVA_OK = 0
 STATUS_NAMES = ["FVA_OK", "FVA_ERR_INVALID_ARG", "FVA_ERR_SHAPE", "FVA_ERR_TOPK", "FVA_ERR_SCALE",

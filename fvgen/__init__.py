@@ -44,9 +44,10 @@ _lib = None
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
+        override = os.environ.get("FVGEN_LIB")   # another build of the same source (e.g. with sanitizers)
+        if not override and not os.path.exists(_LIB):
             build()
-        lib = ctypes.CDLL(_LIB)
+        lib = ctypes.CDLL(override or _LIB)
         lib.fvgen_qkv.restype = ctypes.c_int
         lib.fvgen_qkv.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double),

@@ -36,9 +36,10 @@ _P = ctypes.c_void_p
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
+        override = os.environ.get("FVO_LIB")   # another build of the same source (e.g. with sanitizers)
+        if not override and not os.path.exists(_LIB):
             build()
-        lib = ctypes.CDLL(_LIB)
+        lib = ctypes.CDLL(override or _LIB)
         lib.fvo_num_blocks.restype = ctypes.c_int
         lib.fvo_num_blocks.argtypes = [_P]
         lib.fvo_block_table.restype = ctypes.c_int
