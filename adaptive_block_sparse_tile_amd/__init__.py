@@ -31,7 +31,7 @@ SCHEDS = {"lpt": SCHED_LPT, "naive": SCHED_NAIVE, "xcd": SCHED_XCD}
 
 # every symbol include/fva.h declares
 EXPORTS = ["fva_num_blocks", "fva_route_workspace_bytes", "fva_attn_workspace_bytes", "fva_attn_workgroups",
-           "fva_route", "fva_route_noalloc", "fva_static_mask", "fva_sparse_attn", "fva_attn_plan", "fva_attn_exec", "fva_attn_items",
+           "fva_route", "fva_route_noalloc", "fva_static_mask", "fva_sparse_attn", "fva_attn_plan", "fva_attn_exec", "fva_routed_attn_workspace_bytes", "fva_routed_attn", "fva_attn_items",
            "fva_attn_schedule", "fva_sasa_workspace_bytes", "fva_sasa",
            "fva_dense_workspace_bytes", "fva_dense_attn_ref",
            "fva_trace_imbalance", "fva_last_error", "fva_status_name"]
@@ -95,6 +95,11 @@ def load():
     lib.fva_attn_plan.argtypes = [_P, _P, D, G, _P, ctypes.c_int32, _P, _P, ctypes.c_size_t, _P]
     lib.fva_attn_exec.restype = ctypes.c_int
     lib.fva_attn_exec.argtypes = [_P, _P, D, G, _P, ctypes.c_float, ctypes.c_int32, _P, _P, ctypes.c_size_t, _P]
+    lib.fva_routed_attn_workspace_bytes.restype = ctypes.c_size_t
+    lib.fva_routed_attn_workspace_bytes.argtypes = [D, G, ctypes.c_int32]
+    lib.fva_routed_attn.restype = ctypes.c_int
+    lib.fva_routed_attn.argtypes = [_P, _P, _P, _P, D, G, C, ctypes.c_float, ctypes.c_int32, _P, _P, _P, _P,
+                                    ctypes.c_size_t, _P, _P]
     lib.fva_attn_items.restype = ctypes.c_int32
     lib.fva_attn_items.argtypes = [D, G]
     lib.fva_attn_schedule.restype = ctypes.c_int
@@ -313,6 +318,41 @@ def attn_exec(q, grid, block, mask, ws, scale=None, sched: str = "lpt", trace=No
                                 ctypes.byref(make_grid(grid, block)), mask.data_ptr(), float(scale), SCHEDS[sched],
                                 tp, ws.data_ptr(), ws.numel(), _stream_ptr(stream)))
     return o
+
+
+def routed_attn_workspace_bytes(shape, grid, block, groups=1) -> int:
+    return int(load().fva_routed_attn_workspace_bytes(ctypes.byref(make_desc(*shape)),
+                                                      ctypes.byref(make_grid(grid, block)), int(groups)))
+
+
+@_on_stream
+def routed_attn(q, k, v, grid, block, top_p: float, k_floor: int, groups: int = 1, side_stream=None, scale=None,
+                ws=None, out=None, stream=None):
+    """The whole layer (fva_routed_attn): routing, then sparse attention on
+    its mask, pipelined over `groups` head groups alternating between the
+    current stream and `side_stream` -> (o, mask, kv_cnt, status)."""
+    torch = _torch()
+    shape = _check_qkv(q, k, v)
+    B, L, heads, D = shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    N = num_blocks(grid, block)
+    if out is None:
+        out = (torch.empty_like(q), torch.empty((B, heads, N, (N + 31) // 32), dtype=torch.int32, device=q.device),
+               torch.empty((B, heads, N), dtype=torch.int32, device=q.device),
+               torch.empty((1,), dtype=torch.int32, device=q.device))
+    o, mask, cnt, status = out
+    if ws is None:
+        ws = workspace(routed_attn_workspace_bytes(shape, grid, block, groups), q.device)
+    side = ctypes.c_void_p(side_stream.cuda_stream) if side_stream is not None else None
+    if side_stream is not None:
+        ws.record_stream(side_stream)     # the side stream's kernels use the workspace too
+    _check(load().fva_routed_attn(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                  ctypes.byref(make_desc(*shape)), ctypes.byref(make_grid(grid, block)),
+                                  ctypes.byref(RouteCfg(float(top_p), int(k_floor))), float(scale), int(groups),
+                                  mask.data_ptr(), cnt.data_ptr(), status.data_ptr(), ws.data_ptr(), ws.numel(),
+                                  _stream_ptr(stream), side))
+    return o, mask, cnt, status
 
 
 def attn_items(shape, grid, block) -> int:

@@ -226,20 +226,29 @@ static fva_status route_check(const void* q, const void* k, const fva_desc* desc
   return FVA_OK;
 }
 
-// The router's launches on a validated call, its workspace at ws.
+// The router's launches on a validated call for the heads hd selects, its
+// workspace at ws: the pooling (which zeroes *status first if clear_status)
+// and then the slabs of scores and row routing (route_slabs false: only the
+// pooling).
 static fva_status route_launch(const void* q, const void* k, const fva_desc* desc, const fva::Geo& g,
                                const fva_route_cfg* cfg, const RouteWs& lay, uint32_t* mask, int32_t* kv_cnt,
-                               uint32_t* status, void* ws, void* stream) {
+                               uint32_t* status, void* ws, void* stream, const fva::Heads& hd,
+                               bool clear_status = true, bool pool = true, bool route_slabs = true) {
   hipStream_t s = (hipStream_t)stream;
   char* w = (char*)ws;
   double* qbar = (double*)(w + lay.qbar);
   double* kbar = (double*)(w + lay.kbar);
   double* S = (double*)(w + lay.s);
-  hipError_t e = fva::launch_pool(q, k, g, desc->B, desc->L, desc->heads, desc->D, qbar, kbar, status, s);
-  if (e != hipSuccess) return device_error(e, "pool kernel launch");
-  e = fva::launch_route_slabs(qbar, kbar, desc->B * desc->heads, g.N, desc->D, cfg->top_p, cfg->k_floor, S,
-                              lay.slab_tiles, mask, kv_cnt, status, s);
-  if (e != hipSuccess) return device_error(e, "router launch");
+  hipError_t e = hipSuccess;
+  if (pool) {
+    e = fva::launch_pool(q, k, g, desc->B, desc->L, hd, desc->D, qbar, kbar, status, clear_status, s);
+    if (e != hipSuccess) return device_error(e, "pool kernel launch");
+  }
+  if (route_slabs) {
+    e = fva::launch_route_slabs(qbar, kbar, desc->B, hd, g.N, desc->D, cfg->top_p, cfg->k_floor, S, lay.slab_tiles,
+                                mask, kv_cnt, status, s);
+    if (e != hipSuccess) return device_error(e, "router launch");
+  }
   return ok();
 }
 
@@ -251,7 +260,8 @@ fva_status fva_route(const void* q, const void* k, const fva_desc* desc, const f
   fva_status st = route_check(q, k, desc, grid, cfg, mask, kScoreSlabBytes, &g, &lay);
   if (st != FVA_OK) return st;
   if ((st = check_ws(ws, ws_bytes, lay.total)) != FVA_OK) return st;
-  return route_launch(q, k, desc, g, cfg, lay, mask, kv_cnt, status, ws, stream);
+  return route_launch(q, k, desc, g, cfg, lay, mask, kv_cnt, status, ws, stream,
+                      fva::Heads{desc->heads, 0, desc->heads});
 }
 
 fva_status fva_route_noalloc(const void* q, const void* k, const fva_desc* desc, const fva_grid* grid,
@@ -270,7 +280,8 @@ fva_status fva_route_noalloc(const void* q, const void* k, const fva_desc* desc,
   void* scratch = nullptr;
   const hipError_t e = fva::route_scratch(&scratch);
   if (e != hipSuccess) return device_error(e, "static scratch lookup");
-  return route_launch(q, k, desc, g, cfg, lay, mask, kv_cnt, status, scratch, stream);
+  return route_launch(q, k, desc, g, cfg, lay, mask, kv_cnt, status, scratch, stream,
+                      fva::Heads{desc->heads, 0, desc->heads});
 }
 
 // Shared validation and workspace views of the sparse attention calls.
@@ -298,6 +309,7 @@ static fva_status sparse_setup(const void* q, const void* k, const void* v, void
   char* w = (char*)ws;
   a->q = q; a->k = k; a->v = v; a->o = o;
   a->B = desc->B; a->L = desc->L; a->heads = desc->heads; a->D = desc->D;
+  a->hd = fva::Heads{desc->heads, 0, desc->heads};
   a->g = g;
   a->mask = mask;
   a->scale = scale;
@@ -319,13 +331,17 @@ static fva_status sparse_setup(const void* q, const void* k, const void* v, void
 // SASA workspace: per-row candidates int32 [rows][rounds], per-row costs
 // int64 [rows], heads per XCD int32 [8][BH], head counts int32 [8].
 struct SasaWs {
-  size_t cand, cost, slot, nh, total;
+  size_t s, cand, cost, slot, nh, total;
+  int64_t slab_tiles;
 };
 static SasaWs sasa_ws_layout(const fva_desc* d, const fva::Geo& g, int rounds) {
   SasaWs w;
   const size_t BH = (size_t)d->B * d->heads;
   const size_t rows = BH * g.N;
+  const RouteWs rl = route_ws_layout(d, g);  // the same slab of scores as the router's
+  w.slab_tiles = rl.slab_tiles;
   size_t off = 0;
+  w.s = off; off += rl.total - rl.s;
   w.cand = off; off += align_up(rows * (size_t)std::max(rounds, 1) * sizeof(int32_t));
   w.cost = off; off += align_up(rows * sizeof(int64_t));
   w.slot = off; off += align_up(8 * BH * sizeof(int32_t));
@@ -361,8 +377,8 @@ fva_status fva_sasa(const fva_desc* desc, const fva_grid* grid, const uint32_t* 
   char* w = (char*)ws;
   const double* qbar = (const double*)((const char*)route_ws + rl.qbar);
   const double* kbar = (const double*)((const char*)route_ws + rl.kbar);
-  hipError_t e = fva::launch_sasa(qbar, kbar, desc->D, mask_in, g, desc->B * desc->heads, rounds, mask_out, kv_cnt,
-                                  head_xcd, xcd_load,
+  hipError_t e = fva::launch_sasa(qbar, kbar, desc->D, mask_in, g, desc->B * desc->heads, rounds,
+                                  (double*)(w + lay.s), lay.slab_tiles, mask_out, kv_cnt, head_xcd, xcd_load,
                                   (int32_t*)(w + lay.cand), (int64_t*)(w + lay.cost), (int32_t*)(w + lay.slot),
                                   (int32_t*)(w + lay.nh), (hipStream_t)stream);
   if (e != hipSuccess) return device_error(e, "sasa launch");
@@ -424,6 +440,101 @@ fva_status fva_attn_exec(const void* q, void* o, const fva_desc* desc, const fva
   a.trace = trace;
   hipError_t e = fva::launch_sparse_exec(a, sched, (hipStream_t)stream);
   if (e != hipSuccess) return device_error(e, "sparse attention launch");
+  return ok();
+}
+
+// Whole layer over head groups: group g holds heads [g*heads/G, (g+1)*heads/G).
+static int group_first_head(int heads, int groups, int g) { return (int)((int64_t)g * heads / groups); }
+
+// Workspace of one stream of fva_routed_attn: a router and an attention
+// workspace sized for the largest group, back to back.
+struct LayerWs {
+  RouteWs route;
+  AttnWs attn;
+  size_t one;  // bytes of one stream's set
+};
+static LayerWs layer_ws_layout(const fva_desc* desc, const fva::Geo& g, int groups) {
+  fva_desc dmax = *desc;
+  dmax.heads = (desc->heads + groups - 1) / groups;
+  LayerWs w;
+  w.route = route_ws_layout(&dmax, g);
+  w.attn = attn_ws_layout(&dmax, g);
+  w.one = w.route.total + w.attn.total;
+  return w;
+}
+
+size_t fva_routed_attn_workspace_bytes(const fva_desc* desc, const fva_grid* grid, int32_t groups) {
+  fva::Geo g;
+  if (check_desc(desc) != FVA_OK || check_grid(desc, grid, &g) != FVA_OK || groups < 1 || groups > desc->heads)
+    return 0;
+  return (groups > 1 ? 2 : 1) * layer_ws_layout(desc, g, groups).one;
+}
+
+fva_status fva_routed_attn(const void* q, const void* k, const void* v, void* o, const fva_desc* desc,
+                           const fva_grid* grid, const fva_route_cfg* cfg, float scale, int32_t groups,
+                           uint32_t* mask, int32_t* kv_cnt, uint32_t* status, void* ws, size_t ws_bytes,
+                           void* stream, void* side_stream) {
+  if (!v || !o) return fail(FVA_ERR_INVALID_ARG, "tensor pointers must not be null");
+  fva::Geo g;
+  RouteWs whole;
+  fva_status st = route_check(q, k, desc, grid, cfg, mask, kScoreSlabBytes, &g, &whole);
+  if (st != FVA_OK) return st;
+  if ((st = check_scale(desc->D, scale)) != FVA_OK) return st;
+  if (groups < 1 || groups > desc->heads)
+    return fail(FVA_ERR_INVALID_ARG, "groups %d outside 1..heads (%d)", groups, desc->heads);
+  const LayerWs lay = layer_ws_layout(desc, g, groups);
+  const hipStream_t s0 = (hipStream_t)stream;
+  const hipStream_t s1 = (groups > 1 && side_stream && side_stream != stream) ? (hipStream_t)side_stream : s0;
+  const int sets = s1 != s0 ? 2 : 1;
+  if ((st = check_ws(ws, ws_bytes, (size_t)sets * lay.one)) != FVA_OK) return st;
+  // every group is validated before anything is enqueued
+  std::vector<fva::AttnLaunch> al(groups);
+  std::vector<fva_desc> dg(groups, *desc);
+  for (int gi = 0; gi < groups; ++gi) {
+    const int hb = group_first_head(desc->heads, groups, gi), he = group_first_head(desc->heads, groups, gi + 1);
+    dg[gi].heads = he - hb;
+    char* base = (char*)ws + (size_t)(sets == 2 ? gi % 2 : 0) * lay.one;
+    if ((st = check_route_launches(&dg[gi], g, lay.route.slab_tiles)) != FVA_OK) return st;
+    if ((st = sparse_setup(q, k, v, o, true, true, &dg[gi], grid, mask, scale, true, FVA_SCHED_LPT,
+                           base + lay.route.total, lay.attn.total, &al[gi])) != FVA_OK)
+      return st;
+    al[gi].hd = fva::Heads{he - hb, hb, desc->heads};
+  }
+  hipError_t e = hipSuccess;
+  for (int gi = 0; gi < groups; ++gi) {
+    const hipStream_t s = gi % 2 ? s1 : s0;
+    char* base = (char*)ws + (size_t)(sets == 2 ? gi % 2 : 0) * lay.one;
+    const fva::Heads hd = al[gi].hd;
+    // group 0's pooling zeroes the status word, before the side stream joins
+    if ((st = route_launch(q, k, &dg[gi], g, cfg, lay.route, mask, kv_cnt, status, base, s, hd, gi == 0, true,
+                           false)) != FVA_OK)
+      return st;
+    if (gi == 0 && s1 != s0) {
+      // the side stream starts after the caller's earlier work on stream and this clear
+      hipEvent_t ev;
+      if ((e = hipEventCreateWithFlags(&ev, hipEventDisableTiming)) != hipSuccess) return device_error(e, "event");
+      e = hipEventRecord(ev, s0);
+      if (e == hipSuccess) e = hipStreamWaitEvent(s1, ev, 0);
+      hipEventDestroy(ev);
+      if (e != hipSuccess) return device_error(e, "stream fork");
+    }
+    if ((st = route_launch(q, k, &dg[gi], g, cfg, lay.route, mask, kv_cnt, status, base, s, hd, false, false,
+                           true)) != FVA_OK)
+      return st;
+    if ((e = fva::launch_sparse_plan(al[gi], FVA_SCHED_LPT, nullptr, s)) != hipSuccess)
+      return device_error(e, "sparse attention plan launch");
+    if ((e = fva::launch_sparse_exec(al[gi], FVA_SCHED_LPT, s)) != hipSuccess)
+      return device_error(e, "sparse attention launch");
+  }
+  if (s1 != s0) {
+    // stream resumes after everything enqueued on the side stream
+    hipEvent_t ev;
+    if ((e = hipEventCreateWithFlags(&ev, hipEventDisableTiming)) != hipSuccess) return device_error(e, "event");
+    e = hipEventRecord(ev, s1);
+    if (e == hipSuccess) e = hipStreamWaitEvent(s0, ev, 0);
+    hipEventDestroy(ev);
+    if (e != hipSuccess) return device_error(e, "stream join");
+  }
   return ok();
 }
 

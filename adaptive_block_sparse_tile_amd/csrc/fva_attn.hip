@@ -74,7 +74,8 @@ struct AttnParams {
   const bf16_bits* k;
   const bf16_bits* v;
   bf16_bits* o;
-  int B, L, heads;
+  int B, L, heads;  // heads: the launch's own heads (hd.n)
+  Heads hd;         // which heads of the tensors, masks and counts they are
   Geo g;
   int words, cpb;          // mask words per row; chunk slots per block
   const uint32_t* mask;
@@ -334,8 +335,10 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
     // NaN (grid-stride over the persistent workgroups) rather than output
     // computed from mismatched tables
     const int64_t n = (int64_t)p.B * p.L * p.heads * D;
-    for (int64_t e = (int64_t)blockIdx.x * THREADS + tid; e < n; e += (int64_t)gridDim.x * THREADS)
-      p.o[e] = (bf16_bits)0x7FC0;
+    for (int64_t e = (int64_t)blockIdx.x * THREADS + tid; e < n; e += (int64_t)gridDim.x * THREADS) {
+      const int64_t row = e / D;  // (b*L + l)*heads + h
+      p.o[((row / p.heads) * p.hd.stride + p.hd.h0 + row % p.heads) * D + e % D] = (bf16_bits)0x7FC0;
+    }
     return;
   }
   if (!DENSE)  // ordered before any read by the barrier after the first item fetch
@@ -375,7 +378,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
   auto stage_mask = [&](int item) {
     if (!GRP) {
       const int n = item % p.g.N;
-      const uint32_t* row = p.mask + ((int64_t)(item / p.g.N) * p.g.N + n) * p.words;
+      const uint32_t* row = p.mask + (p.hd.global(item / p.g.N) * p.g.N + n) * p.words;
       for (int wi = tid; wi < p.words; wi += THREADS) {
         const int rem = p.g.N - wi * 32;
         umask[wi] = rem < 32 ? row[wi] & ((1u << rem) - 1u) : row[wi];
@@ -388,7 +391,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
         uint32_t u = 0u;
         for (int k = 0; k < 4; ++k) {
           const int n = k < ng ? group_member(p, gid, k) : -1;
-          const uint32_t x = n >= 0 ? p.mask[((int64_t)bhg * p.g.N + n) * p.words + wi] : 0u;
+          const uint32_t x = n >= 0 ? p.mask[(p.hd.global(bhg) * p.g.N + n) * p.words + wi] : 0u;
           gmask[k * p.words + wi] = x;
           u |= x;
         }
@@ -486,8 +489,8 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(AttnParams p) {
     }
     h = bh % p.heads;
     b = bh / p.heads;
-    const int64_t rs = (int64_t)p.heads * D;
-    const int64_t head_off = (int64_t)b * p.L * rs + (int64_t)h * D;
+    const int64_t rs = (int64_t)p.hd.stride * D;
+    const int64_t head_off = (int64_t)b * p.L * rs + (int64_t)(p.hd.h0 + h) * D;
 
     // ---- Q fragments: sub-tile qt holds row row0 + 32*qt + lr of the block, d = 16s + 8hi .. +7,
     //      times the score scale in log2 units (rounded to bf16), so that the
@@ -989,7 +992,7 @@ __global__ __launch_bounds__(256) void layout_kernel(Geo g, int32_t* __restrict_
 // (the dense reference's single block of L tokens).
 template <int D>
 __global__ __launch_bounds__(256) void tile_kernel(const bf16_bits* __restrict__ k, const bf16_bits* __restrict__ v,
-                                                   const int32_t* __restrict__ tok, Geo g, int L, int heads, int cpb,
+                                                   const int32_t* __restrict__ tok, Geo g, int L, Heads hd, int cpb,
                                                    bf16_bits* __restrict__ tiles) {
   __shared__ __attribute__((aligned(16))) bf16_bits ks[KCH][D + 8];
   __shared__ __attribute__((aligned(16))) bf16_bits vs[KCH][D + 8];
@@ -997,12 +1000,12 @@ __global__ __launch_bounds__(256) void tile_kernel(const bf16_bits* __restrict__
   const int c = cs % cpb;
   const int n = (cs / cpb) % g.N;
   const int bh = cs / (cpb * g.N);
-  const int h = bh % heads, b = bh / heads;
+  const int h = bh % hd.n, b = bh / hd.n;
   const Box bx = block_box(g, n);
   const int valid = bx.count - c * KCH;
   if (valid <= 0) return;  // slot past the block's chunks: never read
-  const int64_t rs = (int64_t)heads * D;
-  const int64_t head_off = (int64_t)b * L * rs + (int64_t)h * D;
+  const int64_t rs = (int64_t)hd.stride * D;
+  const int64_t head_off = (int64_t)b * L * rs + (int64_t)(hd.h0 + h) * D;
   constexpr int PIECES = KCH * D / 8;  // 16-byte pieces of K (and of V)
   const u32x4 zero = {0u, 0u, 0u, 0u};
   for (int s = threadIdx.x; s < PIECES; s += 256) {
@@ -1063,7 +1066,7 @@ __global__ __launch_bounds__(COST_WAVES * 64) void cost_kernel(AttnParams p, con
   for (int k = 0; k < p.gt * p.gh * p.gw; ++k) {
     const int n = group_member(p, gid, k);
     if (n < 0) continue;
-    rows[nrows++] = p.mask + ((int64_t)bh * p.g.N + n) * p.words;
+    rows[nrows++] = p.mask + (p.hd.global(bh) * p.g.N + n) * p.words;
     qrows += (uint32_t)cnt_s[n];
   }
   uint32_t kv = 0;
@@ -1278,6 +1281,7 @@ static AttnParams sparse_params(const AttnLaunch& a) {
   prm.B = a.B;
   prm.L = a.L;
   prm.heads = a.heads;
+  prm.hd = a.hd;
   prm.g = a.g;
   prm.words = (a.g.N + 31) / 32;
   prm.cpb = attn_chunks_per_block(vol);
@@ -1313,10 +1317,10 @@ hipError_t launch_sparse_plan(const AttnLaunch& a, int sched, const int32_t* hea
   const unsigned slots = (unsigned)(BH * a.g.N * cpb);
   if (a.D == 128)
     hipLaunchKernelGGL(tile_kernel<128>, dim3(slots), dim3(256), 0, st, (const bf16_bits*)a.k, (const bf16_bits*)a.v,
-                       a.tok, a.g, a.L, a.heads, cpb, a.tiles);
+                       a.tok, a.g, a.L, a.hd, cpb, a.tiles);
   else
     hipLaunchKernelGGL(tile_kernel<64>, dim3(slots), dim3(256), 0, st, (const bf16_bits*)a.k, (const bf16_bits*)a.v,
-                       a.tok, a.g, a.L, a.heads, cpb, a.tiles);
+                       a.tok, a.g, a.L, a.hd, cpb, a.tiles);
   hipLaunchKernelGGL(cost_kernel, dim3((n_items + COST_WAVES - 1) / COST_WAVES), dim3(COST_WAVES * 64),
                      (size_t)a.g.N * sizeof(int32_t), st, prm, a.blk_cnt, a.keys, a.rank, a.qctr, a.head_cost,
                      a.plan_tag);
@@ -1365,6 +1369,7 @@ hipError_t launch_dense_attn(const void* q, const void* k, const void* v, void* 
   prm.B = B;
   prm.L = L;
   prm.heads = heads;
+  prm.hd = Heads{heads, 0, heads};
   prm.g = dense_geo(L);
   prm.cpb = (L + KCH - 1) / KCH;
   prm.tiles = (const bf16_bits*)tiles;
@@ -1374,10 +1379,10 @@ hipError_t launch_dense_attn(const void* q, const void* k, const void* v, void* 
   prm.trace = nullptr;
   const unsigned slots = (unsigned)(B * heads * prm.cpb);
   if (D == 128)
-    hipLaunchKernelGGL(tile_kernel<128>, dim3(slots), dim3(256), 0, st, prm.k, prm.v, nullptr, prm.g, L, heads,
+    hipLaunchKernelGGL(tile_kernel<128>, dim3(slots), dim3(256), 0, st, prm.k, prm.v, nullptr, prm.g, L, prm.hd,
                        prm.cpb, (bf16_bits*)tiles);
   else
-    hipLaunchKernelGGL(tile_kernel<64>, dim3(slots), dim3(256), 0, st, prm.k, prm.v, nullptr, prm.g, L, heads, prm.cpb,
+    hipLaunchKernelGGL(tile_kernel<64>, dim3(slots), dim3(256), 0, st, prm.k, prm.v, nullptr, prm.g, L, prm.hd, prm.cpb,
                        (bf16_bits*)tiles);
   const int grid = NXCD * ((prm.n_items + NXCD - 1) / NXCD);
   if (D == 128)

@@ -24,6 +24,15 @@ struct Geo {
   int nT, nH, nW, N;
 };
 
+// The heads a launch works on: heads h0 .. h0 + n - 1 of tensors with
+// `stride` heads per token, and the matching rows of [B, stride, N, ...]
+// masks and counts.  A whole-tensor launch has h0 = 0 and stride = n.
+struct Heads {
+  int n, h0, stride;
+  // the tensor-wide (b*stride + h0 + h) of the launch's (b*n + h)
+  __host__ __device__ int64_t global(int64_t bh) const { return (bh / n) * stride + h0 + bh % n; }
+};
+
 struct Box {
   int t0, y0, x0, et, eh, ew, count, start;
 };

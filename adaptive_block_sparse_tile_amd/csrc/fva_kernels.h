@@ -9,8 +9,10 @@
 namespace fva {
 
 // Router (fva_route.hip)
-hipError_t launch_pool(const void* q, const void* k, const Geo& g, int B, int L, int heads, int D, double* qbar,
-                       double* kbar, uint32_t* status, hipStream_t st);
+// Pooled means of the heads hd selects (written compactly, [B, hd.n, N, D]);
+// clear_status: zero *status first (the router's row kernels OR into it).
+hipError_t launch_pool(const void* q, const void* k, const Geo& g, int B, int L, const Heads& hd, int D, double* qbar,
+                       double* kbar, uint32_t* status, bool clear_status, hipStream_t st);
 // Bytes of the router's static scratch on each GPU, and its device address
 // on the current device (looked up on the first call per device).
 constexpr size_t kRouteScratchBytes = (size_t)128 << 20;
@@ -18,13 +20,19 @@ hipError_t route_scratch(void** ptr);
 // Scores and row routing slab by slab: the query rows of every head are cut
 // into tiles of 64 query blocks, and slab_tiles tiles at a time get their
 // fp64 scores in S ([slab_tiles * 64][N]) and are routed from there.
-hipError_t launch_route_slabs(const double* qbar, const double* kbar, int BH, int N, int D, float top_p, int k_floor,
-                              double* S, int64_t slab_tiles, uint32_t* mask, int32_t* kv_cnt, uint32_t* status,
+// Mask and count rows are those of the heads hd selects in [B, hd.stride, N, ...].
+hipError_t launch_route_slabs(const double* qbar, const double* kbar, int B, const Heads& hd, int N, int D,
+                              float top_p, int k_floor, double* S, int64_t slab_tiles, uint32_t* mask,
+                              int32_t* kv_cnt, uint32_t* status, hipStream_t st);
+// Scores of the tiles t0 .. t0 + nt - 1 (64 query blocks of one head each)
+// into S [nt * 64][N], as the router computes them.
+hipError_t launch_scores_slab(const double* qbar, const double* kbar, int N, int D, int t0, int nt, double* S,
                               hipStream_t st);
-// Slack-aware augmentation; each row's scores are recomputed from the
-// router's pooled means (fp64 [BH, N, D]) exactly as the router computed them.
+// Slack-aware augmentation; the scores are recomputed slab by slab from the
+// router's pooled means (fp64 [BH, N, D]) with the router's scores kernel, in
+// S (slab_tiles tiles of 64 rows).
 hipError_t launch_sasa(const double* qbar, const double* kbar, int D, const uint32_t* mask_in, const Geo& g, int BH,
-                       int R, uint32_t* mask_out,
+                       int R, double* S, int64_t slab_tiles, uint32_t* mask_out,
                        int32_t* kv_cnt, int32_t* head_xcd, int64_t* xcd_load, int32_t* cand, int64_t* row_cost,
                        int32_t* slot_head, int32_t* nh, hipStream_t st);
 
@@ -39,7 +47,8 @@ struct AttnLaunch {
   const void* k;
   const void* v;
   void* o;
-  int B, L, heads, D;
+  int B, L, heads, D;  // heads: this launch's heads (hd.n)
+  Heads hd;            // which heads of q, k, v, o, the mask and the counts
   Geo g;
   const uint32_t* mask;
   float scale;

@@ -32,25 +32,25 @@ namespace fva {
 // 16-byte loads across the lanes of a wave.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void pool_kernel(const bf16_bits* __restrict__ q, const bf16_bits* __restrict__ k,
-                                                   Geo g, int L, int heads, int D, int chunks,
+                                                   Geo g, int L, Heads hd, int D, int chunks,
                                                    double* __restrict__ qbar, double* __restrict__ kbar,
-                                                   uint32_t* __restrict__ status) {
+                                                   uint32_t* __restrict__ status, bool clear_status) {
   const int n = blockIdx.x / chunks;
   const int chunk = blockIdx.x % chunks;
   const int which = blockIdx.y;
   const int b = blockIdx.z;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  if (status && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) *status = 0u;
+  if (clear_status && status && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) *status = 0u;
 
   const bf16_bits* x = which == 0 ? q : k;
   double* out = which == 0 ? qbar : kbar;
-  const int nvec = heads * D / 8;
+  const int nvec = hd.n * D / 8;
   const int vec = chunk * 64 + lane;
   const bool active = vec < nvec;
   const Box bx = block_box(g, n);
-  const int64_t row_stride = (int64_t)heads * D;
-  const bf16_bits* base = x + (int64_t)b * L * row_stride + (int64_t)vec * 8;
+  const int64_t row_stride = (int64_t)hd.stride * D;
+  const bf16_bits* base = x + (int64_t)b * L * row_stride + (int64_t)hd.h0 * D + (int64_t)vec * 8;
 
   double acc[8];
 #pragma unroll
@@ -93,7 +93,7 @@ __global__ __launch_bounds__(256) void pool_kernel(const bf16_bits* __restrict__
     const double inv_cnt = (double)bx.count;
     const int c0 = vec * 8;
     const int h = c0 / D, d0 = c0 % D;
-    double* o = out + (((int64_t)b * heads + h) * g.N + n) * D + d0;
+    double* o = out + (((int64_t)b * hd.n + h) * g.N + n) * D + d0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       double s = part[0][lane][e];
@@ -171,14 +171,14 @@ __global__ __launch_bounds__(256) void scores_kernel(const double* __restrict__ 
 // Slab row r of a router launch: its (b*heads + h) and query block i, from
 // the slab's first tile t0 (i >= N: a padding row of a head's last tile).
 struct SlabRow {
-  int64_t out;  // (b*heads + h)*N + i, the row of the mask and the counts
+  int64_t out;  // the row of the mask and the counts: (b*stride + h0 + h)*N + i
   int i;
 };
-__device__ inline SlabRow slab_row(int64_t r, int t0, int nIT, int N) {
+__device__ inline SlabRow slab_row(int64_t r, int t0, int nIT, int N, const Heads& hd) {
   const int64_t tile = t0 + r / 64;
   SlabRow x;
   x.i = (int)((tile % nIT) * 64 + r % 64);
-  x.out = (tile / nIT) * N + x.i;
+  x.out = hd.global(tile / nIT) * N + x.i;
   return x;
 }
 
@@ -218,7 +218,7 @@ __device__ inline double block_max(double v, double* red) {
 
 template <int SLOTS, int THREADS>
 __global__ __launch_bounds__(THREADS) void route_rows_kernel(const double* __restrict__ S, int N, int words, int t0,
-                                                             int nIT, float top_p, int k_floor,
+                                                             int nIT, Heads hd, float top_p, int k_floor,
                                                              uint32_t* __restrict__ mask,
                                                              int32_t* __restrict__ kv_cnt,
                                                              uint32_t* __restrict__ status) {
@@ -231,7 +231,7 @@ __global__ __launch_bounds__(THREADS) void route_rows_kernel(const double* __res
   __shared__ int nstar_s;
 
   const int tid = threadIdx.x;
-  const SlabRow sr = slab_row(blockIdx.x, t0, nIT, N);
+  const SlabRow sr = slab_row(blockIdx.x, t0, nIT, N, hd);
   if (sr.i >= N) return;  // padding row of a head's last tile
   const int64_t row = sr.out;
   const double* s = S + (int64_t)blockIdx.x * N;
@@ -463,7 +463,7 @@ struct GroupRed {
 };
 
 __global__ __launch_bounds__(256) void route_select_kernel(const double* __restrict__ S, int N, int words, int t0,
-                                                           int nIT, float top_p, int k_floor,
+                                                           int nIT, Heads hd, float top_p, int k_floor,
                                                            uint32_t* __restrict__ mask,
                                                            int32_t* __restrict__ kv_cnt,
                                                            uint32_t* __restrict__ status) {
@@ -471,7 +471,7 @@ __global__ __launch_bounds__(256) void route_select_kernel(const double* __restr
   const int nwaves = blockDim.x >> 6;
   GroupRed gr{red_slot, nwaves, 0};
   const int tid = threadIdx.x;
-  const SlabRow sr = slab_row(blockIdx.x, t0, nIT, N);
+  const SlabRow sr = slab_row(blockIdx.x, t0, nIT, N, hd);
   if (sr.i >= N) return;  // padding row of a head's last tile (uniform over the workgroup)
   const int64_t row = sr.out;
   const double* s = S + (int64_t)blockIdx.x * N;
@@ -695,13 +695,13 @@ __global__ __launch_bounds__(256) void route_select_kernel(const double* __restr
 // ---------------------------------------------------------------------------
 // launches
 // ---------------------------------------------------------------------------
-hipError_t launch_pool(const void* q, const void* k, const Geo& g, int B, int L, int heads, int D, double* qbar,
-                       double* kbar, uint32_t* status, hipStream_t st) {
-  const int nvec = heads * D / 8;
+hipError_t launch_pool(const void* q, const void* k, const Geo& g, int B, int L, const Heads& hd, int D, double* qbar,
+                       double* kbar, uint32_t* status, bool clear_status, hipStream_t st) {
+  const int nvec = hd.n * D / 8;
   const int chunks = (nvec + 63) / 64;
   dim3 grid(g.N * chunks, 2, B);
-  hipLaunchKernelGGL(pool_kernel, grid, dim3(256), 0, st, (const bf16_bits*)q, (const bf16_bits*)k, g, L, heads, D,
-                     chunks, qbar, kbar, status);
+  hipLaunchKernelGGL(pool_kernel, grid, dim3(256), 0, st, (const bf16_bits*)q, (const bf16_bits*)k, g, L, hd, D,
+                     chunks, qbar, kbar, status, clear_status);
   return hipGetLastError();
 }
 
@@ -735,20 +735,27 @@ hipError_t route_scratch(void** ptr) {
   return hipSuccess;
 }
 
-hipError_t launch_route_slabs(const double* qbar, const double* kbar, int BH, int N, int D, float top_p, int k_floor,
-                              double* S, int64_t slab_tiles, uint32_t* mask, int32_t* kv_cnt, uint32_t* status,
+hipError_t launch_scores_slab(const double* qbar, const double* kbar, int N, int D, int t0, int nt, double* S,
                               hipStream_t st) {
+  hipLaunchKernelGGL(scores_kernel, dim3((N + 63) / 64, nt), dim3(256), 0, st, qbar, kbar, N, D, t0, (N + 63) / 64, S);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_slabs(const double* qbar, const double* kbar, int B, const Heads& hd, int N, int D,
+                              float top_p, int k_floor, double* S, int64_t slab_tiles, uint32_t* mask,
+                              int32_t* kv_cnt, uint32_t* status, hipStream_t st) {
   const int words = (N + 31) / 32;
   const int nIT = (N + 63) / 64;
-  const int64_t tiles = (int64_t)BH * nIT;
+  const int64_t tiles = (int64_t)B * hd.n * nIT;
   for (int64_t t0 = 0; t0 < tiles; t0 += slab_tiles) {
     const int nt = (int)std::min<int64_t>(slab_tiles, tiles - t0);
-    hipLaunchKernelGGL(scores_kernel, dim3((N + 63) / 64, nt), dim3(256), 0, st, qbar, kbar, N, D, (int)t0, nIT, S);
+    hipError_t e = launch_scores_slab(qbar, kbar, N, D, (int)t0, nt, S, st);
+    if (e != hipSuccess) return e;
     const dim3 grid((unsigned)nt * 64);
 #define FVA_ROUTE_CASE(SL, TH)                                                                                  \
     if (N <= SL) {                                                                                              \
-      hipLaunchKernelGGL((route_rows_kernel<SL, TH>), grid, dim3(TH), 0, st, S, N, words, (int)t0, nIT, top_p, \
-                         k_floor, mask, kv_cnt, status);                                                        \
+      hipLaunchKernelGGL((route_rows_kernel<SL, TH>), grid, dim3(TH), 0, st, S, N, words, (int)t0, nIT, hd,    \
+                         top_p, k_floor, mask, kv_cnt, status);                                                 \
       continue;                                                                                                 \
     }
     FVA_ROUTE_CASE(64, 64)
@@ -758,8 +765,8 @@ hipError_t launch_route_slabs(const double* qbar, const double* kbar, int BH, in
 #undef FVA_ROUTE_CASE
     if (N > 8192) return hipErrorInvalidValue;
     const int threads = 64 * ((words + 63) / 64);
-    hipLaunchKernelGGL(route_select_kernel, grid, dim3(threads), 0, st, S, N, words, (int)t0, nIT, top_p, k_floor,
-                       mask, kv_cnt, status);
+    hipLaunchKernelGGL(route_select_kernel, grid, dim3(threads), 0, st, S, N, words, (int)t0, nIT, hd, top_p,
+                       k_floor, mask, kv_cnt, status);
   }
   return hipGetLastError();
 }

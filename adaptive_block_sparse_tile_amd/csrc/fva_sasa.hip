@@ -4,8 +4,14 @@
 // balancing the non-critical ranks still have slack, which is filled with
 // extra high-value attention blocks chosen from the attention scores, so that
 // the critical path does not grow.  On one GPU the ranks are the 8 XCDs:
-//   1. every row's cost is its real token pairs, c_i * sum_{kept j} c_j, and
-//      a head's cost is the sum over its rows;
+//   1. every row's cost is the time the attention kernel spends on it, in
+//      steps of one 32-key half on its busiest SIMD: a query block of c_i
+//      tokens (t_i = ceil(c_i / 32) row tiles on 8 wavefronts, two per SIMD;
+//      a ragged block's tiles split their key halves over two wavefronts)
+//      takes r_i = ceil(t_i / 2) steps per 64-key chunk, and a key block of
+//      c_j tokens is ceil(c_j / 64) chunks, so row cost =
+//      r_i * sum_{kept j} ceil(c_j / 64); a head's cost is the sum over its
+//      rows;
 //   2. heads go longest first (ties: lower head) to the XCD with the least
 //      load so far (ties: lower XCD) -- the LPT rule of the attention
 //      schedule; the heaviest XCD's load is the makespan M;
@@ -13,8 +19,11 @@
 //      in the order they were assigned to x, rows in block order) the r-th
 //      block the router dropped from that row, in the router's order (score
 //      descending, lower index first); the longest prefix of these offers
-//      whose summed cost c_i * c_j fits M - load_x is added to the mask.
+//      whose summed cost r_i * ceil(c_j / 64) fits M - load_x is added to the
+//      mask.
 // The attention then runs with each XCD serving only its own heads.
+#include <algorithm>
+
 #include "fva_dev.h"
 #include "fva_kernels.h"
 
@@ -25,48 +34,42 @@ constexpr int SASA_NXCD = 8;
 __device__ inline bool mask_bit(const uint32_t* row, int j) { return (row[j >> 5] >> (j & 31)) & 1u; }
 
 __device__ inline int block_count(const Geo& g, int j) { return block_box(g, j).count; }
+// steps of a query block per 64-key chunk on the busiest SIMD, and the chunks of a key block
+__device__ inline int row_rate(const Geo& g, int i) { return ((block_count(g, i) + 31) / 32 + 1) / 2; }
+__device__ inline int key_chunks(const Geo& g, int j) { return (block_count(g, j) + 63) / 64; }
 
-// Per row (one wavefront): the row's block scores, recomputed from the
-// router's pooled means with the router's arithmetic (an fma chain over d
-// in increasing order, then division by sqrt(D): bit-equal to the scores it
-// routed on) into LDS; the row cost, the kept count, and the first R dropped
-// blocks in the router's order (-1 past the last one).
-__global__ __launch_bounds__(64) void sasa_cand_kernel(const double* __restrict__ qbar, const double* __restrict__ kbar,
-                                                       int D, const uint32_t* __restrict__ mask, Geo g, int words,
-                                                       int R, int32_t* __restrict__ cand,
-                                                       int64_t* __restrict__ row_cost,
+// Per row (one wavefront), for the rows of one slab of score tiles (tiles
+// of 64 query blocks of one head, scored by the router's own scores kernel,
+// so the scores are bit-equal to what the router ranked): the row cost, the
+// kept count, and the first R dropped blocks in the router's order (-1 past
+// the last one).  Workgroup r of the launch is slab row r (rows past N in a
+// head's last tile do nothing).
+__global__ __launch_bounds__(64) void sasa_cand_kernel(const double* __restrict__ S, int t0, int nIT,
+                                                       const uint32_t* __restrict__ mask, Geo g, int words, int R,
+                                                       int32_t* __restrict__ cand, int64_t* __restrict__ row_cost,
                                                        int32_t* __restrict__ kv_cnt) {
-  extern __shared__ double s[];  // [N]
-  const int64_t row = blockIdx.x;
-  const int lane = threadIdx.x;
   const int N = g.N;
+  const int64_t tile = t0 + blockIdx.x / 64;
+  const int i = (int)((tile % nIT) * 64 + blockIdx.x % 64);
+  if (i >= N) return;
+  const int64_t row = (tile / nIT) * N + i;
+  const int lane = threadIdx.x;
   const uint32_t* m = mask + row * words;
-  {
-    const double* qi = qbar + row * D;
-    const double* kb = kbar + (row / N) * N * D;
-    const double rs = sqrt((double)D);
-    for (int j = lane; j < N; j += 64) {
-      const double* kj = kb + (int64_t)j * D;
-      double acc = 0.0;
-      for (int d = 0; d < D; ++d) acc = fma(qi[d], kj[d], acc);
-      s[j] = acc / rs;
-    }
-    __syncthreads();
-  }
-  int64_t kept_tok = 0;
+  const double* s = S + (int64_t)blockIdx.x * N;
+  int64_t kept_chunks = 0;
   int kept = 0;
   for (int j = lane; j < N; j += 64)
     if (mask_bit(m, j)) {
-      kept_tok += block_count(g, j);
+      kept_chunks += key_chunks(g, j);
       ++kept;
     }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
-    kept_tok += __shfl_xor(kept_tok, off);
+    kept_chunks += __shfl_xor(kept_chunks, off);
     kept += __shfl_xor(kept, off);
   }
   if (lane == 0) {
-    row_cost[row] = (int64_t)block_count(g, (int)(row % N)) * kept_tok;
+    row_cost[row] = (int64_t)row_rate(g, (int)(row % N)) * kept_chunks;
     if (kv_cnt) kv_cnt[row] = kept;
   }
   // the previous pick (ps, pj); the next pick is the best dropped block that
@@ -188,7 +191,7 @@ __global__ __launch_bounds__(1024) void sasa_take_kernel(Geo g, int words, int R
       const int k = (int)(rem / N), i = (int)(rem % N);
       row = (int64_t)slot_head[x * BH + k] * N + i;
       j = cand[row * R + r];
-      if (j >= 0) cost = (int64_t)block_count(g, i) * block_count(g, j);
+      if (j >= 0) cost = (int64_t)row_rate(g, i) * key_chunks(g, j);
     }
     // inclusive scan over the workgroup
     int64_t v = cost;
@@ -215,8 +218,9 @@ __global__ __launch_bounds__(1024) void sasa_take_kernel(Geo g, int words, int R
 }
 
 hipError_t launch_sasa(const double* qbar, const double* kbar, int D, const uint32_t* mask_in, const Geo& g, int BH,
-                       int R, uint32_t* mask_out, int32_t* kv_cnt, int32_t* head_xcd, int64_t* xcd_load, int32_t* cand,
-                       int64_t* row_cost, int32_t* slot_head, int32_t* nh, hipStream_t st) {
+                       int R, double* S, int64_t slab_tiles, uint32_t* mask_out, int32_t* kv_cnt, int32_t* head_xcd,
+                       int64_t* xcd_load, int32_t* cand, int64_t* row_cost, int32_t* slot_head, int32_t* nh,
+                       hipStream_t st) {
   const int words = (g.N + 31) / 32;
   const int64_t rows = (int64_t)BH * g.N;
   if (mask_out != mask_in) {
@@ -224,8 +228,15 @@ hipError_t launch_sasa(const double* qbar, const double* kbar, int D, const uint
                                   hipMemcpyDeviceToDevice, st);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(sasa_cand_kernel, dim3((unsigned)rows), dim3(64), (size_t)g.N * sizeof(double), st, qbar, kbar, D,
-                     mask_in, g, words, R, cand, row_cost, kv_cnt);
+  const int nIT = (g.N + 63) / 64;
+  const int64_t tiles = (int64_t)BH * nIT;
+  for (int64_t t0 = 0; t0 < tiles; t0 += slab_tiles) {
+    const int nt = (int)std::min<int64_t>(slab_tiles, tiles - t0);
+    hipError_t e = launch_scores_slab(qbar, kbar, g.N, D, (int)t0, nt, S, st);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(sasa_cand_kernel, dim3((unsigned)nt * 64), dim3(64), 0, st, S, (int)t0, nIT, mask_in, g, words,
+                       R, cand, row_cost, kv_cnt);
+  }
   hipLaunchKernelGGL(sasa_lpt_kernel, dim3(1), dim3(256), (size_t)BH * 12, st, row_cost, g.N, BH, head_xcd, slot_head,
                      nh, xcd_load);
   hipLaunchKernelGGL(sasa_take_kernel, dim3(SASA_NXCD), dim3(1024), 0, st, g, words, R, BH, cand, slot_head, nh,

@@ -223,6 +223,41 @@ fva_status fva_attn_plan(const void* k, const void* v, const fva_desc* desc, con
 fva_status fva_attn_exec(const void* q, void* o, const fva_desc* desc, const fva_grid* grid, const uint32_t* mask,
                          float scale, int32_t sched, uint64_t* trace, void* ws, size_t ws_bytes, void* stream);
 
+/* The whole layer in one call: fva_route, then fva_sparse_attn (LPT
+ * schedule) on its mask, optionally pipelined over head groups (FVAttn
+ * abstract, "Overlap/Opt.": the overhead of scheduling hidden behind the
+ * attention; summary, key module 4).
+ *   groups = 1: route, plan and attention of all heads in order on stream,
+ *     the same work as fva_route followed by fva_sparse_attn.
+ *   groups = G > 1: the heads are cut into G contiguous groups (group g:
+ *     heads g*heads/G .. (g+1)*heads/G - 1), each routed, planned and
+ *     attended on its own, the groups alternating between stream (even g)
+ *     and side_stream (odd g).  One group's routing, planning and attention
+ *     then start while the previous group's attention still runs: they take
+ *     the compute units that attention frees in its tail, so consecutive
+ *     attention launches overlap instead of each ending in its own tail.
+ *     side_stream NULL or equal to stream runs the groups in order on
+ *     stream.  side_stream waits for the work enqueued on stream before the
+ *     call (and for group 0's pooling), and stream waits for everything the
+ *     call enqueued on side_stream, so to the caller the call is one ordered
+ *     operation on stream.
+ * Outputs are those of fva_route (mask, kv_cnt, status) and fva_sparse_attn
+ * (o), bit for bit the same for every `groups` and stream choice.
+ *   ws   device workspace of at least fva_routed_attn_workspace_bytes():
+ *        one router and one attention workspace (for the largest group) per
+ *        stream used; with G > 1 the size covers two streams.
+ * Measured on one MI355X, the pipeline pays when a head's share of the layer
+ * is long (the 393,216-token video, one head per group) and costs more than
+ * it hides on short layers (the 27,280-token Wan layer), where groups = 1 is
+ * the right choice.
+ * Errors: those of fva_route and fva_sparse_attn, and INVALID_ARG for groups
+ * outside 1..heads. */
+size_t fva_routed_attn_workspace_bytes(const fva_desc* desc, const fva_grid* grid, int32_t groups);
+fva_status fva_routed_attn(const void* q, const void* k, const void* v, void* o, const fva_desc* desc,
+                           const fva_grid* grid, const fva_route_cfg* cfg, float scale, int32_t groups,
+                           uint32_t* mask, int32_t* kv_cnt, uint32_t* status, void* ws, size_t ws_bytes,
+                           void* stream, void* side_stream);
+
 /* Number of work items of the sparse attention for this shape, or -1 for
  * invalid arguments.  A work item is one query block; blocks of at most 64
  * tokens are grouped 2x1x2 (t, y, x) per item and blocks of 65..128 tokens
@@ -255,26 +290,31 @@ fva_status fva_attn_schedule(const fva_desc* desc, const fva_grid* grid, const v
  * summary, key modules 2 and 3: after load balancing, the slack left on the
  * non-critical ranks is filled with extra high-value blocks chosen from the
  * attention scores, without lengthening the critical path).  The ranks are
- * the 8 XCDs.  Row cost = c_i * sum_{kept j} c_j real token pairs; head cost
- * = the sum over its rows; heads go longest first (ties: lower head) to the
- * least loaded XCD (ties: lower XCD); the heaviest XCD's load is the
- * makespan M.  Every other XCD x offers, in rounds r = 1..rounds, each of its
+ * the 8 XCDs.  Row cost = the attention kernel's time on the row, in steps
+ * of one 32-key half on its busiest SIMD: r_i = ceil(ceil(c_i/32)/2) steps
+ * per 64-key chunk (32-row tiles on 8 wavefronts, two per SIMD; a ragged
+ * block's tiles split their key halves over two wavefronts) times
+ * ceil(c_j/64) chunks summed over the kept key blocks j; head cost = the sum
+ * over its rows; heads go longest first (ties: lower head) to the least
+ * loaded XCD (ties: lower XCD); the heaviest XCD's load is the makespan M.  Every other XCD x offers, in rounds r = 1..rounds, each of its
  * rows (heads in the order they were assigned to x, rows in block order) the
  * r-th block the router dropped from that row, in the router's order (block
  * score descending, lower index first); the longest prefix of these offers
- * whose summed cost c_i * c_j fits M - load_x is added.  Run the attention
+ * whose summed cost r_i * ceil(c_j/64) fits M - load_x is added.  Run the attention
  * with FVA_SCHED_XCD and this head_xcd so that each XCD serves its own heads.
  *   mask_in    uint32 [B, heads, N, ceil(N/32)] from fva_route
  *   route_ws   the workspace of that fva_route call, untouched since (its
- *              pooled Q and K; each row's scores are recomputed from them
- *              with the router's arithmetic, bit-equal to what it routed on)
+ *              pooled Q and K; the scores are recomputed from them slab by
+ *              slab with the router's own scores kernel, bit-equal to what it
+ *              routed on)
  *   rounds     0..8 (0 copies the mask)
  *   mask_out   out, same layout (may equal mask_in)
  *   kv_cnt     out, int32 [B, heads, N] kept counts after augmentation (nullable)
  *   head_xcd   out, int32 [B*heads]
  *   xcd_load   out, int64 [16]: load of each XCD before (0..7) and the cost
- *              added to it (8..15), in real token pairs
- *   ws         device workspace of at least fva_sasa_workspace_bytes()
+ *              added to it (8..15), in the steps of the row cost
+ *   ws         device workspace of at least fva_sasa_workspace_bytes() (a
+ *              score slab like the router's, candidates, costs, placement)
  * Errors: INVALID_ARG, SHAPE, UNSUPPORTED, WORKSPACE, DEVICE. */
 size_t fva_sasa_workspace_bytes(const fva_desc* desc, const fva_grid* grid, int32_t rounds);
 fva_status fva_sasa(const fva_desc* desc, const fva_grid* grid, const uint32_t* mask_in, const void* route_ws,

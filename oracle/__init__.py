@@ -330,22 +330,39 @@ def static_mask(grid, block, local=(1, 1, 1), anchor_t=0, B=1, heads=1):
     return mask, counts
 
 
+def sasa_row_rate(counts):
+    """Steps of one 32-key half on the busiest SIMD per 64-key chunk for query
+    blocks of `counts` tokens: ceil(ceil(c / 32) / 2)."""
+    c = np.asarray(counts, dtype=np.int64)
+    return ((c + 31) // 32 + 1) // 2
+
+
+def sasa_key_chunks(counts):
+    """64-key chunks of key blocks of `counts` tokens: ceil(c / 64)."""
+    return (np.asarray(counts, dtype=np.int64) + 63) // 64
+
+
 def sasa(scores: np.ndarray, mask: np.ndarray, grid, block, rounds: int, margin: float = MARGIN):
     """Slack-aware sparse augmentation, one-GPU form (8 XCDs as the ranks).
 
     FVAttn abstract and summary, key modules 2 and 3: after load balancing the
     non-critical ranks have slack, filled with extra high-value blocks chosen
     from the attention scores without lengthening the critical path.  Steps:
-      1. row cost = c_i * sum of c_j over the row's kept blocks (real token
-         pairs); head cost = sum over its rows;
+      1. row cost = the attention kernel's time on the row, in steps of one
+         32-key half on its busiest SIMD: r_i = ceil(ceil(c_i / 32) / 2)
+         steps per 64-key chunk (row tiles of 32 on 8 wavefronts, two per
+         SIMD, a ragged block's tiles splitting their key halves over two
+         wavefronts) times ceil(c_j / 64) chunks summed over the row's kept
+         blocks; head cost = sum over its rows;
       2. heads by cost descending (ties: lower head) each go to the XCD with
          the least load so far (ties: lower XCD); makespan M = max load;
       3. on every XCD, offers in rounds r = 0..rounds-1: for each of its heads
          (in assignment order) and each row (block order), the row's r-th
          dropped block in the router's order (score descending, lower index
          first; non-finite scores are never offered); offers are taken in
-         that order until the first one whose cost c_i * c_j no longer fits
-         M - load (rows without an r-th dropped block are passed over).
+         that order until the first one whose cost r_i * ceil(c_j / 64) no
+         longer fits M - load (rows without an r-th dropped block are passed
+         over).
     scores: fp64 [B, heads, N, N] (oracle.scores); mask: the routed mask.
     Returns (mask_out, counts, head_xcd [B*heads], load [8], added [8],
     flags [B, heads, N]) where a flagged row has two of its first rounds+1
@@ -355,9 +372,11 @@ def sasa(scores: np.ndarray, mask: np.ndarray, grid, block, rounds: int, margin:
     B, heads, N, _ = scores.shape
     BH = B * heads
     c = block_table(grid, block)[:, 6].astype(np.int64)
+    rate = sasa_row_rate(c)
+    chunks = sasa_key_chunks(c)
     keep = mask_to_bool(mask, N).reshape(BH, N, N)
     S = scores.reshape(BH, N, N)
-    row_cost = c[None, :] * (keep * c[None, None, :]).sum(-1)
+    row_cost = rate[None, :] * (keep * chunks[None, None, :]).sum(-1)
     head_cost = row_cost.sum(1)
     load = [0] * 8
     heads_of = [[] for _ in range(8)]
@@ -395,7 +414,7 @@ def sasa(scores: np.ndarray, mask: np.ndarray, grid, block, rounds: int, margin:
                     j = int(cand[h, i, r])
                     if j < 0:
                         continue
-                    cost = int(c[i] * c[j])
+                    cost = int(rate[i] * chunks[j])
                     if acc + cost > slack:
                         stop = True
                         break

@@ -235,3 +235,29 @@ def test_route_noalloc_host_validation():
     assert call(big, fva.make_grid((96, 64, 64), (4, 4, 4)), fva.RouteCfg(0.85, 32)) == 6
     assert "static scratch" in _err()
     assert fva.ROUTE_SCRATCH_BYTES == 128 << 20
+
+
+def test_routed_attn_host_validation_and_workspace():
+    lib = fva.load()
+    desc = fva.make_desc(1, 27280, 40, 128)
+    grid = fva.make_grid((31, 22, 40), (4, 8, 8))
+    one = lib.fva_routed_attn_workspace_bytes(ctypes.byref(desc), ctypes.byref(grid), 1)
+    assert one == fva.route_workspace_bytes((1, 27280, 40, 128), (31, 22, 40), (4, 8, 8)) + \
+        fva.attn_workspace_bytes((1, 27280, 40, 128), (31, 22, 40), (4, 8, 8))
+    # two streams' sets, each for the largest group (14 of 40 heads in 3 groups)
+    three = lib.fva_routed_attn_workspace_bytes(ctypes.byref(desc), ctypes.byref(grid), 3)
+    assert three == 2 * (fva.route_workspace_bytes((1, 27280, 14, 128), (31, 22, 40), (4, 8, 8)) +
+                         fva.attn_workspace_bytes((1, 27280, 14, 128), (31, 22, 40), (4, 8, 8)))
+    assert lib.fva_routed_attn_workspace_bytes(ctypes.byref(desc), ctypes.byref(grid), 41) == 0
+
+    def call(groups=2, cfg=fva.RouteCfg(0.9, 8), scale=128 ** -0.5, ws_bytes=1 << 40, side=FAKE, o=FAKE):
+        return lib.fva_routed_attn(FAKE, FAKE, FAKE, o, ctypes.byref(desc), ctypes.byref(grid), ctypes.byref(cfg),
+                                   scale, groups, FAKE, None, None, FAKE, ws_bytes, None, side)
+    assert call(groups=0) == 1 and "groups 0" in _err()
+    assert call(groups=41) == 1
+    assert call(cfg=fva.RouteCfg(0.9, 121)) == 3
+    assert call(scale=0.1) == 4
+    assert call(o=None) == 1
+    assert call(ws_bytes=three - 1, groups=3) == 5 and "needed" in _err()
+    # one stream: one set suffices, so a two-set workspace minus a byte still covers it
+    assert call(ws_bytes=three // 2 - 1, groups=3, side=None) == 5

@@ -1,5 +1,9 @@
 """Pins of the oracle's slack-aware sparse augmentation (one-GPU form).
 
+Costs are the attention kernel's time model: a query block of c_i tokens
+takes ceil(ceil(c_i/32)/2) steps per 64-key chunk on its busiest SIMD, a key
+block of c_j tokens is ceil(c_j/64) chunks (written out here as a table).
+
 Checked against things other than the rule's own text: an independent stable
 argsort for each row's candidate order; the partition of head costs over the
 XCDs; that nothing is added to the critical XCD and no XCD passes the
@@ -41,8 +45,10 @@ def test_invariants(wl):
     assert (out >= keep).all()
     assert np.array_equal(co.reshape(-1, N), out.sum(-1))
     c = oracle.block_table(wl.grid, wl.block)[:, 6].astype(np.int64)
+    # the kernel's time per (query block, key block): steps per chunk on the busiest SIMD times key chunks
+    cost = np.array([[(((ci + 31) // 32 + 1) // 2) * ((cj + 63) // 64) for cj in c] for ci in c], dtype=np.int64)
     # head costs partition over the XCDs
-    head_cost = (c[None, :, None] * keep * c[None, None, :]).sum((1, 2))
+    head_cost = (keep * cost[None]).sum((1, 2))
     for x in range(8):
         assert load[x] == head_cost[hx == x].sum()
     M = load.max()
@@ -50,7 +56,7 @@ def test_invariants(wl):
     assert ((load + added) <= M).all()
     # the added cost is what the new bits cost, per XCD
     new = out & ~keep
-    per_head = (c[None, :, None] * new * c[None, None, :]).sum((1, 2))
+    per_head = (new * cost[None]).sum((1, 2))
     for x in range(8):
         assert added[x] == per_head[hx == x].sum()
     # per row: the added blocks are the first ones of the dropped order (stable argsort of -score)
@@ -64,7 +70,7 @@ def test_invariants(wl):
             assert set(order[:a].tolist()) == set(np.nonzero(new[h, i])[0].tolist())
             assert a <= rounds
     # every XCD either ran out of offers or kept less slack than the largest offer
-    biggest = int(c.max()) ** 2
+    biggest = int(cost.max())
     for x in range(8):
         rows_x = [h for h in range(B * H) if hx[h] == x]
         dropped = sum(int(min(rounds, (~keep[h]).sum(-1)[i])) for h in rows_x for i in range(N))
@@ -93,3 +99,15 @@ def test_dense_rows_and_zero_rounds():
     S, mask = _routed(wl)
     mo, _, _, _, added, _ = oracle.sasa(S, mask, wl.grid, wl.block, 0)
     assert np.array_equal(mo, mask) and (added == 0).all()
+
+
+def test_time_model_rates():
+    """Steps per chunk on the busiest SIMD for the kernel's wavefront layout
+    (8 wavefronts, two per SIMD; tiles of 32 rows; blocks of at most 6 tiles
+    split key halves): full 256-token blocks 4, the Wan layer's ragged 192- and
+    144-token blocks 3 each (the pair count would charge 144 only 0.5625 of a
+    full block), 128 tokens 2, 64 tokens 1; a 144-token key block is 3 chunks,
+    as many as a 192-token one."""
+    assert oracle.sasa_row_rate([256, 224, 192, 160, 144, 128, 96, 64, 40, 32]).tolist() == \
+        [4, 4, 3, 3, 3, 2, 2, 1, 1, 1]
+    assert oracle.sasa_key_chunks([256, 192, 144, 64, 40]).tolist() == [4, 3, 3, 1, 1]
