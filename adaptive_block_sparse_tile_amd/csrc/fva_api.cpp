@@ -91,8 +91,13 @@ fva_status check_scale(int D, float scale) {
 // The router's workspace: pooled means (fp64 [B*heads, N, D], Q and K) and
 // one slab of fp64 scores.  The scores are produced and consumed tile by
 // tile (64 query blocks of one head per tile), so the slab holds at most
-// kScoreSlabBytes of them, never the whole [B*heads, N, N] matrix.
-constexpr size_t kScoreSlabBytes = (size_t)128 << 20;
+// kScoreSlabBytes of them, never the whole [B*heads, N, N] matrix.  Each slab
+// costs one scores and one routing launch with their tails (about 90 us on
+// the long video's 6144-block rows), hence a slab of a few hundred MiB.
+#ifndef FVA_SCORE_SLAB_MIB
+#define FVA_SCORE_SLAB_MIB 512
+#endif
+constexpr size_t kScoreSlabBytes = (size_t)FVA_SCORE_SLAB_MIB << 20;
 constexpr int64_t kMaxSlabTiles = 65535;  // grid.y of the scores kernel
 
 struct RouteWs {

@@ -452,6 +452,27 @@ struct GroupRed {
     *b = rb;
     flip ^= 1;
   }
+  // a sum over the lanes (fixed order) and a count that is already uniform
+  // in each wavefront, in one round
+  __device__ double reduce_sum_count(double v, uint32_t wave_count, uint32_t* total) {
+    const double w = wave_reduce(v, AddOp());
+    uint64_t* buf = slot + flip * 8;
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) {
+      buf[wave] = to_bits(w);
+      buf[4 + wave] = wave_count;
+    }
+    __syncthreads();
+    double r = from_bits<double>(buf[0]);
+    uint32_t c = (uint32_t)buf[4];
+    for (int i = 1; i < nwaves; ++i) {
+      r += from_bits<double>(buf[i]);
+      c += (uint32_t)buf[4 + i];
+    }
+    flip ^= 1;
+    *total = c;
+    return r;
+  }
   __device__ static uint64_t to_bits(double x) { return (uint64_t)__double_as_longlong(x); }
   __device__ static uint64_t to_bits(uint64_t x) { return x; }
   __device__ static uint64_t to_bits(uint32_t x) { return x; }
@@ -524,19 +545,21 @@ __global__ __launch_bounds__(256) void route_select_kernel(const double* __restr
     }
   gr.reduce2(&kmin, &kmax, MinOp(), MaxOp());
   // mass and count of the blocks with key >= K (fixed summation order)
+  // (A block past N has key 0, below the key of every finite score, and every
+  // K searched is at least kmin, so it never counts.)  The mass adds
+  // fma(sel, pr, m) with sel 1 or 0, the same bits as adding the selected
+  // probability; each wavefront's count comes from the lane masks of the
+  // comparisons (scalar popcounts), so only the mass is reduced across lanes.
   auto mass_count_ge = [&](uint64_t K, uint32_t* cnt) -> double {
     double m = 0.0;
-    uint32_t c = 0;
+    uint32_t c = 0;  // uniform in the wavefront
 #pragma unroll
     for (int e = 0; e < 32; ++e) {
-      const bool ge = j0 + e < N && key[e] >= K;
-      m += ge ? pr[e] : 0.0;
-      c += ge ? 1u : 0u;
+      const bool ge = key[e] >= K;
+      m = fma(ge ? 1.0 : 0.0, pr[e], m);
+      c += (uint32_t)__popcll(__ballot(ge));
     }
-    double cd = (double)c;  // counts are exact in double
-    gr.reduce2(&m, &cd, AddOp(), AddOp());
-    *cnt = (uint32_t)cd;
-    return m;
+    return gr.reduce_sum_count(m, c, cnt);
   };
   // the only key in [lo, hi) (callers know there is exactly one)
   auto only_key_in = [&](uint64_t lo, uint64_t hi) -> uint64_t {

@@ -46,9 +46,9 @@ def test_workspace_sizes():
     r = fva.route_workspace_bytes(shape, (31, 22, 40), (4, 8, 8))
     rows = 40 * 120
     assert r >= 2 * rows * 128 * 8 + rows * 120 * 8
-    # long video: pooled means plus one score slab of 128 MiB (42 tiles of 64 x 6144 fp64), not 30720 x 6144
+    # long video: pooled means plus one score slab of 512 MiB (170 tiles of 64 x 6144 fp64), not 30720 x 6144
     rl = fva.route_workspace_bytes((1, 393216, 5, 128), (96, 64, 64), (4, 4, 4))
-    assert rl == 2 * 5 * 6144 * 128 * 8 + 42 * 64 * 6144 * 8
+    assert rl == 2 * 5 * 6144 * 128 * 8 + 170 * 64 * 6144 * 8
     a = fva.attn_workspace_bytes(shape, (31, 22, 40), (4, 8, 8))
     assert a >= 27280 * 4 + rows * (8 + 4 + 4)
     assert fva.route_workspace_bytes((1, 27281, 40, 128), (31, 22, 40), (4, 8, 8)) == 0   # T*H*W != L
