@@ -34,7 +34,7 @@ EXPORTS = ["fva_num_blocks", "fva_route_workspace_bytes", "fva_attn_workspace_by
            "fva_route", "fva_route_noalloc", "fva_static_mask", "fva_sparse_attn", "fva_attn_plan", "fva_attn_exec", "fva_routed_attn_workspace_bytes", "fva_routed_attn", "fva_attn_items",
            "fva_attn_schedule", "fva_sasa_workspace_bytes", "fva_sasa",
            "fva_dense_workspace_bytes", "fva_dense_attn_ref",
-           "fva_trace_imbalance", "fva_last_error", "fva_status_name"]
+           "fva_trace_imbalance", "fva_trace_xcd_speed", "fva_last_error", "fva_status_name"]
 
 
 class FvaError(RuntimeError):
@@ -107,7 +107,10 @@ def load():
     lib.fva_sasa_workspace_bytes.restype = ctypes.c_size_t
     lib.fva_sasa_workspace_bytes.argtypes = [D, G, ctypes.c_int32]
     lib.fva_sasa.restype = ctypes.c_int
-    lib.fva_sasa.argtypes = [D, G, _P, _P, ctypes.c_size_t, ctypes.c_int32, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.fva_sasa.argtypes = [D, G, _P, _P, ctypes.c_size_t, ctypes.c_int32, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
+                             _P]
+    lib.fva_trace_xcd_speed.restype = ctypes.c_int
+    lib.fva_trace_xcd_speed.argtypes = [_P, ctypes.c_int32, _P, _P]
     lib.fva_dense_workspace_bytes.restype = ctypes.c_size_t
     lib.fva_dense_workspace_bytes.argtypes = [D]
     lib.fva_dense_attn_ref.restype = ctypes.c_int
@@ -384,10 +387,11 @@ def sasa_workspace_bytes(shape, grid, block, rounds) -> int:
 
 
 @_on_stream
-def sasa(shape, grid, block, mask, route_ws, rounds=4, out=None, ws=None, stream=None):
+def sasa(shape, grid, block, mask, route_ws, rounds=4, xcd_weight=None, out=None, ws=None, stream=None):
     """Slack-aware augmentation of a routed mask on the GPU (8 XCDs as ranks).
 
     route_ws: the workspace of the fva_route call that produced mask.
+    xcd_weight: optional 8 relative XCD speeds (per mille), e.g. from xcd_speed().
     Returns (mask_out, kv_cnt, head_xcd int32 [B*heads], xcd_load int64 [16])."""
     torch = _torch()
     B, L, heads, D = (int(x) for x in shape)
@@ -401,8 +405,13 @@ def sasa(shape, grid, block, mask, route_ws, rounds=4, out=None, ws=None, stream
     xcd_load = torch.empty(16, dtype=torch.int64, device=mask.device)
     if ws is None:
         ws = workspace(sasa_workspace_bytes(shape, grid, block, rounds), mask.device)
+    wts = None
+    if xcd_weight is not None:
+        wts = np.ascontiguousarray(xcd_weight, dtype=np.int32)
+        assert wts.shape == (8,)
     _check(load().fva_sasa(ctypes.byref(desc), ctypes.byref(g), mask.data_ptr(), route_ws.data_ptr(),
-                           route_ws.numel(), int(rounds), mask_out.data_ptr(), cnt.data_ptr(), head_xcd.data_ptr(),
+                           route_ws.numel(), int(rounds), wts.ctypes.data if wts is not None else None,
+                           mask_out.data_ptr(), cnt.data_ptr(), head_xcd.data_ptr(),
                            xcd_load.data_ptr(), ws.data_ptr(), ws.numel(), _stream_ptr(stream)))
     return mask_out, cnt, head_xcd, xcd_load
 
@@ -427,6 +436,16 @@ def dense_attn_ref(q, k, v, scale=None, out=None, ws=None, stream=None):
                                      ctypes.byref(make_desc(*shape)), float(scale), ws.data_ptr(), ws.numel(),
                                      _stream_ptr(stream)))
     return o
+
+
+def xcd_speed(trace_host: np.ndarray, xcd_load) -> np.ndarray:
+    """Relative XCD speeds (per mille) from a host copy of a per-XCD-schedule
+    trace and the cost sasa() placed on each XCD (fva_trace_xcd_speed)."""
+    t = np.ascontiguousarray(trace_host).view(np.uint64).reshape(-1)
+    ld = np.ascontiguousarray(np.asarray(xcd_load)[:8], dtype=np.int64)
+    out = np.zeros(8, dtype=np.int32)
+    _check(load().fva_trace_xcd_speed(t.ctypes.data, t.size // 4, ld.ctypes.data, out.ctypes.data))
+    return out
 
 
 def trace_imbalance(trace_host: np.ndarray):

@@ -362,11 +362,17 @@ size_t fva_sasa_workspace_bytes(const fva_desc* desc, const fva_grid* grid, int3
 }
 
 fva_status fva_sasa(const fva_desc* desc, const fva_grid* grid, const uint32_t* mask_in, const void* route_ws,
-                    size_t route_ws_bytes, int32_t rounds, uint32_t* mask_out, int32_t* kv_cnt, int32_t* head_xcd,
-                    int64_t* xcd_load, void* ws, size_t ws_bytes, void* stream) {
+                    size_t route_ws_bytes, int32_t rounds, const int32_t* xcd_weight, uint32_t* mask_out,
+                    int32_t* kv_cnt, int32_t* head_xcd, int64_t* xcd_load, void* ws, size_t ws_bytes, void* stream) {
   if (!mask_in || !route_ws || !mask_out || !head_xcd || !xcd_load)
     return fail(FVA_ERR_INVALID_ARG, "mask_in, route_ws, mask_out, head_xcd and xcd_load must not be null");
   if (rounds < 0 || rounds > 8) return fail(FVA_ERR_INVALID_ARG, "rounds %d outside 0..8", rounds);
+  fva::XcdWeights w;
+  for (int x = 0; x < 8; ++x) {
+    w.w[x] = xcd_weight ? xcd_weight[x] : 1000;
+    if (w.w[x] < 1 || w.w[x] > 1000000)
+      return fail(FVA_ERR_INVALID_ARG, "xcd_weight[%d] = %lld outside 1..1000000", x, (long long)w.w[x]);
+  }
   fva_status st = check_desc(desc);
   if (st != FVA_OK) return st;
   fva::Geo g;
@@ -379,13 +385,13 @@ fva_status fva_sasa(const fva_desc* desc, const fva_grid* grid, const uint32_t* 
     return fail(FVA_ERR_WORKSPACE, "route workspace holds %zu bytes, the router's is %zu", route_ws_bytes, rl.total);
   const SasaWs lay = sasa_ws_layout(desc, g, rounds);
   if ((st = check_ws(ws, ws_bytes, lay.total)) != FVA_OK) return st;
-  char* w = (char*)ws;
+  char* base = (char*)ws;
   const double* qbar = (const double*)((const char*)route_ws + rl.qbar);
   const double* kbar = (const double*)((const char*)route_ws + rl.kbar);
-  hipError_t e = fva::launch_sasa(qbar, kbar, desc->D, mask_in, g, desc->B * desc->heads, rounds,
-                                  (double*)(w + lay.s), lay.slab_tiles, mask_out, kv_cnt, head_xcd, xcd_load,
-                                  (int32_t*)(w + lay.cand), (int64_t*)(w + lay.cost), (int32_t*)(w + lay.slot),
-                                  (int32_t*)(w + lay.nh), (hipStream_t)stream);
+  hipError_t e = fva::launch_sasa(qbar, kbar, desc->D, mask_in, g, desc->B * desc->heads, rounds, w,
+                                  (double*)(base + lay.s), lay.slab_tiles, mask_out, kv_cnt, head_xcd, xcd_load,
+                                  (int32_t*)(base + lay.cand), (int64_t*)(base + lay.cost),
+                                  (int32_t*)(base + lay.slot), (int32_t*)(base + lay.nh), (hipStream_t)stream);
   if (e != hipSuccess) return device_error(e, "sasa launch");
   return ok();
 }
@@ -629,6 +635,26 @@ fva_status fva_trace_imbalance(const uint64_t* t, int32_t n_wg, double* busy_rat
   *busy_ratio = bsum > 0 ? bmax / (bsum / n) : 0.0;
   *finish_ratio = fsum > 0 ? fmax_ / (fsum / n) : 0.0;
   if (n_cu) *n_cu = (int32_t)cu.size();
+  return ok();
+}
+
+fva_status fva_trace_xcd_speed(const uint64_t* t, int32_t n_wg, const int64_t* xcd_load, int32_t* xcd_weight) {
+  if (!t || n_wg < 1 || !xcd_load || !xcd_weight) return fail(FVA_ERR_INVALID_ARG, "bad trace arguments");
+  double busy[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int i = 0; i < n_wg; ++i) {
+    const uint64_t* r = t + (size_t)i * 4;
+    if (!(r[3] >> 40)) continue;
+    busy[(r[3] >> 32) & 7] += (double)r[2];
+  }
+  double speed[8], mean = 0.0;
+  for (int x = 0; x < 8; ++x) {
+    if (busy[x] <= 0.0 || xcd_load[x] <= 0)
+      return fail(FVA_ERR_INVALID_ARG, "XCD %d has no measured work (load %lld, busy %.0f ticks)", x,
+                  (long long)xcd_load[x], busy[x]);
+    speed[x] = (double)xcd_load[x] / busy[x];
+    mean += speed[x] / 8.0;
+  }
+  for (int x = 0; x < 8; ++x) xcd_weight[x] = (int32_t)std::lround(1000.0 * speed[x] / mean);
   return ok();
 }
 

@@ -31,8 +31,12 @@ hipError_t launch_scores_slab(const double* qbar, const double* kbar, int N, int
 // Slack-aware augmentation; the scores are recomputed slab by slab from the
 // router's pooled means (fp64 [BH, N, D]) with the router's scores kernel, in
 // S (slab_tiles tiles of 64 rows).
+// Relative speeds of the 8 XCDs (per mille of the mean; all equal: unweighted).
+struct XcdWeights {
+  int64_t w[8];
+};
 hipError_t launch_sasa(const double* qbar, const double* kbar, int D, const uint32_t* mask_in, const Geo& g, int BH,
-                       int R, double* S, int64_t slab_tiles, uint32_t* mask_out,
+                       int R, const XcdWeights& w, double* S, int64_t slab_tiles, uint32_t* mask_out,
                        int32_t* kv_cnt, int32_t* head_xcd, int64_t* xcd_load, int32_t* cand, int64_t* row_cost,
                        int32_t* slot_head, int32_t* nh, hipStream_t st);
 

@@ -22,6 +22,13 @@
 //      whose summed cost r_i * ceil(c_j / 64) fits M - load_x is added to the
 //      mask.
 // The attention then runs with each XCD serving only its own heads.
+//
+// The XCDs of one MI355X need not run at one speed (measured per-XCD time per
+// unit of this cost differs by up to 9% on one box), so each XCD x may carry a
+// relative speed w_x (per mille of the mean, measured from a trace): a head
+// then goes to the XCD where it would finish first, (load_x + c) / w_x, the
+// critical XCD m is the one with the largest load_m / w_m, and XCD x's slack is
+// floor(load_m * w_x / w_m) - load_x.  All w_x equal is the unweighted rule.
 #include <algorithm>
 
 #include "fva_dev.h"
@@ -107,10 +114,11 @@ __global__ __launch_bounds__(64) void sasa_cand_kernel(const double* __restrict_
   }
 }
 
-// Heads to XCDs, longest first (one workgroup).  Writes head_xcd, the heads
-// of each XCD in assignment order (slot_head[x * BH + k]), their number
-// (nh[x]) and the XCD loads (load[x]); makespan = max load.
-__global__ __launch_bounds__(256) void sasa_lpt_kernel(const int64_t* __restrict__ row_cost, int N, int BH,
+// Heads to XCDs, longest first (one workgroup), each to the XCD where it
+// would finish first (ties: lower XCD).  Writes head_xcd, the heads of each
+// XCD in assignment order (slot_head[x * BH + k]), their number (nh[x]) and
+// the XCD loads (load[x]).
+__global__ __launch_bounds__(256) void sasa_lpt_kernel(const int64_t* __restrict__ row_cost, int N, int BH, XcdWeights w,
                                                        int32_t* __restrict__ head_xcd, int32_t* __restrict__ slot_head,
                                                        int32_t* __restrict__ nh, int64_t* __restrict__ load) {
   extern __shared__ int64_t hs[];  // [BH] head costs, then [BH] int32 order
@@ -138,10 +146,11 @@ __global__ __launch_bounds__(256) void sasa_lpt_kernel(const int64_t* __restrict
     for (int x = 0; x < SASA_NXCD; ++x) ld[x] = 0, cnt[x] = 0;
     for (int r = 0; r < BH; ++r) {
       const int hd = horder[r];
+      const int64_t c = hcost[hd];
       int best = 0;
-      for (int x = 1; x < SASA_NXCD; ++x)
-        if (ld[x] < ld[best]) best = x;
-      ld[best] += hcost[hd];
+      for (int x = 1; x < SASA_NXCD; ++x)  // (ld[x] + c) / w[x] < (ld[best] + c) / w[best]
+        if ((ld[x] + c) * w.w[best] < (ld[best] + c) * w.w[x]) best = x;
+      ld[best] += c;
       head_xcd[hd] = best;
       slot_head[best * BH + cnt[best]] = hd;
       ++cnt[best];
@@ -157,7 +166,7 @@ __global__ __launch_bounds__(256) void sasa_lpt_kernel(const int64_t* __restrict
 // inclusive prefix sum of their costs, and every offer whose prefix fits the
 // slack is added (offers without a block cost 0 and add nothing).  added[x]
 // receives the added cost.
-__global__ __launch_bounds__(1024) void sasa_take_kernel(Geo g, int words, int R, int BH,
+__global__ __launch_bounds__(1024) void sasa_take_kernel(Geo g, int words, int R, int BH, XcdWeights w,
                                                          const int32_t* __restrict__ cand,
                                                          const int32_t* __restrict__ slot_head,
                                                          const int32_t* __restrict__ nh,
@@ -168,9 +177,11 @@ __global__ __launch_bounds__(1024) void sasa_take_kernel(Geo g, int words, int R
   const int x = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int N = g.N;
-  int64_t M = 0;
-  for (int y = 0; y < SASA_NXCD; ++y) M = max(M, load[y]);
-  const int64_t slack = M - load[x];
+  // the critical XCD: largest load / weight (ties: lower XCD)
+  int m = 0;
+  for (int y = 1; y < SASA_NXCD; ++y)
+    if (load[y] * w.w[m] > load[m] * w.w[y]) m = y;
+  const int64_t slack = load[m] * w.w[x] / w.w[m] - load[x];
   const int64_t Q = (int64_t)nh[x] * N;
   const int64_t total = Q * R;
   if (tid == 0) {
@@ -218,7 +229,7 @@ __global__ __launch_bounds__(1024) void sasa_take_kernel(Geo g, int words, int R
 }
 
 hipError_t launch_sasa(const double* qbar, const double* kbar, int D, const uint32_t* mask_in, const Geo& g, int BH,
-                       int R, double* S, int64_t slab_tiles, uint32_t* mask_out, int32_t* kv_cnt, int32_t* head_xcd,
+                       int R, const XcdWeights& w, double* S, int64_t slab_tiles, uint32_t* mask_out, int32_t* kv_cnt, int32_t* head_xcd,
                        int64_t* xcd_load, int32_t* cand, int64_t* row_cost, int32_t* slot_head, int32_t* nh,
                        hipStream_t st) {
   const int words = (g.N + 31) / 32;
@@ -237,9 +248,9 @@ hipError_t launch_sasa(const double* qbar, const double* kbar, int D, const uint
     hipLaunchKernelGGL(sasa_cand_kernel, dim3((unsigned)nt * 64), dim3(64), 0, st, S, (int)t0, nIT, mask_in, g, words,
                        R, cand, row_cost, kv_cnt);
   }
-  hipLaunchKernelGGL(sasa_lpt_kernel, dim3(1), dim3(256), (size_t)BH * 12, st, row_cost, g.N, BH, head_xcd, slot_head,
+  hipLaunchKernelGGL(sasa_lpt_kernel, dim3(1), dim3(256), (size_t)BH * 12, st, row_cost, g.N, BH, w, head_xcd, slot_head,
                      nh, xcd_load);
-  hipLaunchKernelGGL(sasa_take_kernel, dim3(SASA_NXCD), dim3(1024), 0, st, g, words, R, BH, cand, slot_head, nh,
+  hipLaunchKernelGGL(sasa_take_kernel, dim3(SASA_NXCD), dim3(1024), 0, st, g, words, R, BH, w, cand, slot_head, nh,
                      xcd_load, mask_out, kv_cnt, xcd_load + SASA_NXCD);
   return hipGetLastError();
 }

@@ -311,10 +311,13 @@ def _overlap_leg(fva, wl, q, k, v, o_ref, mask_ref, args):
 
 
 def _sasa_leg(fva, wl, q, k, v, host, shape, ws_r, ws_a, stream, args):
-    """Slack-aware augmentation on the per-XCD schedule: ms/layer with and
-    without it (same timing protocol as the main loop), and the mean absolute
-    error of O against dense attention (fp64 oracle) on sampled query blocks,
-    most of them blocks that received extra key blocks."""
+    """Slack-aware augmentation on the per-XCD schedule: ms/layer without it
+    (the plan's own LPT placement), with it on equal XCDs, and with it on
+    measured XCD speeds (a traced per-XCD run under SASA's placement gives each
+    XCD's time per unit of cost; fva_trace_xcd_speed turns that into weights).
+    Same timing protocol as the main loop.  Also the mean absolute error of O
+    against dense attention (fp64 oracle) on sampled query blocks, most of them
+    blocks that received extra key blocks."""
     import torch
     import oracle
     B, L, heads, D = shape
@@ -326,35 +329,53 @@ def _sasa_leg(fva, wl, q, k, v, host, shape, ws_r, ws_a, stream, args):
     status = torch.empty((1,), dtype=torch.int32, device="cuda")
     sws = fva.workspace(fva.sasa_workspace_bytes(shape, wl.grid, wl.block, args.sasa), q.device)
 
-    def layer(aug):
+    def layer(rounds, weight):
         fva.route(q, k, wl.grid, wl.block, wl.top_p, wl.k_floor, ws=ws_r, out=(mask, cnt, status), stream=stream)
         m, hx = mask, None
-        if aug:
-            m, _, hx, _ = fva.sasa(shape, wl.grid, wl.block, mask, ws_r, rounds=args.sasa, out=(mask_s, cnt_s),
-                                   ws=sws, stream=stream)
+        if rounds is not None:
+            m, _, hx, _ = fva.sasa(shape, wl.grid, wl.block, mask, ws_r, rounds=rounds, xcd_weight=weight,
+                                   out=(mask_s, cnt_s), ws=sws, stream=stream)
         fva.attn_plan(k, v, wl.grid, wl.block, m, sched="xcd", head_xcd=hx, ws=ws_a, stream=stream)
         fva.attn_exec(q, wl.grid, wl.block, m, ws_a, sched="xcd", out=o, stream=stream)
         return m
 
-    res = {}
-    outs = {}
-    for aug in (False, True):
+    def timed(rounds, weight):
         for _ in range(args.warmup):
-            layer(aug)
+            layer(rounds, weight)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(args.steps):
-            m = layer(aug)
+            m = layer(rounds, weight)
         e1.record(stream)
         torch.cuda.synchronize()
-        res["ms_per_layer_sasa" if aug else "ms_per_layer_xcd"] = round(e0.elapsed_time(e1) / args.steps, 4)
-        outs[aug] = (o.clone(), m.clone())
-    _, _, _, load = fva.sasa(shape, wl.grid, wl.block, mask, ws_r, rounds=args.sasa, out=(mask_s, cnt_s), ws=sws)
+        return round(e0.elapsed_time(e1) / args.steps, 4), o.clone(), m.clone()
+
+    # XCD speeds: a traced per-XCD run under SASA's placement (no augmentation)
+    layer(0, None)
+    _, _, hx0, load0 = fva.sasa(shape, wl.grid, wl.block, mask, ws_r, rounds=0, out=(mask_s, cnt_s), ws=sws)
+    ws_t = fva.attn_plan(k, v, wl.grid, wl.block, mask, sched="xcd", head_xcd=hx0)
+    nwg = fva.attn_workgroups(shape, wl.grid, wl.block)
+    tr = torch.zeros(nwg * 4, dtype=torch.int64, device="cuda")
+    for _ in range(2):     # the second launch, with warm caches, is the one kept
+        fva.attn_exec(q, wl.grid, wl.block, mask, ws_t, sched="xcd", trace=tr)
+    torch.cuda.synchronize()
+    weight = fva.xcd_speed(tr.cpu().numpy(), load0.cpu().numpy())
+    del ws_t
+
+    res = {"rounds": args.sasa, "xcd_weight": weight.tolist()}
+    ms_xcd, o_xcd, m_xcd = timed(None, None)
+    ms_sasa, o_sasa, m_sasa = timed(args.sasa, None)
+    ms_place, _, _ = timed(0, weight)
+    ms_wsasa, o_wsasa, m_wsasa = timed(args.sasa, weight)
+    res.update({"ms_per_layer_xcd": ms_xcd, "ms_per_layer_sasa": ms_sasa,
+                "ms_per_layer_xcd_weighted_placement": ms_place, "ms_per_layer_sasa_weighted": ms_wsasa})
+    _, _, _, load = fva.sasa(shape, wl.grid, wl.block, mask, ws_r, rounds=args.sasa, xcd_weight=weight,
+                             out=(mask_s, cnt_s), ws=sws)
     torch.cuda.synchronize()
     ld = load.cpu().numpy()
-    kept0 = outs[False][1].cpu().numpy().view(np.uint32)
-    kept1 = outs[True][1].cpu().numpy().view(np.uint32)
+    kept0 = m_xcd.cpu().numpy().view(np.uint32)
+    kept1 = m_wsasa.cpu().numpy().view(np.uint32)
     bits = lambda m: int(np.unpackbits(m.view(np.uint8)).sum())
     grown = np.nonzero((kept1 != kept0).any(-1).reshape(-1))[0]
     rng = np.random.default_rng(2)
@@ -364,35 +385,32 @@ def _sasa_leg(fva, wl, q, k, v, host, shape, ws_r, ws_a, stream, args):
     items = np.array(sorted(pick))
     print("[bench] sasa: dense oracle on %d sampled items" % len(items), file=sys.stderr, flush=True)
     qh, kh, vh = host
-    threads = oracle.host_threads()
     dense = oracle.attn(qh, kh, vh, wl.grid, wl.block, oracle.dense_mask(B, heads, N), 1.0 / math.sqrt(D),
-                        items=items, nthreads=threads)
+                        items=items, nthreads=oracle.host_threads())
     tb = oracle.token_block(wl.grid, wl.block)
+    import fvgen
     err = {}
-    for aug in (False, True):
-        out = outs[aug][0].view(torch.int16).cpu().numpy().view(np.uint16)
-        import fvgen
-        out = fvgen.bf16_to_f64(out)
+    grown_set = set(grown.tolist())
+    for name, out in (("xcd", o_xcd), ("xcd_sasa_weighted", o_wsasa)):
+        out = fvgen.bf16_to_f64(out.view(torch.int16).cpu().numpy().view(np.uint16))
         e_all, e_grown = [], []
         for it in items:
             i, h, b = it % N, (it // N) % heads, it // (N * heads)
             d = np.abs(out[b, tb == i, h] - dense[b, tb == i, h]).mean()
             e_all.append(d)
-            if it in set(grown.tolist()):
+            if it in grown_set:
                 e_grown.append(d)
-        err[aug] = (float(np.mean(e_all)), float(np.mean(e_grown)) if e_grown else None)
+        err[name] = (float(np.mean(e_all)), float(np.mean(e_grown)) if e_grown else None)
     res.update({
-        "rounds": args.sasa,
         "xcd_load_before": [int(x) for x in ld[:8]],
         "xcd_added": [int(x) for x in ld[8:]],
         "kept_blocks_before": bits(kept0),
         "kept_blocks_after": bits(kept1),
         "rows_augmented": int(grown.size),
         "sampled_items": int(items.size),
-        "mean_abs_err_vs_dense": {"xcd": round(err[False][0], 6), "xcd_sasa": round(err[True][0], 6)},
-        "mean_abs_err_vs_dense_on_augmented_rows": {
-            "xcd": None if err[False][1] is None else round(err[False][1], 6),
-            "xcd_sasa": None if err[True][1] is None else round(err[True][1], 6)},
+        "mean_abs_err_vs_dense": {k2: round(v2[0], 6) for k2, v2 in err.items()},
+        "mean_abs_err_vs_dense_on_augmented_rows": {k2: None if v2[1] is None else round(v2[1], 6)
+                                                    for k2, v2 in err.items()},
     })
     return res
 

@@ -308,6 +308,12 @@ fva_status fva_attn_schedule(const fva_desc* desc, const fva_grid* grid, const v
  *              slab with the router's own scores kernel, bit-equal to what it
  *              routed on)
  *   rounds     0..8 (0 copies the mask)
+ *   xcd_weight nullable host int32 [8]: relative speed of each XCD (per
+ *              mille; 1..1000000), e.g. from fva_trace_xcd_speed.  A head
+ *              goes to the XCD where it would finish first, (load_x + c) /
+ *              w_x; the critical XCD m has the largest load_m / w_m; XCD x
+ *              may add up to floor(load_m * w_x / w_m) - load_x.  NULL: all
+ *              XCDs equal (the rule above).
  *   mask_out   out, same layout (may equal mask_in)
  *   kv_cnt     out, int32 [B, heads, N] kept counts after augmentation (nullable)
  *   head_xcd   out, int32 [B*heads]
@@ -318,8 +324,17 @@ fva_status fva_attn_schedule(const fva_desc* desc, const fva_grid* grid, const v
  * Errors: INVALID_ARG, SHAPE, UNSUPPORTED, WORKSPACE, DEVICE. */
 size_t fva_sasa_workspace_bytes(const fva_desc* desc, const fva_grid* grid, int32_t rounds);
 fva_status fva_sasa(const fva_desc* desc, const fva_grid* grid, const uint32_t* mask_in, const void* route_ws,
-                    size_t route_ws_bytes, int32_t rounds, uint32_t* mask_out, int32_t* kv_cnt, int32_t* head_xcd,
-                    int64_t* xcd_load, void* ws, size_t ws_bytes, void* stream);
+                    size_t route_ws_bytes, int32_t rounds, const int32_t* xcd_weight, uint32_t* mask_out,
+                    int32_t* kv_cnt, int32_t* head_xcd, int64_t* xcd_load, void* ws, size_t ws_bytes, void* stream);
+
+/* Host helper: relative speeds of the 8 XCDs for fva_sasa's xcd_weight, from
+ * a trace (copied to host memory) of the per-XCD schedule (FVA_SCHED_XCD,
+ * placed as fva_sasa placed the heads) and the cost fva_sasa assigned each
+ * XCD (xcd_load[0..7]): speed_x = xcd_load[x] / (summed item time of the
+ * workgroups on XCD x), weight_x = round(1000 * speed_x / mean speed).
+ * Returns INVALID_ARG for null pointers, n_wg < 1 or an XCD with no work. */
+fva_status fva_trace_xcd_speed(const uint64_t* host_trace, int32_t n_wg, const int64_t* xcd_load,
+                               int32_t* xcd_weight);
 
 /* Dense softmax attention over all L tokens (the FlashAttention baseline the
  * FVAttn abstract measures against), on the same kernel as fva_sparse_attn:

@@ -342,7 +342,7 @@ def sasa_key_chunks(counts):
     return (np.asarray(counts, dtype=np.int64) + 63) // 64
 
 
-def sasa(scores: np.ndarray, mask: np.ndarray, grid, block, rounds: int, margin: float = MARGIN):
+def sasa(scores: np.ndarray, mask: np.ndarray, grid, block, rounds: int, margin: float = MARGIN, xcd_weight=None):
     """Slack-aware sparse augmentation, one-GPU form (8 XCDs as the ranks).
 
     FVAttn abstract and summary, key modules 2 and 3: after load balancing the
@@ -364,6 +364,11 @@ def sasa(scores: np.ndarray, mask: np.ndarray, grid, block, rounds: int, margin:
          longer fits M - load (rows without an r-th dropped block are passed
          over).
     scores: fp64 [B, heads, N, N] (oracle.scores); mask: the routed mask.
+    xcd_weight: optional relative speed w_x of each XCD (integers); a head then
+    goes to the XCD where it would finish first, (load_x + c) / w_x (ties:
+    lower XCD), the critical XCD m has the largest load_m / w_m (ties: lower),
+    and XCD x takes offers up to floor(load_m * w_x / w_m) - load_x.  None:
+    all equal (the rule above).
     Returns (mask_out, counts, head_xcd [B*heads], load [8], added [8],
     flags [B, heads, N]) where a flagged row has two of its first rounds+1
     dropped candidates within margin * max(1, |s|) of each other without being
@@ -378,15 +383,24 @@ def sasa(scores: np.ndarray, mask: np.ndarray, grid, block, rounds: int, margin:
     S = scores.reshape(BH, N, N)
     row_cost = rate[None, :] * (keep * chunks[None, None, :]).sum(-1)
     head_cost = row_cost.sum(1)
+    w = [1000] * 8 if xcd_weight is None else [int(v) for v in xcd_weight]
     load = [0] * 8
     heads_of = [[] for _ in range(8)]
     head_xcd = np.zeros(BH, dtype=np.int32)
     for h in sorted(range(BH), key=lambda h: (-int(head_cost[h]), h)):
-        x = min(range(8), key=lambda x: (load[x], x))
-        load[x] += int(head_cost[h])
+        cst = int(head_cost[h])
+        # the XCD where the head would finish first: compare (load + c) / w by cross-multiplying
+        x = 0
+        for y in range(1, 8):
+            if (load[y] + cst) * w[x] < (load[x] + cst) * w[y]:
+                x = y
+        load[x] += cst
         heads_of[x].append(h)
         head_xcd[h] = x
-    M = max(load)
+    m = 0
+    for y in range(1, 8):
+        if load[y] * w[m] > load[m] * w[y]:
+            m = y
 
     # each row's first rounds+1 dropped blocks in the router's order
     cand = np.full((BH, N, rounds + 1), -1, dtype=np.int64)
@@ -405,7 +419,7 @@ def sasa(scores: np.ndarray, mask: np.ndarray, grid, block, rounds: int, margin:
     out = keep.copy()
     added = [0] * 8
     for x in range(8):
-        slack = M - load[x]
+        slack = load[m] * w[x] // w[m] - load[x]
         acc = 0
         stop = False
         for r in range(rounds):

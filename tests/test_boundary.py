@@ -261,3 +261,21 @@ def test_routed_attn_host_validation_and_workspace():
     assert call(ws_bytes=three - 1, groups=3) == 5 and "needed" in _err()
     # one stream: one set suffices, so a two-set workspace minus a byte still covers it
     assert call(ws_bytes=three // 2 - 1, groups=3, side=None) == 5
+
+
+def test_trace_xcd_speed_host_helper():
+    import numpy as np
+    # 16 workgroups, 2 per XCD; XCD x does load 1000*(x+1) in busy time 10*(x+1)*(1 + x/100) ticks
+    recs = []
+    for x in range(8):
+        busy = 10.0 * (x + 1) * (1 + x / 100.0) * 1000
+        for _ in range(2):
+            recs.append([0, 1, int(busy / 2), (1 << 40) | (x << 32)])
+    t = np.array(recs, dtype=np.uint64)
+    load = np.array([1000 * (x + 1) for x in range(8)], dtype=np.int64)
+    w = fva.xcd_speed(t, load)
+    speed = np.array([1.0 / (1 + x / 100.0) for x in range(8)])
+    assert w.tolist() == np.round(1000 * speed / speed.mean()).astype(int).tolist()
+    load[3] = 0
+    with pytest.raises(fva.FvaError, match="XCD 3 has no measured work"):
+        fva.xcd_speed(t, load)

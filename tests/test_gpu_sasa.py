@@ -29,11 +29,11 @@ CASES = [_wl("h12", 12, (9, 17, 23), (4, 8, 8), 0.8, 2), _wl("h11_small", 11, (6
          fvgen.WORKLOADS["wan14b"], fvgen.WORKLOADS["720p"]]
 
 
-def _gpu_sasa(wl, qd, kd, rounds):
+def _gpu_sasa(wl, qd, kd, rounds, xcd_weight=None):
     shape = tuple(qd.shape)
     ws_r = fva.workspace(fva.route_workspace_bytes(shape, wl.grid, wl.block), qd.device)
     mask, _, _ = fva.route(qd, kd, wl.grid, wl.block, wl.top_p, wl.k_floor, ws=ws_r)
-    mo, cnt, hx, load = fva.sasa(shape, wl.grid, wl.block, mask, ws_r, rounds=rounds)
+    mo, cnt, hx, load = fva.sasa(shape, wl.grid, wl.block, mask, ws_r, rounds=rounds, xcd_weight=xcd_weight)
     torch.cuda.synchronize()
     return mask, mo, cnt, hx, load
 
@@ -56,6 +56,31 @@ def test_sasa_matches_oracle(wl):
     assert np.array_equal(hx_g.cpu().numpy(), hx)
     lg = load_g.cpu().numpy()
     assert np.array_equal(lg[:8], load) and np.array_equal(lg[8:], added)
+
+
+W8 = [1000, 1040, 960, 1000, 1090, 920, 1010, 980]
+
+
+@pytest.mark.parametrize("wl", [CASES[0], CASES[2], CASES[3]], ids=lambda w: w.name)
+def test_sasa_weighted_matches_oracle(wl):
+    """XCDs of unequal speed (xcd_weight): mask, counts, placement and loads
+    bit-exact against the oracle's weighted rule."""
+    q, k, v = fvgen.generate_qkv(wl)
+    qd, kd = _dev(q), _dev(k)
+    mask_g, mo_g, cnt_g, hx_g, load_g = _gpu_sasa(wl, qd, kd, 4, xcd_weight=W8)
+    S = oracle.scores(oracle.pool(q, wl.grid, wl.block), oracle.pool(k, wl.grid, wl.block))
+    mask_o, _, rflags, _ = oracle.route(q, k, wl.grid, wl.block, wl.top_p, wl.k_floor, margin=1e-10)
+    mo, co, hx, load, added, sflags = oracle.sasa(S, mask_o, wl.grid, wl.block, 4, margin=1e-10, xcd_weight=W8)
+    print("\n[%s weighted] loads %s added %s" % (wl.name, load.tolist(), added.tolist()), flush=True)
+    assert not (rflags != 0).any() and not sflags.any()
+    assert np.array_equal(mo_g.cpu().numpy().view(np.uint32), mo)
+    assert np.array_equal(cnt_g.cpu().numpy(), co)
+    assert np.array_equal(hx_g.cpu().numpy(), hx)
+    lg = load_g.cpu().numpy()
+    assert np.array_equal(lg[:8], load) and np.array_equal(lg[8:], added)
+    with pytest.raises(fva.FvaError, match="xcd_weight"):
+        fva.sasa(tuple(qd.shape), wl.grid, wl.block, mask_g, fva.workspace(
+            fva.route_workspace_bytes(tuple(qd.shape), wl.grid, wl.block), "cuda"), rounds=1, xcd_weight=[0] * 8)
 
 
 @pytest.mark.parametrize("wl", [CASES[0], CASES[2]], ids=lambda w: w.name)

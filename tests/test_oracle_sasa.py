@@ -111,3 +111,48 @@ def test_time_model_rates():
     assert oracle.sasa_row_rate([256, 224, 192, 160, 144, 128, 96, 64, 40, 32]).tolist() == \
         [4, 4, 3, 3, 3, 2, 2, 1, 1, 1]
     assert oracle.sasa_key_chunks([256, 192, 144, 64, 40]).tolist() == [4, 3, 3, 1, 1]
+
+
+W8 = [1000, 1040, 960, 1000, 1090, 920, 1010, 980]
+
+
+@pytest.mark.parametrize("wl", CASES[:2], ids=lambda w: w.name)
+def test_weighted_xcds(wl):
+    """XCDs of unequal speed w_x: every head went to the XCD where it finished
+    first at the time (replayed here), nothing is added to the critical XCD
+    (largest load/w), no XCD passes the critical time ((load + added) / w <=
+    load_m / w_m), and an XCD that did not run out of offers has less weighted
+    slack left than the largest offer; equal weights give the unweighted result."""
+    S, mask = _routed(wl)
+    rounds = 4
+    B, H, N, _ = S.shape
+    mo, co, hx, load, added, flags = oracle.sasa(S, mask, wl.grid, wl.block, rounds, xcd_weight=W8)
+    keep = oracle.mask_to_bool(mask, N).reshape(B * H, N, N)
+    c = oracle.block_table(wl.grid, wl.block)[:, 6].astype(np.int64)
+    cost = np.array([[(((ci + 31) // 32 + 1) // 2) * ((cj + 63) // 64) for cj in c] for ci in c], dtype=np.int64)
+    head_cost = (keep * cost[None]).sum((1, 2))
+    ld = [0] * 8
+    for h in sorted(range(B * H), key=lambda h: (-int(head_cost[h]), h)):
+        finish = [(ld[x] + int(head_cost[h])) / W8[x] for x in range(8)]
+        best = min(range(8), key=lambda x: (finish[x], x))
+        assert hx[h] == best
+        ld[best] += int(head_cost[h])
+    assert ld == load.tolist()
+    m = max(range(8), key=lambda x: (load[x] / W8[x], -x))
+    assert added[m] == 0
+    for x in range(8):
+        assert (load[x] + added[x]) * W8[m] <= load[m] * W8[x]
+    out = oracle.mask_to_bool(mo, N).reshape(B * H, N, N)
+    new = out & ~keep
+    biggest = int(cost.max())
+    for x in range(8):
+        rows_x = [h for h in range(B * H) if hx[h] == x]
+        dropped = sum(int(min(rounds, (~keep[h]).sum(-1)[i])) for h in rows_x for i in range(N))
+        taken = int(sum(new[h].sum() for h in rows_x))
+        if taken < dropped:
+            assert load[m] * W8[x] // W8[m] - (load[x] + added[x]) < biggest
+    # a different placement than the unweighted one, and equal weights reproduce it
+    plain = oracle.sasa(S, mask, wl.grid, wl.block, rounds)
+    same = oracle.sasa(S, mask, wl.grid, wl.block, rounds, xcd_weight=[7] * 8)
+    for a, b in zip(plain, same):
+        assert np.array_equal(a, b)
