@@ -97,7 +97,7 @@ int32_t fva_num_blocks(const fva_grid* grid);
 /* Device workspace fva_route needs, or 0 for invalid arguments: the pooled
  * Q and K (fp64 [B*heads, N, D] each) and one slab of fp64 block scores.
  * The scores are computed and routed in tiles of 64 query blocks of one
- * head, as many tiles at a time as fit 128 MiB (at least one), so the whole
+ * head, as many tiles at a time as fit 512 MiB (at least one), so the whole
  * [B*heads, N, N] score matrix is never held.  Host only. */
 size_t fva_route_workspace_bytes(const fva_desc* desc, const fva_grid* grid);
 
