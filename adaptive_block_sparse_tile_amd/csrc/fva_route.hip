@@ -111,59 +111,79 @@ __global__ __launch_bounds__(256) void pool_kernel(const bf16_bits* __restrict__
 // head); a slab is the tiles t0 .. t0 + gridDim.y - 1, and its scores go to
 // S[(tile - t0) * 64 + i % 64][j] (rows past N in a head's last tile are
 // left unwritten).  grid = (ceil(N/64) key tiles, tiles in the slab), 256
-// threads, each a 4x4 set of outputs i = i0 + ty + 16a, j = j0 + tx + 16c.
-// The dot product runs over d in increasing order for every (i, j), so equal
+// threads.  fp64 matrix cores: wavefront w computes the 16 x 64 scores of
+// query rows i0 + 16w .. + 15 as four 16 x 16 tiles of v_mfma_f64_16x16x4,
+// with the 64 x 32 slices of Qbar and Kbar for each 32 channels staged in
+// LDS.  Every (i, j) is summed over d in the same order (slices in order,
+// steps of 4 channels in order, the instruction's fixed 4-term sum), so equal
 // key blocks get bit-equal scores (exact ties stay exact).
 // ---------------------------------------------------------------------------
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+typedef double f64x2 __attribute__((ext_vector_type(2)));
+
 __global__ __launch_bounds__(256) void scores_kernel(const double* __restrict__ qbar, const double* __restrict__ kbar,
                                                      int N, int D, int t0, int nIT, double* __restrict__ S) {
   __shared__ double As[64][33];
   __shared__ double Bs[64][33];
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r16 = lane & 15, g = lane >> 4;
   const int tile = t0 + blockIdx.y;
   const int64_t bh = tile / nIT;
   const int i0 = (tile % nIT) * 64, j0 = blockIdx.x * 64;
   const double* qa = qbar + bh * N * D;
   const double* kb = kbar + bh * N * D;
-  double acc[4][4];
+  f64x4 acc[4];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) acc[a][c] = 0.0;
+  for (int t = 0; t < 4; ++t) acc[t] = f64x4{0.0, 0.0, 0.0, 0.0};
 
-  for (int d0 = 0; d0 < D; d0 += 32) {
+  // staging: thread loads rows lr + 16u (u = 0..3) of both slices, channels
+  // lc, lc + 1 as one 16-byte load; rows past N read row N - 1 and store 0
+  const int lr = threadIdx.x >> 4, lc = (threadIdx.x & 15) * 2;
+  f64x2 ra[4], rb[4];
+  auto load = [&](int d0) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int e = threadIdx.x + u * 256;  // 0..2047
-      const int r = e >> 5, c = e & 31;
-      As[r][c] = (i0 + r < N) ? qa[(int64_t)(i0 + r) * D + d0 + c] : 0.0;
-      Bs[r][c] = (j0 + r < N) ? kb[(int64_t)(j0 + r) * D + d0 + c] : 0.0;
+    for (int u = 0; u < 4; ++u) {
+      const int row = lr + 16 * u;
+      ra[u] = *(const f64x2*)(qa + (int64_t)min(i0 + row, N - 1) * D + d0 + lc);
+      rb[u] = *(const f64x2*)(kb + (int64_t)min(j0 + row, N - 1) * D + d0 + lc);
     }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int row = lr + 16 * u;
+      const bool qa_in = i0 + row < N, kb_in = j0 + row < N;
+      As[row][lc] = qa_in ? ra[u].x : 0.0;
+      As[row][lc + 1] = qa_in ? ra[u].y : 0.0;
+      Bs[row][lc] = kb_in ? rb[u].x : 0.0;
+      Bs[row][lc + 1] = kb_in ? rb[u].y : 0.0;
+    }
+  };
+  load(0);
+  for (int d0 = 0; d0 < D; d0 += 32) {
+    store();
     __syncthreads();
-#pragma unroll 8
-    for (int kk = 0; kk < 32; ++kk) {
-      double av[4], bv[4];
+    if (d0 + 32 < D) load(d0 + 32);  // in flight under this slice's products
 #pragma unroll
-      for (int a = 0; a < 4; ++a) av[a] = As[ty + 16 * a][kk];
+    for (int s = 0; s < 8; ++s) {
+      // A: lane holds Qbar[16w + lane % 16][4s + lane / 16]; B: Kbar[16t + lane % 16][4s + lane / 16]
+      const double a = As[16 * w + r16][4 * s + g];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) bv[c] = Bs[tx + 16 * c][kk];
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc[a][c] = fma(av[a], bv[c], acc[a][c]);
+      for (int t = 0; t < 4; ++t)
+        acc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, Bs[16 * t + r16][4 * s + g], acc[t], 0, 0, 0);
     }
     __syncthreads();
   }
+  // D of tile t: lane holds rows 4v + lane / 16, v = 0..3, column lane % 16
   const double rs = sqrt((double)D);
   double* out = S + (int64_t)blockIdx.y * 64 * N;
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const int r = ty + 16 * a;
-    if (i0 + r >= N) continue;
+  for (int t = 0; t < 4; ++t) {
+    const int j = j0 + 16 * t + r16;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int j = j0 + tx + 16 * c;
-      if (j < N) out[(int64_t)r * N + j] = acc[a][c] / rs;
+    for (int v = 0; v < 4; ++v) {
+      const int r = 16 * w + 4 * v + g;
+      if (i0 + r < N && j < N) out[(int64_t)r * N + j] = acc[t][v] / rs;
     }
   }
 }
@@ -360,13 +380,24 @@ __global__ __launch_bounds__(THREADS) void route_rows_kernel(const double* __res
 //        bisecting the key for the largest K with mass(key >= K) >= p,
 //   the kept set = the top `keep` blocks is found by bisecting the key for the
 //        largest K with count(key >= K) >= keep, ties taken in index order.
-// Every sum is a per-lane sequential sum in index order followed by a fixed
-// tree over lanes and wavefronts, so results do not depend on timing.
+// The bisections split the scores' values (not the key codes) and, once few
+// blocks are left inside the bracket, pass over those blocks only.  Every
+// sum is a per-lane sequential sum in a fixed order followed by a fixed tree
+// over lanes and wavefronts, so results do not depend on timing.
 // ---------------------------------------------------------------------------
 __device__ inline uint64_t order_key(double d) {
   const uint64_t b = (uint64_t)__double_as_longlong(d);
   return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
 }
+// the double whose order_key is k
+__device__ inline double key_value(uint64_t k) {
+  const uint64_t b = (k >> 63) ? (k & 0x7fffffffffffffffull) : ~k;
+  return __longlong_as_double((long long)b);
+}
+// candidates per lane kept after a select bracket is compacted
+constexpr int kCand = 4;
+// passes of a select search that split the scores' values
+constexpr int kValueSteps = 40;
 
 // Wavefront reductions for the select kernel: four DPP steps (lane xor 1 and
 // xor 2 inside quads, then the 8- and 16-lane mirrors) leave every lane of a
@@ -473,6 +504,16 @@ struct GroupRed {
     *total = c;
     return r;
   }
+  // a count that is already uniform in each wavefront, summed over wavefronts
+  __device__ uint32_t reduce_count(uint32_t wave_count) {
+    uint64_t* buf = slot + flip * 8;
+    if ((threadIdx.x & 63) == 0) buf[threadIdx.x >> 6] = wave_count;
+    __syncthreads();
+    uint32_t c = (uint32_t)buf[0];
+    for (int i = 1; i < nwaves; ++i) c += (uint32_t)buf[i];
+    flip ^= 1;
+    return c;
+  }
   __device__ static uint64_t to_bits(double x) { return (uint64_t)__double_as_longlong(x); }
   __device__ static uint64_t to_bits(uint64_t x) { return x; }
   __device__ static uint64_t to_bits(uint32_t x) { return x; }
@@ -544,43 +585,178 @@ __global__ __launch_bounds__(256) void route_select_kernel(const double* __restr
       kmax = key[e] > kmax ? key[e] : kmax;
     }
   gr.reduce2(&kmin, &kmax, MinOp(), MaxOp());
-  // mass and count of the blocks with key >= K (fixed summation order)
-  // (A block past N has key 0, below the key of every finite score, and every
-  // K searched is at least kmin, so it never counts.)  The mass adds
+
+  // Candidates of a search bracket [lo, hi) once it holds at most kCand per
+  // lane: copied out of the 32 per-lane registers into LDS (wavefronts in
+  // order, then register slot, then lane), then kCand per lane (entries tid,
+  // tid + threads, ...), padding with key 0 (below every finite score) and
+  // probability 0.
+  __shared__ uint64_t cand_key[kCand * 256];
+  __shared__ double cand_pr[kCand * 256];
+  __shared__ uint32_t wt[4];
+  const int lane = tid & 63, wave = tid >> 6;
+  const int threads = blockDim.x;
+  uint64_t ck[kCand];
+  double cp[kCand];
+  // exclusive prefix over the workgroup of a per-lane count (lanes in order)
+  auto exclusive_prefix = [&](uint32_t mine) -> uint32_t {
+    uint32_t incl = mine;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t o = __shfl_up(incl, off);
+      if (lane >= off) incl += o;
+    }
+    __syncthreads();
+    if (lane == 63) wt[wave] = incl;
+    __syncthreads();
+    uint32_t r = incl - mine;
+    for (int w = 0; w < wave; ++w) r += wt[w];
+    return r;
+  };
+  auto compact = [&](uint64_t lo, uint64_t hi, uint32_t total) {
+    // order: wavefronts in order, then slot e, then lanes; each wavefront's
+    // offset comes from its count, a position from the lanes below it
+    uint32_t mine = 0;  // uniform in the wavefront
+#pragma unroll
+    for (int e = 0; e < 32; ++e) mine += (uint32_t)__popcll(__ballot(key[e] >= lo && key[e] < hi));
+    __syncthreads();
+    if (lane == 0) wt[wave] = mine;
+    __syncthreads();
+    uint32_t base = 0;
+    for (int w = 0; w < wave; ++w) base += wt[w];
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      const bool in = key[e] >= lo && key[e] < hi;
+      const uint64_t bal = __ballot(in);
+      if (in) {
+        const uint32_t pos = base + (uint32_t)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                                        __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+        cand_key[pos] = key[e];
+        cand_pr[pos] = pr[e];
+      }
+      base += (uint32_t)__popcll(bal);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kCand; ++r) {
+      const uint32_t idx = (uint32_t)(tid + r * threads);
+      ck[r] = idx < total ? cand_key[idx] : 0ull;
+      cp[r] = idx < total ? cand_pr[idx] : 0.0;
+    }
+    __syncthreads();  // the arrays are rewritten by the next compaction
+  };
+  // Mass (when with_mass) and count of the blocks with key >= K, over the
+  // registers or over the compacted candidates (then without the blocks at
+  // or above the bracket's top, which the caller adds).  A block past N has
+  // key 0 and never counts (every K searched is at least kmin).  The mass adds
   // fma(sel, pr, m) with sel 1 or 0, the same bits as adding the selected
   // probability; each wavefront's count comes from the lane masks of the
   // comparisons (scalar popcounts), so only the mass is reduced across lanes.
-  auto mass_count_ge = [&](uint64_t K, uint32_t* cnt) -> double {
+  auto mass_count_ge = [&](uint64_t K, bool compacted, bool with_mass, uint32_t* cnt) -> double {
     double m = 0.0;
     uint32_t c = 0;  // uniform in the wavefront
+    if (!compacted) {
 #pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      const bool ge = key[e] >= K;
-      m = fma(ge ? 1.0 : 0.0, pr[e], m);
-      c += (uint32_t)__popcll(__ballot(ge));
+      for (int e = 0; e < 32; ++e) {
+        const bool ge = key[e] >= K;
+        if (with_mass) m = fma(ge ? 1.0 : 0.0, pr[e], m);
+        c += (uint32_t)__popcll(__ballot(ge));
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < kCand; ++r) {
+        const bool ge = ck[r] >= K;
+        if (with_mass) m = fma(ge ? 1.0 : 0.0, cp[r], m);
+        c += (uint32_t)__popcll(__ballot(ge));
+      }
     }
-    return gr.reduce_sum_count(m, c, cnt);
+    if (with_mass) return gr.reduce_sum_count(m, c, cnt);
+    *cnt = gr.reduce_count(c);
+    return 0.0;
   };
   // the only key in [lo, hi) (callers know there is exactly one)
-  auto only_key_in = [&](uint64_t lo, uint64_t hi) -> uint64_t {
+  auto only_key_in = [&](uint64_t lo, uint64_t hi, bool compacted) -> uint64_t {
     uint64_t k = 0;
+    if (!compacted) {
 #pragma unroll
-    for (int e = 0; e < 32; ++e)
-      if (j0 + e < N && key[e] >= lo && key[e] < hi) k = key[e];
+      for (int e = 0; e < 32; ++e)
+        if (key[e] >= lo && key[e] < hi) k = key[e];
+    } else {
+#pragma unroll
+      for (int r = 0; r < kCand; ++r)
+        if (ck[r] >= lo && ck[r] < hi) k = ck[r];
+    }
     return gr.reduce(k, MaxOp());
   };
+  // Bisection of the key range for the largest K with pred(K): pred holds at
+  // lo and fails at hi, with the counts of keys >= lo and >= hi (and, for the
+  // mass search, the mass at hi) at hand.  The pivot halves the scores
+  // between the bracket's ends (keys that order doubles leave long runs of
+  // unused codes between the exponents of the scores present); it falls back
+  // to the middle key when that is not strictly inside.  Once the bracket
+  // holds at most kCand blocks per lane they are compacted and later passes
+  // touch only them.  Once a single key lies in [lo, hi), that key is the
+  // answer and the search stops (otherwise it runs until hi = lo + 1).  At
+  // the end no key lies in (lo, hi), so "keys > lo" are exactly "keys >= hi".
+  auto search = [&](bool with_mass, double target, uint64_t& lo, uint64_t& hi, uint32_t& c_lo, uint32_t& c_hi,
+                    double& m_hi) {
+    // the value midpoint for the first kValueSteps passes (two distinct
+    // scores close to zero could take a thousand value halvings to part),
+    // then the key midpoint, which ends within 64 more
+    int steps = 0;
+    auto pivot = [&]() -> uint64_t {
+      if (steps++ < kValueSteps) {
+        const double a = key_value(lo), b = key_value(hi);
+        const uint64_t mid = order_key(a + (b - a) * 0.5);
+        if (mid > lo && mid < hi) return mid;
+      }
+      return lo + (hi - lo) / 2;
+    };
+    auto step = [&](uint64_t mid, double m, uint32_t c_mid) {
+      if (with_mass ? m >= target : c_mid >= (uint32_t)target) {
+        lo = mid;
+        c_lo = c_mid;
+      } else {
+        hi = mid;
+        c_hi = c_mid;
+        m_hi = m;
+      }
+    };
+    // passes over all blocks while the bracket holds more than kCand per lane
+    while (hi - lo > 1 && c_lo - c_hi > (uint32_t)(kCand * threads)) {
+      const uint64_t mid = pivot();
+      uint32_t c_mid;
+      const double m = mass_count_ge(mid, false, with_mass, &c_mid);
+      step(mid, m, c_mid);
+    }
+    if (hi - lo <= 1) return;
+    if (c_lo - c_hi == 1) {
+      lo = only_key_in(lo, hi, false);
+      return;
+    }
+    // then over the compacted candidates, adding what lies at or above the top
+    compact(lo, hi, c_lo - c_hi);
+    const double m_above = m_hi;
+    const uint32_t c_above = c_hi;
+    while (hi - lo > 1) {
+      if (c_lo - c_hi == 1) {
+        lo = only_key_in(lo, hi, true);
+        return;
+      }
+      const uint64_t mid = pivot();
+      uint32_t c_mid;
+      const double m = m_above + mass_count_ge(mid, true, with_mass, &c_mid);
+      step(mid, m, c_mid + c_above);
+    }
+  };
 
-  // Both searches bisect the key range [lo, hi] keeping a predicate true at
-  // lo and false at hi, with the counts of keys >= lo and >= hi at hand:
-  // once a single key lies in [lo, hi), that key is the answer and the
-  // search stops (otherwise it runs until hi = lo + 1).  At the end no key
-  // lies in (lo, hi), so "keys > lo" are exactly "keys >= hi".
   const double p = (double)top_p;
   uint32_t n_real = 0;
-  const double total = mass_count_ge(kmin, &n_real);
+  const double total = mass_count_ge(kmin, false, true, &n_real);
   int nstar;
   uint64_t cut = 0;        // crossing key of the Top-p search
   uint32_t cut_above = 0;  // blocks with key > cut
+  uint32_t cut_at = 0;     // blocks with key >= cut
   bool have_cut = false;
   if (p >= 1.0) {
     nstar = N;
@@ -592,7 +768,7 @@ __global__ __launch_bounds__(256) void route_select_kernel(const double* __restr
     // largest K with mass(key >= K) >= p: the key of the crossing block
     uint64_t lo = kmin, hi = kmax;
     uint32_t c_lo = n_real, c_hi = 0;
-    double m_hi = mass_count_ge(hi, &c_hi);
+    double m_hi = mass_count_ge(hi, false, true, &c_hi);
     double above;
     uint32_t n_above;
     if (m_hi >= p) {
@@ -601,23 +777,7 @@ __global__ __launch_bounds__(256) void route_select_kernel(const double* __restr
       above = 0.0;  // nothing above the largest key
       n_above = 0;
     } else {
-      while (hi - lo > 1) {
-        if (c_lo - c_hi == 1) {
-          lo = only_key_in(lo, hi);
-          break;
-        }
-        const uint64_t mid = lo + (hi - lo) / 2;
-        uint32_t c_mid;
-        const double m = mass_count_ge(mid, &c_mid);
-        if (m >= p) {
-          lo = mid;
-          c_lo = c_mid;
-        } else {
-          hi = mid;
-          c_hi = c_mid;
-          m_hi = m;
-        }
-      }
+      search(true, p, lo, hi, c_lo, c_hi, m_hi);
       above = m_hi;
       n_above = c_hi;
     }
@@ -638,6 +798,7 @@ __global__ __launch_bounds__(256) void route_select_kernel(const double* __restr
     nstar = (int)n_above + need;
     cut = lo;
     cut_above = n_above;
+    cut_at = c_lo;
     have_cut = true;
   }
   const int keep = min(N, max(k_floor, nstar));
@@ -647,37 +808,31 @@ __global__ __launch_bounds__(256) void route_select_kernel(const double* __restr
     const int nb = min(32, N - j0);
     word = nb >= 32 ? 0xffffffffu : (nb > 0 ? ((1u << nb) - 1u) : 0u);
   } else {
-    // largest K with count(key >= K) >= keep; when the floor does not bind,
-    // that is the Top-p crossing key itself
+    // largest K with count(key >= K) >= keep: the Top-p crossing key itself
+    // when the floor does not reach below its ties, else a key below it
     uint64_t lo = kmin;
     uint32_t n_above;
-    if (have_cut && keep == nstar) {
+    if (have_cut && cut_at >= (uint32_t)keep) {
       lo = cut;
       n_above = cut_above;
     } else {
       uint64_t hi = kmax;
       uint32_t c_lo = n_real, c_hi = 0;
-      mass_count_ge(hi, &c_hi);
-      if (c_hi >= (uint32_t)keep) {
-        lo = hi;
-        n_above = 0;
+      double m_unused = 0.0;
+      bool done = false;
+      if (have_cut) {
+        hi = cut;
+        c_hi = cut_at;
       } else {
-        while (hi - lo > 1) {
-          if (c_lo - c_hi == 1) {
-            lo = only_key_in(lo, hi);
-            break;
-          }
-          const uint64_t mid = lo + (hi - lo) / 2;
-          uint32_t c_mid;
-          mass_count_ge(mid, &c_mid);
-          if (c_mid >= (uint32_t)keep) {
-            lo = mid;
-            c_lo = c_mid;
-          } else {
-            hi = mid;
-            c_hi = c_mid;
-          }
+        mass_count_ge(hi, false, false, &c_hi);
+        if (c_hi >= (uint32_t)keep) {
+          lo = hi;
+          n_above = 0;
+          done = true;
         }
+      }
+      if (!done) {
+        search(false, (double)keep, lo, hi, c_lo, c_hi, m_unused);
         n_above = c_hi;
       }
     }
@@ -686,19 +841,7 @@ __global__ __launch_bounds__(256) void route_select_kernel(const double* __restr
     uint32_t my_ties = 0;
 #pragma unroll
     for (int e = 0; e < 32; ++e) my_ties += (j0 + e < N && key[e] == lo) ? 1u : 0u;
-    uint32_t incl = my_ties;
-    const int lane = tid & 63, wave = tid >> 6;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t o = __shfl_up(incl, off);
-      if (lane >= off) incl += o;
-    }
-    __shared__ uint32_t wt[4];
-    __syncthreads();
-    if (lane == 63) wt[wave] = incl;
-    __syncthreads();
-    uint32_t rank = incl - my_ties;
-    for (int w = 0; w < wave; ++w) rank += wt[w];
+    uint32_t rank = exclusive_prefix(my_ties);
 #pragma unroll
     for (int e = 0; e < 32; ++e) {
       const int j = j0 + e;
