@@ -524,7 +524,11 @@ struct GroupRed {
   }
 };
 
-__global__ __launch_bounds__(256) void route_select_kernel(const double* __restrict__ S, int N, int words, int t0,
+// Three wavefronts per SIMD (at most 168 registers): the 32 keys and
+// probabilities per lane take 128, and the passes are bound by latency
+// (reductions and a barrier each), so the extra occupancy is worth the few
+// registers the compiler moves to scratch (long video 640 -> 525 us per slab).
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void route_select_kernel(const double* __restrict__ S, int N, int words, int t0,
                                                            int nIT, Heads hd, float top_p, int k_floor,
                                                            uint32_t* __restrict__ mask,
                                                            int32_t* __restrict__ kv_cnt,
@@ -545,13 +549,12 @@ __global__ __launch_bounds__(256) void route_select_kernel(const double* __restr
   double lmax = -INFINITY;
 #pragma unroll
   for (int e = 0; e < 32; ++e) {
+    // blocks past N read block N - 1 and hold -inf (their exp below is 0)
     const int j = j0 + e;
-    double v = -INFINITY;
-    if (j < N) {
-      v = s[j];
-      if (!isfinite(v)) bad = true;
-      lmax = fmax(lmax, v);
-    }
+    const double x = s[min(j, N - 1)];
+    const double v = j < N ? x : -INFINITY;
+    bad = bad || (j < N && !isfinite(x));
+    lmax = fmax(lmax, v);
     pr[e] = v;
   }
   if (__syncthreads_or(bad)) {
@@ -571,7 +574,7 @@ __global__ __launch_bounds__(256) void route_select_kernel(const double* __restr
   for (int e = 0; e < 32; ++e) {
     const bool in = j0 + e < N;
     key[e] = in ? order_key(pr[e]) : 0ull;  // below every finite score
-    pr[e] = in ? exp(pr[e] - M) : 0.0;
+    pr[e] = exp(pr[e] - M);                 // -inf - M: exactly 0
     lz += pr[e];
   }
   const double Z = gr.reduce(lz, AddOp());
@@ -648,30 +651,32 @@ __global__ __launch_bounds__(256) void route_select_kernel(const double* __restr
   // Mass (when with_mass) and count of the blocks with key >= K, over the
   // registers or over the compacted candidates (then without the blocks at
   // or above the bracket's top, which the caller adds).  A block past N has
-  // key 0 and never counts (every K searched is at least kmin).  The mass adds
-  // fma(sel, pr, m) with sel 1 or 0, the same bits as adding the selected
-  // probability; each wavefront's count comes from the lane masks of the
-  // comparisons (scalar popcounts), so only the mass is reduced across lanes.
+  // key 0 and never counts (every K searched is at least kmin).  A lane adds
+  // fma(sel, pr, m) with sel 1 or 0 (the same bits as adding the selected
+  // probability) into four partial sums by register slot mod 4, then (m0 +
+  // m1) + (m2 + m3); the lane counts and masses are then summed over lanes
+  // by fixed trees and over wavefronts in order.
   auto mass_count_ge = [&](uint64_t K, bool compacted, bool with_mass, uint32_t* cnt) -> double {
-    double m = 0.0;
-    uint32_t c = 0;  // uniform in the wavefront
+    double m4[4] = {0.0, 0.0, 0.0, 0.0};
+    uint32_t c = 0;
     if (!compacted) {
 #pragma unroll
       for (int e = 0; e < 32; ++e) {
         const bool ge = key[e] >= K;
-        if (with_mass) m = fma(ge ? 1.0 : 0.0, pr[e], m);
-        c += (uint32_t)__popcll(__ballot(ge));
+        if (with_mass) m4[e & 3] = fma(ge ? 1.0 : 0.0, pr[e], m4[e & 3]);
+        c += ge ? 1u : 0u;
       }
     } else {
 #pragma unroll
       for (int r = 0; r < kCand; ++r) {
         const bool ge = ck[r] >= K;
-        if (with_mass) m = fma(ge ? 1.0 : 0.0, cp[r], m);
-        c += (uint32_t)__popcll(__ballot(ge));
+        if (with_mass) m4[r & 3] = fma(ge ? 1.0 : 0.0, cp[r], m4[r & 3]);
+        c += ge ? 1u : 0u;
       }
     }
-    if (with_mass) return gr.reduce_sum_count(m, c, cnt);
-    *cnt = gr.reduce_count(c);
+    const uint32_t wc = wave_reduce(c, AddOp());
+    if (with_mass) return gr.reduce_sum_count((m4[0] + m4[1]) + (m4[2] + m4[3]), wc, cnt);
+    *cnt = gr.reduce_count(wc);
     return 0.0;
   };
   // the only key in [lo, hi) (callers know there is exactly one)
