@@ -114,13 +114,14 @@ __global__ __launch_bounds__(64) void sasa_cand_kernel(const double* __restrict_
   }
 }
 
-// Heads to XCDs, longest first (one workgroup), each to the XCD where it
-// would finish first (ties: lower XCD).  Writes head_xcd, the heads of each
-// XCD in assignment order (slot_head[x * BH + k]), their number (nh[x]) and
-// the XCD loads (load[x]).
-__global__ __launch_bounds__(256) void sasa_lpt_kernel(const int64_t* __restrict__ row_cost, int N, int BH, XcdWeights w,
-                                                       int32_t* __restrict__ head_xcd, int32_t* __restrict__ slot_head,
-                                                       int32_t* __restrict__ nh, int64_t* __restrict__ load) {
+// Heads to XCDs, longest first (one workgroup of 1024), each to the XCD where
+// it would finish first (ties: lower XCD).  Writes head_xcd, the heads of
+// each XCD in assignment order (slot_head[x * BH + k]), their number (nh[x])
+// and the XCD loads (load[x]).  The head costs are summed one wavefront per
+// head; the assignment is uniform code on wavefront 0.
+__global__ __launch_bounds__(1024) void sasa_lpt_kernel(const int64_t* __restrict__ row_cost, int N, int BH, XcdWeights w,
+                                                        int32_t* __restrict__ head_xcd, int32_t* __restrict__ slot_head,
+                                                        int32_t* __restrict__ nh, int64_t* __restrict__ load) {
   extern __shared__ int64_t hs[];  // [BH] head costs, then [BH] int32 order
   int64_t* hcost = hs;
   int32_t* horder = (int32_t*)(hs + BH);
@@ -140,21 +141,42 @@ __global__ __launch_bounds__(256) void sasa_lpt_kernel(const int64_t* __restrict
     horder[r] = x;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int64_t ld[SASA_NXCD];
-    int cnt[SASA_NXCD];
-    for (int x = 0; x < SASA_NXCD; ++x) ld[x] = 0, cnt[x] = 0;
-    for (int r = 0; r < BH; ++r) {
-      const int hd = horder[r];
-      const int64_t c = hcost[hd];
-      int best = 0;
-      for (int x = 1; x < SASA_NXCD; ++x)  // (ld[x] + c) / w[x] < (ld[best] + c) / w[best]
-        if ((ld[x] + c) * w.w[best] < (ld[best] + c) * w.w[x]) best = x;
-      ld[best] += c;
-      head_xcd[hd] = best;
-      slot_head[best * BH + cnt[best]] = hd;
-      ++cnt[best];
+  if (wave != 0) return;
+  // the assignment as uniform (scalar) code on wavefront 0
+  int64_t ld[SASA_NXCD];
+  int cnt[SASA_NXCD];
+#pragma unroll
+  for (int x = 0; x < SASA_NXCD; ++x) {
+    ld[x] = 0;
+    cnt[x] = 0;
+  }
+  for (int r = 0; r < BH; ++r) {
+    const int hd = __builtin_amdgcn_readfirstlane(horder[r]);
+    const int64_t hc = hcost[hd];
+    const int64_t c = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(hc >> 32)) << 32) |
+                                (uint32_t)__builtin_amdgcn_readfirstlane((int)hc));
+    int best = 0;
+    int64_t bnum = ld[0] + c, bw = w.w[0];
+#pragma unroll
+    for (int x = 1; x < SASA_NXCD; ++x) {  // (ld[x] + c) / w[x] < (ld[best] + c) / w[best]
+      const int64_t num = ld[x] + c;
+      if (num * bw < bnum * w.w[x]) {
+        best = x;
+        bnum = num;
+        bw = w.w[x];
+      }
     }
+#pragma unroll
+    for (int x = 0; x < SASA_NXCD; ++x)
+      if (x == best) {
+        if (lane == 0) slot_head[x * BH + cnt[x]] = hd;
+        ld[x] += c;
+        ++cnt[x];
+      }
+    if (lane == 0) head_xcd[hd] = best;
+  }
+  if (lane == 0) {
+#pragma unroll
     for (int x = 0; x < SASA_NXCD; ++x) {
       nh[x] = cnt[x];
       load[x] = ld[x];
@@ -248,7 +270,7 @@ hipError_t launch_sasa(const double* qbar, const double* kbar, int D, const uint
     hipLaunchKernelGGL(sasa_cand_kernel, dim3((unsigned)nt * 64), dim3(64), 0, st, S, (int)t0, nIT, mask_in, g, words,
                        R, cand, row_cost, kv_cnt);
   }
-  hipLaunchKernelGGL(sasa_lpt_kernel, dim3(1), dim3(256), (size_t)BH * 12, st, row_cost, g.N, BH, w, head_xcd, slot_head,
+  hipLaunchKernelGGL(sasa_lpt_kernel, dim3(1), dim3(1024), (size_t)BH * 12, st, row_cost, g.N, BH, w, head_xcd, slot_head,
                      nh, xcd_load);
   hipLaunchKernelGGL(sasa_take_kernel, dim3(SASA_NXCD), dim3(1024), 0, st, g, words, R, BH, w, cand, slot_head, nh,
                      xcd_load, mask_out, kv_cnt, xcd_load + SASA_NXCD);
