@@ -44,6 +44,9 @@ def main():
     ap.add_argument("--sasa", type=int, default=0, metavar="R",
                     help="also measure slack-aware augmentation with R rounds on the per-XCD schedule, with its "
                          "error against the dense oracle on sampled items")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the layer captured once in a HIP graph and replayed (outputs checked bitwise "
+                         "against the eager loop)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only copy 2 GiB device-to-device three times (reference for rocprofv3 FETCH/WRITE_SIZE)")
     args = ap.parse_args()
@@ -186,6 +189,10 @@ def main():
     if args.overlap > 0 and not wl.static:
         overlap = _overlap_leg(fva, wl, q, k, v, o, mask, args)
 
+    graph = None
+    if args.graph:
+        graph = _graph_leg(fva, wl, q, k, v, shape, ws_r, ws_a, o, mask, args)
+
     sasa = None
     if args.sasa > 0 and not wl.static:
         sasa = _sasa_leg(fva, wl, q, k, v, host, shape, ws_r, ws_a, stream, args)
@@ -243,6 +250,7 @@ def main():
         "cpu_baseline": cpu,
         "sasa": sasa,
         "overlap": overlap,
+        "graph": graph,
     }
     print(json.dumps(res), flush=True)
 
@@ -275,6 +283,57 @@ def _block_counts(wl):
     eh = [min(bh, H - i * bh) for i in range(-(-H // bh))]
     ew = [min(bw, W - i * bw) for i in range(-(-W // bw))]
     return np.array([a * b * c for a in et for b in eh for c in ew], dtype=np.int64)
+
+
+def _graph_leg(fva, wl, q, k, v, shape, ws_r, ws_a, o_ref, mask_ref, args):
+    """The same layer (mask, plan, attention kernel) captured once into a HIP
+    graph on a side stream and replayed: no host work between the kernels.
+    Same timing protocol as the main loop; each timed run's output checked
+    bitwise against the main loop's, with eager work between replays."""
+    import torch
+    B, L, heads, D = shape
+    N = fva.num_blocks(wl.grid, wl.block)
+    o = torch.empty_like(q)
+    mask = torch.empty((B, heads, N, (N + 31) // 32), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((B, heads, N), dtype=torch.int32, device="cuda")
+    status = torch.empty((1,), dtype=torch.int32, device="cuda")
+    side = torch.cuda.Stream()
+
+    def layer(s):
+        if wl.static:
+            fva.static_mask(shape, wl.grid, wl.block, local=wl.static[0], anchor_t=wl.static[1], out=(mask, cnt),
+                            stream=s)
+        else:
+            fva.route(q, k, wl.grid, wl.block, wl.top_p, wl.k_floor, ws=ws_r, out=(mask, cnt, status), stream=s)
+        fva.attn_plan(k, v, wl.grid, wl.block, mask, sched=args.sched, ws=ws_a, stream=s)
+        fva.attn_exec(q, wl.grid, wl.block, mask, ws_a, sched=args.sched, out=o, stream=s)
+
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer(side)            # warm the side stream before capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        layer(side)
+    torch.cuda.synchronize()
+    equal = True
+    main = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        o.zero_()
+        mask.zero_()
+        g.replay()
+    torch.cuda.synchronize()
+    equal &= bool(torch.equal(o.view(torch.int16), o_ref.view(torch.int16)) and torch.equal(mask, mask_ref))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(main)
+    for _ in range(args.steps):
+        g.replay()
+    e1.record(main)
+    torch.cuda.synchronize()
+    equal &= bool(torch.equal(o.view(torch.int16), o_ref.view(torch.int16)) and torch.equal(mask, mask_ref))
+    res = {"ms_per_layer_graph": round(e0.elapsed_time(e1) / args.steps, 4), "bitwise_equal": equal}
+    del g
+    return res
 
 
 def _overlap_leg(fva, wl, q, k, v, o_ref, mask_ref, args):

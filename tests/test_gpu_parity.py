@@ -530,6 +530,41 @@ def test_route_ties_lower_index_first(wl, period):
     assert kept.sum(-1).min() >= wl.k_floor
 
 
+@pytest.mark.parametrize("top_p,k_floor", [(0.7, 3), (0.93, 5), (0.0, 300)])
+def test_select_exact_scores_far_below_the_range(top_p, k_floor):
+    """Scores both sides compute exactly (Q = 1, K constant per block at
+    values with 8 significant bits: the block means, the 64-term sums and the
+    division by sqrt(64) = 8 are exact), 574 of them within 2^-56 of zero and
+    two at +-1.  Then exp(s - max) is exp(-1) for all 574, the Top-p cut falls
+    among them, and telling the cut from its neighbour takes about 65 halvings
+    of the score range: the selection kernel runs past its value-midpoint
+    passes into key-midpoint ones.  With exact scores the kept set is fully
+    determined, so every row is compared, flagged by the 1e-5 rules or not;
+    the Top-p cuts sit 5e-5 or more from a mass step, far outside the
+    last-bit differences two exp(-1) may have."""
+    wl = _custom("select_exact_tiny", 1, 64, (12, 16, 24), (2, 2, 2), top_p, k_floor)
+    N = oracle.num_blocks(wl.grid, wl.block)
+    assert N == 576
+    c = np.empty(N)
+    c[0], c[1] = 0.125, -0.125
+    for j in range(2, N):  # (37 j mod 128, j mod 5, j mod 3) differ for j < 1920: distinct values
+        c[j] = (1 if j % 3 else -1) * (1 + ((37 * j) % 128) / 128) * 2.0 ** (-60 - j % 5)
+    assert len(set(c.tolist())) == N
+    tb = oracle.token_block(wl.grid, wl.block)
+    L = int(np.prod(wl.grid))
+    q = fvgen.f64_to_bf16(np.ones((1, L, 1, 64)))
+    k = fvgen.f64_to_bf16(np.ascontiguousarray(np.broadcast_to(c[tb][None, :, None, None], (1, L, 1, 64))))
+    assert np.array_equal(fvgen.bf16_to_f64(k)[0, :, 0, 0], c[tb])
+    (mg, cg, sg), (mo, co, flags, so) = _route_both(wl, q, k, _dev(q), _dev(k))
+    S = oracle.scores(oracle.pool(q, wl.grid, wl.block), oracle.pool(k, wl.grid, wl.block))
+    assert np.array_equal(S[0, 0, 0], 8 * c)  # exact
+    print("\n[select_exact_tiny p=%g floor=%d] kept %d of %d; rows flagged by the 1e-5 rules %d of %d"
+          % (top_p, k_floor, int(co[0, 0, 0]), N, int((flags != 0).sum()), flags.size), flush=True)
+    assert sg == so == 0
+    assert np.array_equal(cg, co)
+    assert np.array_equal(mg, mo)
+
+
 @pytest.mark.parametrize("name", ["tiny", "wan14b", "long"])
 def test_plan_exec_equals_sparse_attn(name):
     """fva_attn_plan + fva_attn_exec is fva_sparse_attn split in two: bitwise equal O."""
