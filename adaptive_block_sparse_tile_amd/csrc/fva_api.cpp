@@ -388,7 +388,10 @@ fva_status fva_sasa(const fva_desc* desc, const fva_grid* grid, const uint32_t* 
   char* base = (char*)ws;
   const double* qbar = (const double*)((const char*)route_ws + rl.qbar);
   const double* kbar = (const double*)((const char*)route_ws + rl.kbar);
-  hipError_t e = fva::launch_sasa(qbar, kbar, desc->D, mask_in, g, desc->B * desc->heads, rounds, w,
+  // the router's scores, when its one slab held every tile
+  const int64_t tiles = (int64_t)desc->B * desc->heads * ((g.N + 63) / 64);
+  const double* s_ready = rl.slab_tiles >= tiles ? (const double*)((const char*)route_ws + rl.s) : nullptr;
+  hipError_t e = fva::launch_sasa(qbar, kbar, desc->D, mask_in, g, desc->B * desc->heads, rounds, w, s_ready,
                                   (double*)(base + lay.s), lay.slab_tiles, mask_out, kv_cnt, head_xcd, xcd_load,
                                   (int32_t*)(base + lay.cand), (int64_t*)(base + lay.cost),
                                   (int32_t*)(base + lay.slot), (int32_t*)(base + lay.nh), (hipStream_t)stream);

@@ -36,9 +36,9 @@ struct XcdWeights {
   int64_t w[8];
 };
 hipError_t launch_sasa(const double* qbar, const double* kbar, int D, const uint32_t* mask_in, const Geo& g, int BH,
-                       int R, const XcdWeights& w, double* S, int64_t slab_tiles, uint32_t* mask_out,
-                       int32_t* kv_cnt, int32_t* head_xcd, int64_t* xcd_load, int32_t* cand, int64_t* row_cost,
-                       int32_t* slot_head, int32_t* nh, hipStream_t st);
+                       int R, const XcdWeights& w, const double* S_ready, double* S, int64_t slab_tiles,
+                       uint32_t* mask_out, int32_t* kv_cnt, int32_t* head_xcd, int64_t* xcd_load, int32_t* cand,
+                       int64_t* row_cost, int32_t* slot_head, int32_t* nh, hipStream_t st);
 
 // Static block mask of every (b, h): rows = B*heads*N.
 hipError_t launch_static_mask(const Geo& g, int64_t rows, int lt, int lh, int lw, int anchor_t, uint32_t* mask,

@@ -49,12 +49,13 @@ __device__ inline int key_chunks(const Geo& g, int j) { return (block_count(g, j
 // of 64 query blocks of one head, scored by the router's own scores kernel,
 // so the scores are bit-equal to what the router ranked): the row cost, the
 // kept count, and the first R dropped blocks in the router's order (-1 past
-// the last one).  Workgroup r of the launch is slab row r (rows past N in a
-// head's last tile do nothing).
+// the last one), and a copy of the row's mask words into mask_out (null:
+// augmented in place).  Workgroup r of the launch is slab row r (rows past N
+// in a head's last tile do nothing).
 __global__ __launch_bounds__(64) void sasa_cand_kernel(const double* __restrict__ S, int t0, int nIT,
                                                        const uint32_t* __restrict__ mask, Geo g, int words, int R,
                                                        int32_t* __restrict__ cand, int64_t* __restrict__ row_cost,
-                                                       int32_t* __restrict__ kv_cnt) {
+                                                       int32_t* __restrict__ kv_cnt, uint32_t* __restrict__ mask_out) {
   const int N = g.N;
   const int64_t tile = t0 + blockIdx.x / 64;
   const int i = (int)((tile % nIT) * 64 + blockIdx.x % 64);
@@ -62,6 +63,8 @@ __global__ __launch_bounds__(64) void sasa_cand_kernel(const double* __restrict_
   const int64_t row = (tile / nIT) * N + i;
   const int lane = threadIdx.x;
   const uint32_t* m = mask + row * words;
+  if (mask_out)
+    for (int w = lane; w < words; w += 64) mask_out[row * words + w] = m[w];
   const double* s = S + (int64_t)blockIdx.x * N;
   int64_t kept_chunks = 0;
   int kept = 0;
@@ -117,32 +120,39 @@ __global__ __launch_bounds__(64) void sasa_cand_kernel(const double* __restrict_
 // Heads to XCDs, longest first (one workgroup of 1024), each to the XCD where
 // it would finish first (ties: lower XCD).  Writes head_xcd, the heads of
 // each XCD in assignment order (slot_head[x * BH + k]), their number (nh[x])
-// and the XCD loads (load[x]).  The head costs are summed one wavefront per
-// head; the assignment is uniform code on wavefront 0.
+// and the XCD loads (load[x]).  Head costs: each head's rows are summed by a
+// group of lanes (in a fixed order), the heads are ranked, and the costs are
+// stored in rank order; the assignment is uniform code on wavefront 0.
 __global__ __launch_bounds__(1024) void sasa_lpt_kernel(const int64_t* __restrict__ row_cost, int N, int BH, XcdWeights w,
                                                         int32_t* __restrict__ head_xcd, int32_t* __restrict__ slot_head,
                                                         int32_t* __restrict__ nh, int64_t* __restrict__ load) {
-  extern __shared__ int64_t hs[];  // [BH] head costs, then [BH] int32 order
+  extern __shared__ int64_t hs[];  // [BH] head costs, [BH] costs in rank order, then [BH] int32 heads in rank order
   int64_t* hcost = hs;
-  int32_t* horder = (int32_t*)(hs + BH);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
-  for (int x = wave; x < BH; x += nwaves) {
+  int64_t* rcost = hs + BH;
+  int32_t* horder = (int32_t*)(hs + 2 * BH);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // lanes per head: a power of two up to 64, so that every head's group fits in one wavefront
+  int per = 64;
+  while (per > 1 && per * BH > (int)blockDim.x) per >>= 1;
+  const int heads_per_pass = (int)blockDim.x / per;
+  for (int x0 = 0; x0 < BH; x0 += heads_per_pass) {
+    const int x = x0 + tid / per, sub = tid % per;
     int64_t c = 0;
-    for (int i = lane; i < N; i += 64) c += row_cost[(int64_t)x * N + i];
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
-    if (lane == 0) hcost[x] = c;
+    if (x < BH)
+      for (int i = sub; i < N; i += per) c += row_cost[(int64_t)x * N + i];
+    for (int off = per / 2; off > 0; off >>= 1) c += __shfl_xor(c, off);
+    if (x < BH && sub == 0) hcost[x] = c;
   }
   __syncthreads();
-  for (int x = threadIdx.x; x < BH; x += blockDim.x) {
+  for (int x = tid; x < BH; x += blockDim.x) {
     int r = 0;
     for (int y = 0; y < BH; ++y)
       if (hcost[y] > hcost[x] || (hcost[y] == hcost[x] && y < x)) ++r;
     horder[r] = x;
+    rcost[r] = hcost[x];
   }
   __syncthreads();
   if (wave != 0) return;
-  // the assignment as uniform (scalar) code on wavefront 0
   int64_t ld[SASA_NXCD];
   int cnt[SASA_NXCD];
 #pragma unroll
@@ -152,9 +162,9 @@ __global__ __launch_bounds__(1024) void sasa_lpt_kernel(const int64_t* __restric
   }
   for (int r = 0; r < BH; ++r) {
     const int hd = __builtin_amdgcn_readfirstlane(horder[r]);
-    const int64_t hc = hcost[hd];
-    const int64_t c = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(hc >> 32)) << 32) |
-                                (uint32_t)__builtin_amdgcn_readfirstlane((int)hc));
+    const int64_t rc = rcost[r];
+    const int64_t c = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(rc >> 32)) << 32) |
+                                (uint32_t)__builtin_amdgcn_readfirstlane((int)rc));
     int best = 0;
     int64_t bnum = ld[0] + c, bw = w.w[0];
 #pragma unroll
@@ -251,27 +261,27 @@ __global__ __launch_bounds__(1024) void sasa_take_kernel(Geo g, int words, int R
 }
 
 hipError_t launch_sasa(const double* qbar, const double* kbar, int D, const uint32_t* mask_in, const Geo& g, int BH,
-                       int R, const XcdWeights& w, double* S, int64_t slab_tiles, uint32_t* mask_out, int32_t* kv_cnt, int32_t* head_xcd,
-                       int64_t* xcd_load, int32_t* cand, int64_t* row_cost, int32_t* slot_head, int32_t* nh,
-                       hipStream_t st) {
+                       int R, const XcdWeights& w, const double* S_ready, double* S, int64_t slab_tiles,
+                       uint32_t* mask_out, int32_t* kv_cnt, int32_t* head_xcd, int64_t* xcd_load, int32_t* cand,
+                       int64_t* row_cost, int32_t* slot_head, int32_t* nh, hipStream_t st) {
   const int words = (g.N + 31) / 32;
-  const int64_t rows = (int64_t)BH * g.N;
-  if (mask_out != mask_in) {
-    hipError_t e = hipMemcpyAsync(mask_out, mask_in, (size_t)rows * words * sizeof(uint32_t),
-                                  hipMemcpyDeviceToDevice, st);
-    if (e != hipSuccess) return e;
-  }
+  uint32_t* copy_to = mask_out != mask_in ? mask_out : nullptr;
   const int nIT = (g.N + 63) / 64;
   const int64_t tiles = (int64_t)BH * nIT;
+  if (S_ready) slab_tiles = tiles;  // the router's one slab holds every tile
   for (int64_t t0 = 0; t0 < tiles; t0 += slab_tiles) {
     const int nt = (int)std::min<int64_t>(slab_tiles, tiles - t0);
-    hipError_t e = launch_scores_slab(qbar, kbar, g.N, D, (int)t0, nt, S, st);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(sasa_cand_kernel, dim3((unsigned)nt * 64), dim3(64), 0, st, S, (int)t0, nIT, mask_in, g, words,
-                       R, cand, row_cost, kv_cnt);
+    const double* slab = S_ready;
+    if (!slab) {
+      hipError_t e = launch_scores_slab(qbar, kbar, g.N, D, (int)t0, nt, S, st);
+      if (e != hipSuccess) return e;
+      slab = S;
+    }
+    hipLaunchKernelGGL(sasa_cand_kernel, dim3((unsigned)nt * 64), dim3(64), 0, st, slab, (int)t0, nIT, mask_in, g,
+                       words, R, cand, row_cost, kv_cnt, copy_to);
   }
-  hipLaunchKernelGGL(sasa_lpt_kernel, dim3(1), dim3(1024), (size_t)BH * 12, st, row_cost, g.N, BH, w, head_xcd, slot_head,
-                     nh, xcd_load);
+  hipLaunchKernelGGL(sasa_lpt_kernel, dim3(1), dim3(1024), (size_t)BH * 20, st, row_cost, g.N, BH, w, head_xcd,
+                     slot_head, nh, xcd_load);
   hipLaunchKernelGGL(sasa_take_kernel, dim3(SASA_NXCD), dim3(1024), 0, st, g, words, R, BH, w, cand, slot_head, nh,
                      xcd_load, mask_out, kv_cnt, xcd_load + SASA_NXCD);
   return hipGetLastError();

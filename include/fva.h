@@ -303,10 +303,11 @@ fva_status fva_attn_schedule(const fva_desc* desc, const fva_grid* grid, const v
  * whose summed cost r_i * ceil(c_j/64) fits M - load_x is added.  Run the attention
  * with FVA_SCHED_XCD and this head_xcd so that each XCD serves its own heads.
  *   mask_in    uint32 [B, heads, N, ceil(N/32)] from fva_route
- *   route_ws   the workspace of that fva_route call, untouched since (its
- *              pooled Q and K; the scores are recomputed from them slab by
- *              slab with the router's own scores kernel, bit-equal to what it
- *              routed on)
+ *   route_ws   the workspace of that fva_route call, untouched since: its
+ *              pooled Q and K, and its score slab when that held every tile
+ *              (the scores are then read from it; otherwise they are
+ *              recomputed slab by slab with the router's own scores kernel,
+ *              bit-equal to what it routed on)
  *   rounds     0..8 (0 copies the mask)
  *   xcd_weight nullable host int32 [8]: relative speed of each XCD (per
  *              mille; 1..1000000), e.g. from fva_trace_xcd_speed.  A head

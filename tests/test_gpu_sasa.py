@@ -61,6 +61,37 @@ def test_sasa_matches_oracle(wl):
 W8 = [1000, 1040, 960, 1000, 1090, 920, 1010, 980]
 
 
+def test_sasa_long_video_scores_recomputed_per_slab():
+    """The long video's router holds its scores in 3 slabs, so the
+    augmentation recomputes them slab by slab from the pooled means (the
+    other cases read the router's single slab); in place (mask_out =
+    mask_in), on measured-looking XCD weights."""
+    wl = fvgen.WORKLOADS["long"]
+    q, k, v = fvgen.generate_qkv(wl)
+    qd, kd = _dev(q), _dev(k)
+    shape = tuple(qd.shape)
+    W8 = [1000, 1040, 960, 1000, 1090, 920, 1010, 980]
+    ws_r = fva.workspace(fva.route_workspace_bytes(shape, wl.grid, wl.block), qd.device)
+    mask, _, _ = fva.route(qd, kd, wl.grid, wl.block, wl.top_p, wl.k_floor, ws=ws_r)
+    cnt = torch.empty(mask.shape[:-1], dtype=torch.int32, device=qd.device)
+    mo_g, cnt_g, hx_g, load_g = fva.sasa(shape, wl.grid, wl.block, mask, ws_r, rounds=2, xcd_weight=W8,
+                                         out=(mask, cnt))
+    torch.cuda.synchronize()
+    S = oracle.scores(oracle.pool(q, wl.grid, wl.block), oracle.pool(k, wl.grid, wl.block))
+    mask_o, _, rflags, _ = oracle.route(q, k, wl.grid, wl.block, wl.top_p, wl.k_floor, margin=1e-10)
+    mo, co, hx, load, added, sflags = oracle.sasa(S, mask_o, wl.grid, wl.block, 2, margin=1e-10, xcd_weight=W8)
+    print("\n[long] loads %s added %s, rows flagged (route, sasa) %d %d" % (
+        load.tolist(), added.tolist(), int((rflags != 0).sum()), int(sflags.sum())), flush=True)
+    assert not (rflags != 0).any() and not sflags.any()
+    assert mo_g.data_ptr() == mask.data_ptr()
+    assert np.array_equal(mo_g.cpu().numpy().view(np.uint32), mo)
+    assert np.array_equal(cnt_g.cpu().numpy(), co)
+    assert np.array_equal(hx_g.cpu().numpy(), hx)
+    lg = load_g.cpu().numpy()
+    assert np.array_equal(lg[:8], load) and np.array_equal(lg[8:], added)
+    assert added.sum() > 0
+
+
 @pytest.mark.parametrize("wl", [CASES[0], CASES[2], CASES[3]], ids=lambda w: w.name)
 def test_sasa_weighted_matches_oracle(wl):
     """XCDs of unequal speed (xcd_weight): mask, counts, placement and loads
