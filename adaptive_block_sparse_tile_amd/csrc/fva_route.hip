@@ -395,7 +395,7 @@ __device__ inline double key_value(uint64_t k) {
   return __longlong_as_double((long long)b);
 }
 // candidates per lane kept after a select bracket is compacted
-constexpr int kCand = 4;
+constexpr int kCand = 2;
 // passes of a select search that split the scores' values
 constexpr int kValueSteps = 40;
 
