@@ -1056,9 +1056,16 @@ __global__ __launch_bounds__(COST_WAVES * 64) void cost_kernel(AttnParams p, con
   if (blockIdx.x == 0 && threadIdx.x < NXCD) qctr[threadIdx.x] = 0u;
   if (blockIdx.x == 0 && threadIdx.x == 0) *tag = p.want_tag;
   __syncthreads();
-  const int lane = threadIdx.x & 63;
-  const int item = blockIdx.x * COST_WAVES + (threadIdx.x >> 6);
-  if (item >= p.n_items) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int item = blockIdx.x * COST_WAVES + wave;
+  // each wavefront's cost and head, summed per head by wavefront 0 below
+  __shared__ uint64_t wave_cost[COST_WAVES];
+  __shared__ int wave_bh[COST_WAVES];
+  if (item >= p.n_items) {
+    if (lane == 0) wave_bh[wave] = -1;
+    __syncthreads();
+    return;
+  }
   const int gid = item % p.n_groups, bh = item / p.n_groups;
   const uint32_t* rows[4];
   int nrows = 0;
@@ -1086,7 +1093,25 @@ __global__ __launch_bounds__(COST_WAVES * 64) void cost_kernel(AttnParams p, con
     const uint32_t cost = qrows * kv;
     keys[item] = ((uint64_t)cost << 32) | (uint64_t)(~(uint32_t)item);
     rank[item] = 0u;
-    atomicAdd((unsigned long long*)&head_cost[bh], (unsigned long long)cost);
+    wave_cost[wave] = cost;
+    wave_bh[wave] = bh;
+  }
+  __syncthreads();
+  // one atomic per run of wavefronts on the same head (a head's items are
+  // consecutive): many wavefronts adding to one address serialise in L2
+  if (threadIdx.x == 0) {
+    uint64_t run = 0;
+    int run_bh = -1;
+    for (int w = 0; w < COST_WAVES; ++w) {
+      const int b = wave_bh[w];
+      if (b != run_bh) {
+        if (run_bh >= 0) atomicAdd((unsigned long long*)&head_cost[run_bh], (unsigned long long)run);
+        run = 0;
+        run_bh = b;
+      }
+      if (b >= 0) run += wave_cost[w];
+    }
+    if (run_bh >= 0) atomicAdd((unsigned long long*)&head_cost[run_bh], (unsigned long long)run);
   }
 }
 
