@@ -11,10 +11,10 @@
 // reference would):
 //   pool_kernel        HBM stream of Q and K -> fp64 block means [B,h,N,D]
 //   scores_kernel      per (b,h): S = Qbar Kbar^T / sqrt(D), 64x64 tiles
-//   route_rows_kernel  N <= 512: one wavefront per row: softmax, bitonic
+//   route_rows_kernel  N <= 256: one wavefront per row: softmax, bitonic
 //                      sort on (score desc, index asc), scan, Top-p count,
 //                      floor, mask words and kept count
-//   route_select_kernel N > 512: the same decisions by bisection on
+//   route_select_kernel N > 256: the same decisions by a search over
 //                      order-preserving keys (no full sort)
 #include <algorithm>
 #include <mutex>
@@ -372,9 +372,11 @@ __global__ __launch_bounds__(THREADS) void route_rows_kernel(const double* __res
 }
 
 // ---------------------------------------------------------------------------
-// Row routing for large N (N > 512): selection instead of a full sort.
-// One workgroup of ceil(N/32) lanes (rounded up to whole wavefronts) per row;
-// lane t owns blocks 32t .. 32t+31 and writes mask word t.  Blocks are ranked
+// Row routing for 256 < N <= 8192: selection instead of a full sort.  One
+// workgroup per row; lane t owns blocks E t .. E t + E - 1: for N <= 512 one
+// wavefront with E = 8 (four lanes form a mask word), above that
+// ceil(N/32) lanes (rounded up to whole wavefronts) with E = 32 (lane t
+// writes mask word t).  Blocks are ranked
 // by a 64-bit key that orders fp64 scores exactly (ties by lower index), and
 //   n* = the smallest prefix whose probability mass reaches p is found by
 //        bisecting the key for the largest K with mass(key >= K) >= p,
@@ -528,6 +530,7 @@ struct GroupRed {
 // probabilities per lane take 128, and the passes are bound by latency
 // (reductions and a barrier each), so the extra occupancy is worth the few
 // registers the compiler moves to scratch (long video 640 -> 525 us per slab).
+template <int E>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void route_select_kernel(const double* __restrict__ S, int N, int words, int t0,
                                                            int nIT, Heads hd, float top_p, int k_floor,
                                                            uint32_t* __restrict__ mask,
@@ -541,14 +544,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
   if (sr.i >= N) return;  // padding row of a head's last tile (uniform over the workgroup)
   const int64_t row = sr.out;
   const double* s = S + (int64_t)blockIdx.x * N;
-  const int j0 = tid * 32;
+  const int j0 = tid * E;
 
-  double pr[32];
-  uint64_t key[32];
+  double pr[E];
+  uint64_t key[E];
   bool bad = false;
   double lmax = -INFINITY;
 #pragma unroll
-  for (int e = 0; e < 32; ++e) {
+  for (int e = 0; e < E; ++e) {
     // blocks past N read block N - 1 and hold -inf (their exp below is 0)
     const int j = j0 + e;
     const double x = s[min(j, N - 1)];
@@ -559,7 +562,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
   }
   if (__syncthreads_or(bad)) {
     if (tid < words) {
-      const int nb = min(32, N - j0);
+      const int nb = min(32, N - 32 * tid);
       mask[row * words + tid] = nb == 32 ? 0xffffffffu : ((1u << nb) - 1u);
     }
     if (tid == 0) {
@@ -571,7 +574,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
   const double M = gr.reduce(lmax, MaxOp());
   double lz = 0.0;
 #pragma unroll
-  for (int e = 0; e < 32; ++e) {
+  for (int e = 0; e < E; ++e) {
     const bool in = j0 + e < N;
     key[e] = in ? order_key(pr[e]) : 0ull;  // below every finite score
     pr[e] = exp(pr[e] - M);                 // -inf - M: exactly 0
@@ -579,10 +582,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
   }
   const double Z = gr.reduce(lz, AddOp());
 #pragma unroll
-  for (int e = 0; e < 32; ++e) pr[e] = pr[e] / Z;
+  for (int e = 0; e < E; ++e) pr[e] = pr[e] / Z;
   uint64_t kmin = ~0ull, kmax = 0ull;
 #pragma unroll
-  for (int e = 0; e < 32; ++e)
+  for (int e = 0; e < E; ++e)
     if (j0 + e < N) {
       kmin = key[e] < kmin ? key[e] : kmin;
       kmax = key[e] > kmax ? key[e] : kmax;
@@ -621,14 +624,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
     // offset comes from its count, a position from the lanes below it
     uint32_t mine = 0;  // uniform in the wavefront
 #pragma unroll
-    for (int e = 0; e < 32; ++e) mine += (uint32_t)__popcll(__ballot(key[e] >= lo && key[e] < hi));
+    for (int e = 0; e < E; ++e) mine += (uint32_t)__popcll(__ballot(key[e] >= lo && key[e] < hi));
     __syncthreads();
     if (lane == 0) wt[wave] = mine;
     __syncthreads();
     uint32_t base = 0;
     for (int w = 0; w < wave; ++w) base += wt[w];
 #pragma unroll
-    for (int e = 0; e < 32; ++e) {
+    for (int e = 0; e < E; ++e) {
       const bool in = key[e] >= lo && key[e] < hi;
       const uint64_t bal = __ballot(in);
       if (in) {
@@ -661,7 +664,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
     uint32_t c = 0;
     if (!compacted) {
 #pragma unroll
-      for (int e = 0; e < 32; ++e) {
+      for (int e = 0; e < E; ++e) {
         const bool ge = key[e] >= K;
         if (with_mass) m4[e & 3] = fma(ge ? 1.0 : 0.0, pr[e], m4[e & 3]);
         c += ge ? 1u : 0u;
@@ -684,7 +687,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
     uint64_t k = 0;
     if (!compacted) {
 #pragma unroll
-      for (int e = 0; e < 32; ++e)
+      for (int e = 0; e < E; ++e)
         if (key[e] >= lo && key[e] < hi) k = key[e];
     } else {
 #pragma unroll
@@ -789,7 +792,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
     // blocks above the crossing key, then as many tied blocks as needed
     double ptie = 0.0;
 #pragma unroll
-    for (int e = 0; e < 32; ++e)
+    for (int e = 0; e < E; ++e)
       if (key[e] == lo) ptie = pr[e];
     // every tied block has the same probability; any holder reports it
     ptie = gr.reduce(ptie, MaxOp());
@@ -808,9 +811,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
   }
   const int keep = min(N, max(k_floor, nstar));
 
-  uint32_t word = 0u;
+  uint32_t word = 0u;  // bit e: block j0 + e is kept
   if (keep >= N) {
-    const int nb = min(32, N - j0);
+    const int nb = min(E, N - j0);
     word = nb >= 32 ? 0xffffffffu : (nb > 0 ? ((1u << nb) - 1u) : 0u);
   } else {
     // largest K with count(key >= K) >= keep: the Top-p crossing key itself
@@ -845,10 +848,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
     // ties at the cut key, in index order: exclusive prefix over lanes
     uint32_t my_ties = 0;
 #pragma unroll
-    for (int e = 0; e < 32; ++e) my_ties += (j0 + e < N && key[e] == lo) ? 1u : 0u;
+    for (int e = 0; e < E; ++e) my_ties += (j0 + e < N && key[e] == lo) ? 1u : 0u;
     uint32_t rank = exclusive_prefix(my_ties);
 #pragma unroll
-    for (int e = 0; e < 32; ++e) {
+    for (int e = 0; e < E; ++e) {
       const int j = j0 + e;
       if (j >= N) continue;
       bool kept = key[e] > lo;
@@ -859,7 +862,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
       if (kept) word |= 1u << e;
     }
   }
-  if (tid < words) mask[row * words + tid] = word;
+  if constexpr (E == 32) {
+    if (tid < words) mask[row * words + tid] = word;
+  } else {
+    // E = 8: lanes 4w .. 4w + 3 hold the four bytes of mask word w
+    static_assert(E == 8, "8 or 32 blocks per lane");
+    uint32_t part = word << (8 * (tid & 3));
+    part |= dpp_move<DPP_XOR1>(part);
+    part |= dpp_move<DPP_XOR2>(part);
+    if ((tid & 3) == 0 && (tid >> 2) < words) mask[row * words + (tid >> 2)] = part;
+  }
   if (tid == 0 && kv_cnt) kv_cnt[row] = keep;
 }
 
@@ -932,11 +944,15 @@ hipError_t launch_route_slabs(const double* qbar, const double* kbar, int B, con
     FVA_ROUTE_CASE(64, 64)
     FVA_ROUTE_CASE(128, 64)
     FVA_ROUTE_CASE(256, 64)
-    FVA_ROUTE_CASE(512, 64)
 #undef FVA_ROUTE_CASE
+    if (N <= 512) {  // one wavefront, 8 blocks per lane
+      hipLaunchKernelGGL(route_select_kernel<8>, grid, dim3(64), 0, st, S, N, words, (int)t0, nIT, hd, top_p, k_floor,
+                         mask, kv_cnt, status);
+      continue;
+    }
     if (N > 8192) return hipErrorInvalidValue;
     const int threads = 64 * ((words + 63) / 64);
-    hipLaunchKernelGGL(route_select_kernel, grid, dim3(threads), 0, st, S, N, words, (int)t0, nIT, hd, top_p,
+    hipLaunchKernelGGL(route_select_kernel<32>, grid, dim3(threads), 0, st, S, N, words, (int)t0, nIT, hd, top_p,
                        k_floor, mask, kv_cnt, status);
   }
   return hipGetLastError();

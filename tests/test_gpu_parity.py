@@ -334,19 +334,21 @@ def test_nonfinite_rows_repaired_dense():
 
 
 
-def test_select_router_nonfinite_and_all_kept():
-    # N = 576 > 512: the bisection router.  A NaN in one query token of head 1
+@pytest.mark.parametrize("block,n_expect", [((2, 2, 2), 576), ((2, 2, 4), 288)])
+def test_select_router_nonfinite_and_all_kept(block, n_expect):
+    # N = 576 (32 blocks per lane) and N = 288 (one wavefront, 8 blocks per
+    # lane): the selection router.  A NaN in one query token of head 1
     # makes that query block's row non-finite; a +inf in one key token of
     # head 0 makes every row of head 0 non-finite.  Both are repaired to all
     # blocks with status bit 0 set; top_p = 1 keeps every block of every row.
-    wl = _custom("select_nonfinite", 2, 64, (12, 16, 24), (2, 2, 2), 0.7, 3)
+    wl = _custom("select_nonfinite", 2, 64, (12, 16, 24), block, 0.7, 3)
     N = oracle.num_blocks(wl.grid, wl.block)
-    assert N == 576
+    assert N == n_expect
     q0, k0, _ = fvgen.generate_qkv(wl)
     q, k = q0.copy(), k0.copy()
     tb = oracle.token_block(wl.grid, wl.block)
     q[0, int(np.nonzero(tb == 100)[0][0]), 1, 5] = 0x7FC0   # NaN (bf16 bits)
-    k[0, int(np.nonzero(tb == 300)[0][2]), 0, 9] = 0x7F80   # +inf (bf16 bits)
+    k[0, int(np.nonzero(tb == N // 2 + 12)[0][2]), 0, 9] = 0x7F80   # +inf (bf16 bits)
     qd, kd = _dev(q), _dev(k)
     (mg, cg, sg), (mo, co, flags, so) = _route_both(wl, q, k, qd, kd)
     print("\n[select_nonfinite] status gpu %d oracle %d, flagged rows %d" % (sg, so, int((flags != 0).sum())),
@@ -461,6 +463,9 @@ def test_calls_on_a_side_stream_without_workspace():
     # N = 576 > 512 key blocks: the bisection router
     _custom("select_n576", 2, 64, (12, 16, 24), (2, 2, 2), 0.7, 3),
     _custom("select_topk", 1, 128, (12, 16, 24), (2, 2, 2), 0.0, 7),
+    # 256 < N = 288 <= 512: the selection router on one wavefront, 8 blocks per lane
+    _custom("select_n288", 3, 64, (12, 16, 24), (2, 2, 4), 0.8, 4),
+    _custom("select_n288_topk", 1, 128, (12, 16, 24), (2, 2, 4), 0.0, 9),
     # grouped 64-token blocks with B = 2 (items of both batches in one queue) and D = 64
     _custom("batch2_grouped", 2, 64, (7, 10, 9), (4, 4, 4), 0.8, 2, batch=2),
     # 128-token blocks with D = 64, ragged in every dimension
@@ -509,6 +514,8 @@ def _with_tied_key_blocks(wl, k, period):
     (_custom("ties_topk_bitonic", 2, 128, (8, 16, 24), (2, 4, 4), 0.0, 9), 4),
     (_custom("ties_select", 2, 64, (12, 16, 24), (2, 2, 2), 0.5, 3), 7),
     (_custom("ties_topk_select", 2, 64, (12, 16, 24), (2, 2, 2), 0.0, 10), 6),
+    (_custom("ties_select8", 2, 64, (12, 16, 24), (2, 2, 4), 0.5, 3), 7),
+    (_custom("ties_topk_select8", 2, 64, (12, 16, 24), (2, 2, 4), 0.0, 10), 6),
 ], ids=lambda x: x.name if hasattr(x, "name") else str(x))
 def test_route_ties_lower_index_first(wl, period):
     q, k, v = fvgen.generate_qkv(wl)
@@ -530,21 +537,22 @@ def test_route_ties_lower_index_first(wl, period):
     assert kept.sum(-1).min() >= wl.k_floor
 
 
-@pytest.mark.parametrize("top_p,k_floor", [(0.7, 3), (0.93, 5), (0.0, 300)])
-def test_select_exact_scores_far_below_the_range(top_p, k_floor):
+@pytest.mark.parametrize("block", [(2, 2, 2), (2, 2, 4)], ids=["n576", "n288"])
+@pytest.mark.parametrize("top_p,k_floor", [(0.7, 3), (0.93, 5), (0.0, 150)])
+def test_select_exact_scores_far_below_the_range(top_p, k_floor, block):
     """Scores both sides compute exactly (Q = 1, K constant per block at
     values with 8 significant bits: the block means, the 64-term sums and the
-    division by sqrt(64) = 8 are exact), 574 of them within 2^-56 of zero and
-    two at +-1.  Then exp(s - max) is exp(-1) for all 574, the Top-p cut falls
+    division by sqrt(64) = 8 are exact), all but two of them within 2^-56 of zero and
+    two at +-1.  Then exp(s - max) is exp(-1) for all the others, the Top-p cut falls
     among them, and telling the cut from its neighbour takes about 65 halvings
     of the score range: the selection kernel runs past its value-midpoint
     passes into key-midpoint ones.  With exact scores the kept set is fully
     determined, so every row is compared, flagged by the 1e-5 rules or not;
     the Top-p cuts sit 5e-5 or more from a mass step, far outside the
     last-bit differences two exp(-1) may have."""
-    wl = _custom("select_exact_tiny", 1, 64, (12, 16, 24), (2, 2, 2), top_p, k_floor)
+    wl = _custom("select_exact_tiny", 1, 64, (12, 16, 24), block, top_p, k_floor)
     N = oracle.num_blocks(wl.grid, wl.block)
-    assert N == 576
+    assert N in (576, 288)
     c = np.empty(N)
     c[0], c[1] = 0.125, -0.125
     for j in range(2, N):  # (37 j mod 128, j mod 5, j mod 3) differ for j < 1920: distinct values
