@@ -537,8 +537,8 @@ def test_route_ties_lower_index_first(wl, period):
     assert kept.sum(-1).min() >= wl.k_floor
 
 
-@pytest.mark.parametrize("block", [(2, 2, 2), (2, 2, 4)], ids=["n576", "n288"])
-@pytest.mark.parametrize("top_p,k_floor", [(0.7, 3), (0.93, 5), (0.0, 150)])
+@pytest.mark.parametrize("block", [(2, 2, 2), (2, 2, 4), (2, 4, 4), (2, 4, 8)], ids=["n576", "n288", "n144", "n72"])
+@pytest.mark.parametrize("top_p,k_floor", [(0.7, 3), (0.93, 5), (0.0, None)])
 def test_select_exact_scores_far_below_the_range(top_p, k_floor, block):
     """Scores both sides compute exactly (Q = 1, K constant per block at
     values with 8 significant bits: the block means, the 64-term sums and the
@@ -549,10 +549,14 @@ def test_select_exact_scores_far_below_the_range(top_p, k_floor, block):
     passes into key-midpoint ones.  With exact scores the kept set is fully
     determined, so every row is compared, flagged by the 1e-5 rules or not;
     the Top-p cuts sit 5e-5 or more from a mass step, far outside the
-    last-bit differences two exp(-1) may have."""
+    last-bit differences two exp(-1) may have.  N = 576 runs the selection
+    with 32 blocks per lane, 288 on one wavefront with 8, and 144 and 72 the
+    row kernel's bitonic sort."""
+    N = oracle.num_blocks((12, 16, 24), block)
+    assert N in (576, 288, 144, 72)
+    if k_floor is None:
+        k_floor = N // 2 + 6  # fixed top-k: the count search alone
     wl = _custom("select_exact_tiny", 1, 64, (12, 16, 24), block, top_p, k_floor)
-    N = oracle.num_blocks(wl.grid, wl.block)
-    assert N in (576, 288)
     c = np.empty(N)
     c[0], c[1] = 0.125, -0.125
     for j in range(2, N):  # (37 j mod 128, j mod 5, j mod 3) differ for j < 1920: distinct values
