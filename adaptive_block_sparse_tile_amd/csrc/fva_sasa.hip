@@ -38,6 +38,18 @@ namespace fva {
 
 constexpr int SASA_NXCD = 8;
 
+// Register exchange between lanes (DPP; CTRL 0xB1: lane ^ 1, 0x4E: lane ^ 2,
+// 0x141: lane 7 - i within each 8 lanes), 32 or 64 bits.
+template <int CTRL>
+__device__ inline int sasa_dpp(int x) {
+  return __builtin_amdgcn_update_dpp(x, x, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ inline int64_t sasa_dpp(int64_t x) {
+  const uint32_t lo = (uint32_t)sasa_dpp<CTRL>((int)(uint32_t)x), hi = (uint32_t)sasa_dpp<CTRL>((int)(x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 __device__ inline bool mask_bit(const uint32_t* row, int j) { return (row[j >> 5] >> (j & 31)) & 1u; }
 
 __device__ inline int block_count(const Geo& g, int j) { return block_box(g, j).count; }
@@ -122,7 +134,7 @@ __global__ __launch_bounds__(64) void sasa_cand_kernel(const double* __restrict_
 // each XCD in assignment order (slot_head[x * BH + k]), their number (nh[x])
 // and the XCD loads (load[x]).  Head costs: each head's rows are summed by a
 // group of lanes (in a fixed order), the heads are ranked, and the costs are
-// stored in rank order; the assignment is uniform code on wavefront 0.
+// stored in rank order; the assignment runs on wavefront 0.
 __global__ __launch_bounds__(1024) void sasa_lpt_kernel(const int64_t* __restrict__ row_cost, int N, int BH, XcdWeights w,
                                                         int32_t* __restrict__ head_xcd, int32_t* __restrict__ slot_head,
                                                         int32_t* __restrict__ nh, int64_t* __restrict__ load) {
@@ -153,44 +165,48 @@ __global__ __launch_bounds__(1024) void sasa_lpt_kernel(const int64_t* __restric
   }
   __syncthreads();
   if (wave != 0) return;
-  int64_t ld[SASA_NXCD];
-  int cnt[SASA_NXCD];
+  // The assignment on wavefront 0: lane x (mod 8) holds XCD x's load, head
+  // count and weight; the XCD of the earliest finish comes from three
+  // register exchanges inside each group of 8 lanes (lane i with i ^ 1, then
+  // i ^ 2, then 7 - i), every group computing the same thing.
+  const int xl = lane & (SASA_NXCD - 1);
+  int64_t wx = w.w[0];
 #pragma unroll
-  for (int x = 0; x < SASA_NXCD; ++x) {
-    ld[x] = 0;
-    cnt[x] = 0;
-  }
+  for (int x = 1; x < SASA_NXCD; ++x)
+    if (xl == x) wx = w.w[x];
+  int64_t ld = 0;
+  int cnt = 0;
   for (int r = 0; r < BH; ++r) {
-    const int hd = __builtin_amdgcn_readfirstlane(horder[r]);
-    const int64_t rc = rcost[r];
-    const int64_t c = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(rc >> 32)) << 32) |
-                                (uint32_t)__builtin_amdgcn_readfirstlane((int)rc));
-    int best = 0;
-    int64_t bnum = ld[0] + c, bw = w.w[0];
-#pragma unroll
-    for (int x = 1; x < SASA_NXCD; ++x) {  // (ld[x] + c) / w[x] < (ld[best] + c) / w[best]
-      const int64_t num = ld[x] + c;
-      if (num * bw < bnum * w.w[x]) {
-        best = x;
-        bnum = num;
-        bw = w.w[x];
+    const int hd = horder[r];
+    const int64_t c = rcost[r];
+    // earliest finish (ld + c) / w, ties to the lower XCD
+    int64_t a = ld + c, aw = wx;
+    int bx = xl;
+    auto take = [&](int64_t pa, int64_t pw, int px) {
+      const int64_t lhs = pa * aw, rhs = a * pw;  // pa / pw vs a / aw
+      if (lhs < rhs || (lhs == rhs && px < bx)) {
+        a = pa;
+        aw = pw;
+        bx = px;
       }
+    };
+    take(sasa_dpp<0xB1>(a), sasa_dpp<0xB1>(aw), sasa_dpp<0xB1>(bx));     // lane ^ 1
+    take(sasa_dpp<0x4E>(a), sasa_dpp<0x4E>(aw), sasa_dpp<0x4E>(bx));     // lane ^ 2
+    take(sasa_dpp<0x141>(a), sasa_dpp<0x141>(aw), sasa_dpp<0x141>(bx));  // 7 - lane, within 8
+    const int best = __builtin_amdgcn_readfirstlane(bx);
+    const int slot = __builtin_amdgcn_readlane(cnt, best);
+    if (lane == 0) {
+      slot_head[best * BH + slot] = hd;
+      head_xcd[hd] = best;
     }
-#pragma unroll
-    for (int x = 0; x < SASA_NXCD; ++x)
-      if (x == best) {
-        if (lane == 0) slot_head[x * BH + cnt[x]] = hd;
-        ld[x] += c;
-        ++cnt[x];
-      }
-    if (lane == 0) head_xcd[hd] = best;
+    if (xl == best) {
+      ld += c;
+      ++cnt;
+    }
   }
-  if (lane == 0) {
-#pragma unroll
-    for (int x = 0; x < SASA_NXCD; ++x) {
-      nh[x] = cnt[x];
-      load[x] = ld[x];
-    }
+  if (lane < SASA_NXCD) {
+    nh[lane] = cnt;
+    load[lane] = ld;
   }
 }
 
