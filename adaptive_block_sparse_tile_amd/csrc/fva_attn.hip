@@ -1121,18 +1121,27 @@ __global__ __launch_bounds__(COST_WAVES * 64) void cost_kernel(AttnParams p, con
 // (ties: lower XCD).  Writes each head's first position in the order array
 // and the queue segments qoff[0..NXCD].  NAIVE puts every head on queue 0 in
 // head order.  forced (nullable): each head's XCD, given by the caller
-// instead of chosen.  The assignment itself is one thread's sequential walk
-// (each choice depends on the loads before it); the ranking before it and the
-// positions after it are spread over the workgroup.
+// instead of chosen.  The assignment is sequential (each choice depends on
+// the loads before it) and runs on wavefront 0: lane x (mod 8) holds XCD x's
+// load and head count, and the least loaded XCD comes from three register
+// exchanges of the key load << 3 | x inside each group of 8 lanes; the
+// ranking before it and the positions after it are spread over the workgroup.
+template <int CTRL>
+__device__ inline uint64_t dpp_u64(uint64_t x) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)x, (int)(uint32_t)x, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp((int)(x >> 32), (int)(x >> 32), CTRL, 0xF, 0xF, false);
+  return ((uint64_t)hi << 32) | lo;
+}
 __global__ __launch_bounds__(256) void head_plan_kernel(const uint64_t* __restrict__ head_cost, int N, int BH,
                                                         bool lpt, const int32_t* __restrict__ forced,
                                                         int32_t* __restrict__ head_pos, int32_t* __restrict__ qoff) {
-  // [BH] head costs, then [BH] int32 head of each rank, then [BH] int32 place
-  // of each rank (XCD | slot among the XCD's heads << 3)
+  // [BH] head costs, [BH] costs in rank order, then [BH] int32 head of each
+  // rank, then [BH] int32 place of each rank (XCD | slot among the XCD's heads << 3)
   extern __shared__ uint64_t hsh[];
   __shared__ int32_t qoff_s[NXCD + 1];
   uint64_t* hcost = hsh;
-  int32_t* horder = (int32_t*)(hsh + BH);
+  uint64_t* rcost = hsh + BH;
+  int32_t* horder = (int32_t*)(hsh + 2 * BH);
   int32_t* place = horder + BH;
   for (int x = threadIdx.x; x < BH; x += blockDim.x) hcost[x] = lpt ? head_cost[x] : 0;
   __syncthreads();
@@ -1141,40 +1150,48 @@ __global__ __launch_bounds__(256) void head_plan_kernel(const uint64_t* __restri
     for (int y = 0; y < BH; ++y)
       if (hcost[y] > hcost[x] || (hcost[y] == hcost[x] && y < x)) ++r;
     horder[r] = x;
+    rcost[r] = hcost[x];
     place[r] = forced ? min(max(forced[x], 0), NXCD - 1) : 0;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    // per-XCD tallies in registers (every index is a constant after unrolling)
-    uint64_t load[NXCD];
-    int nh[NXCD];
-#pragma unroll
-    for (int x = 0; x < NXCD; ++x) load[x] = 0, nh[x] = 0;
-#pragma unroll 4
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x, xl = lane & (NXCD - 1);
+    uint64_t ld = 0;
+    int cnt = 0;
     for (int r = 0; r < BH; ++r) {
-      const uint64_t c = hcost[horder[r]];
-      int best = place[r];
+      const uint64_t c = rcost[r];
+      int best;
       if (!forced && lpt) {
-        uint64_t lb = load[0];
-        best = 0;
-#pragma unroll
-        for (int x = 1; x < NXCD; ++x)
-          if (load[x] < lb) best = x, lb = load[x];
+        uint64_t key = (ld << 3) | (uint64_t)xl;
+        uint64_t o = dpp_u64<0xB1>(key);  // lane ^ 1
+        key = o < key ? o : key;
+        o = dpp_u64<0x4E>(key);           // lane ^ 2
+        key = o < key ? o : key;
+        o = dpp_u64<0x141>(key);          // 7 - lane, within 8
+        key = o < key ? o : key;
+        best = __builtin_amdgcn_readfirstlane((int)(key & 7));
+      } else {
+        best = __builtin_amdgcn_readfirstlane(place[r]);
       }
-      int slot = 0;
-#pragma unroll
-      for (int x = 0; x < NXCD; ++x)
-        if (x == best) slot = nh[x], load[x] += c, nh[x]++;
-      place[r] = best | (slot << 3);
+      const int slot = __builtin_amdgcn_readlane(cnt, best);
+      if (lane == 0) place[r] = best | (slot << 3);
+      if (xl == best) {
+        ld += c;
+        ++cnt;
+      }
     }
-    int off = 0;
+    // queue segments: XCD x starts after the heads of XCDs 0 .. x-1
+    int off = cnt * N;  // inclusive prefix over lanes 0..7 of each group
 #pragma unroll
-    for (int x = 0; x < NXCD; ++x) {
-      qoff[x] = off;
-      qoff_s[x] = off;
-      off += nh[x] * N;
+    for (int d = 1; d < NXCD; d <<= 1) {
+      const int o = __shfl_up(off, d);
+      if (xl >= d) off += o;
     }
-    qoff[NXCD] = off;
+    if (lane < NXCD) {
+      qoff[lane] = off - cnt * N;
+      qoff_s[lane] = off - cnt * N;
+      if (lane == NXCD - 1) qoff[NXCD] = off;
+    }
   }
   __syncthreads();
   for (int r = threadIdx.x; r < BH; r += blockDim.x)
@@ -1349,7 +1366,7 @@ hipError_t launch_sparse_plan(const AttnLaunch& a, int sched, const int32_t* hea
   hipLaunchKernelGGL(cost_kernel, dim3((n_items + COST_WAVES - 1) / COST_WAVES), dim3(COST_WAVES * 64),
                      (size_t)a.g.N * sizeof(int32_t), st, prm, a.blk_cnt, a.keys, a.rank, a.qctr, a.head_cost,
                      a.plan_tag);
-  hipLaunchKernelGGL(head_plan_kernel, dim3(1), dim3(256), (size_t)BH * 16, st, a.head_cost, per_head, BH, lpt,
+  hipLaunchKernelGGL(head_plan_kernel, dim3(1), dim3(256), (size_t)BH * 24, st, a.head_cost, per_head, BH, lpt,
                      sched == 2 ? head_xcd : nullptr, a.head_pos, a.qoff);
   if (lpt)
     hipLaunchKernelGGL(rank_kernel, dim3((per_head + 255) / 256, (per_head + 2047) / 2048, BH), dim3(256), 0, st,
