@@ -382,10 +382,11 @@ __global__ __launch_bounds__(THREADS) void route_rows_kernel(const double* __res
 //        bisecting the key for the largest K with mass(key >= K) >= p,
 //   the kept set = the top `keep` blocks is found by bisecting the key for the
 //        largest K with count(key >= K) >= keep, ties taken in index order.
-// The bisections split the scores' values (not the key codes) and, once few
-// blocks are left inside the bracket, pass over those blocks only.  Every
-// sum is a per-lane sequential sum in a fixed order followed by a fixed tree
-// over lanes and wavefronts, so results do not depend on timing.
+// The bisections split the scores' values (not the key codes) and, once at
+// most one block per lane is left inside the bracket, wavefront 0 finishes
+// over those blocks alone.  Every sum is a per-lane sequential sum in a
+// fixed order followed by a fixed tree over lanes and wavefronts, so results
+// do not depend on timing.
 // ---------------------------------------------------------------------------
 __device__ inline uint64_t order_key(double d) {
   const uint64_t b = (uint64_t)__double_as_longlong(d);
@@ -396,8 +397,9 @@ __device__ inline double key_value(uint64_t k) {
   const uint64_t b = (k >> 63) ? (k & 0x7fffffffffffffffull) : ~k;
   return __longlong_as_double((long long)b);
 }
-// candidates per lane kept after a select bracket is compacted
-constexpr int kCand = 2;
+// candidates per lane of the workgroup kept after a select bracket is
+// compacted (wavefront 0 then holds all of them)
+constexpr int kCand = 1;
 // passes of a select search that split the scores' values
 constexpr int kValueSteps = 40;
 
@@ -425,6 +427,16 @@ __device__ inline uint64_t read_lane(uint64_t x, int l) {
 }
 __device__ inline double read_lane(double x, int l) {
   return __longlong_as_double((long long)read_lane((uint64_t)__double_as_longlong(x), l));
+}
+
+// a value every lane holds alike, moved to a scalar register, so that the
+// compiler treats branches on it as uniform
+__device__ inline uint32_t uniform(uint32_t x) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)x); }
+__device__ inline uint64_t uniform(uint64_t x) {
+  return (uint64_t)uniform((uint32_t)x) | ((uint64_t)uniform((uint32_t)(x >> 32)) << 32);
+}
+__device__ inline double uniform(double x) {
+  return __longlong_as_double((long long)uniform((uint64_t)__double_as_longlong(x)));
 }
 
 template <typename T, typename Op>
@@ -463,7 +475,7 @@ struct GroupRed {
     T r = from_bits<T>(buf[0]);
     for (int i = 1; i < nwaves; ++i) r = op(r, from_bits<T>(buf[i]));
     flip ^= 1;
-    return r;
+    return uniform(r);
   }
   // two reductions in one round (a and b of the same width)
   template <typename T, typename OpA, typename OpB>
@@ -481,8 +493,8 @@ struct GroupRed {
       ra = opa(ra, from_bits<T>(buf[w]));
       rb = opb(rb, from_bits<T>(buf[4 + w]));
     }
-    *a = ra;
-    *b = rb;
+    *a = uniform(ra);
+    *b = uniform(rb);
     flip ^= 1;
   }
   // a sum over the lanes (fixed order) and a count that is already uniform
@@ -503,8 +515,8 @@ struct GroupRed {
       c += (uint32_t)buf[4 + i];
     }
     flip ^= 1;
-    *total = c;
-    return r;
+    *total = uniform(c);
+    return uniform(r);
   }
   // a count that is already uniform in each wavefront, summed over wavefronts
   __device__ uint32_t reduce_count(uint32_t wave_count) {
@@ -514,7 +526,7 @@ struct GroupRed {
     uint32_t c = (uint32_t)buf[0];
     for (int i = 1; i < nwaves; ++i) c += (uint32_t)buf[i];
     flip ^= 1;
-    return c;
+    return uniform(c);
   }
   __device__ static uint64_t to_bits(double x) { return (uint64_t)__double_as_longlong(x); }
   __device__ static uint64_t to_bits(uint64_t x) { return x; }
@@ -529,7 +541,8 @@ struct GroupRed {
 // Three wavefronts per SIMD (at most 168 registers): the 32 keys and
 // probabilities per lane take 128, and the passes are bound by latency
 // (reductions and a barrier each), so the extra occupancy is worth the few
-// registers the compiler moves to scratch (long video 640 -> 525 us per slab).
+// registers the compiler moves to scratch outside the passes (long video
+// 640 -> 525 us per slab when the passes themselves still reloaded some).
 template <int E>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void route_select_kernel(const double* __restrict__ S, int N, int words, int t0,
                                                            int nIT, Heads hd, float top_p, int k_floor,
@@ -593,17 +606,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
   gr.reduce2(&kmin, &kmax, MinOp(), MaxOp());
 
   // Candidates of a search bracket [lo, hi) once it holds at most kCand per
-  // lane: copied out of the 32 per-lane registers into LDS (wavefronts in
-  // order, then register slot, then lane), then kCand per lane (entries tid,
-  // tid + threads, ...), padding with key 0 (below every finite score) and
-  // probability 0.
+  // lane: copied out of the per-lane registers into LDS (wavefronts in
+  // order, then register slot, then lane); wavefront 0 then takes kSlots per
+  // lane (entries lane, lane + 64, ...), padding with key 0 (below every
+  // finite score) and probability 0, and finishes the search alone.
+  constexpr int kSlots = kCand * (E == 32 ? 4 : 1);
   __shared__ uint64_t cand_key[kCand * 256];
   __shared__ double cand_pr[kCand * 256];
   __shared__ uint32_t wt[4];
+  __shared__ uint64_t res_key[2];  // wavefront 0's lo, hi
+  __shared__ double res_f64[2];    // its m_hi, tie probability
+  __shared__ uint32_t res_cnt[2];  // its c_lo, c_hi
   const int lane = tid & 63, wave = tid >> 6;
   const int threads = blockDim.x;
-  uint64_t ck[kCand];
-  double cp[kCand];
   // exclusive prefix over the workgroup of a per-lane count (lanes in order)
   auto exclusive_prefix = [&](uint32_t mine) -> uint32_t {
     uint32_t incl = mine;
@@ -619,7 +634,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
     for (int w = 0; w < wave; ++w) r += wt[w];
     return r;
   };
-  auto compact = [&](uint64_t lo, uint64_t hi, uint32_t total) {
+  auto compact = [&](uint64_t lo, uint64_t hi, bool with_mass) {
     // order: wavefronts in order, then slot e, then lanes; each wavefront's
     // offset comes from its count, a position from the lanes below it
     uint32_t mine = 0;  // uniform in the wavefront
@@ -638,79 +653,67 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
         const uint32_t pos = base + (uint32_t)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
                                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
         cand_key[pos] = key[e];
-        cand_pr[pos] = pr[e];
+        if (with_mass) cand_pr[pos] = pr[e];
       }
       base += (uint32_t)__popcll(bal);
     }
     __syncthreads();
-#pragma unroll
-    for (int r = 0; r < kCand; ++r) {
-      const uint32_t idx = (uint32_t)(tid + r * threads);
-      ck[r] = idx < total ? cand_key[idx] : 0ull;
-      cp[r] = idx < total ? cand_pr[idx] : 0.0;
-    }
-    __syncthreads();  // the arrays are rewritten by the next compaction
   };
-  // Mass (when with_mass) and count of the blocks with key >= K, over the
-  // registers or over the compacted candidates (then without the blocks at
-  // or above the bracket's top, which the caller adds).  A block past N has
-  // key 0 and never counts (every K searched is at least kmin).  A lane adds
-  // fma(sel, pr, m) with sel 1 or 0 (the same bits as adding the selected
-  // probability) into four partial sums by register slot mod 4, then (m0 +
-  // m1) + (m2 + m3); the lane counts and masses are then summed over lanes
-  // by fixed trees and over wavefronts in order.
-  auto mass_count_ge = [&](uint64_t K, bool compacted, bool with_mass, uint32_t* cnt) -> double {
+  // Mass (when with_mass) and count of the blocks with key >= K.  A block
+  // past N has key 0 and never counts (every K searched is at least kmin).
+  // A lane adds fma(sel, pr, m) with sel 1 or 0 (the same bits as adding the
+  // selected probability) into four partial sums by register slot mod 4,
+  // then (m0 + m1) + (m2 + m3); the masses are then summed over lanes by a
+  // fixed tree and over wavefronts in order.  The count is the wavefront's:
+  // the population of each comparison's lane mask, summed on the scalar unit.
+  auto mass_count_ge = [&](uint64_t K, bool with_mass, uint32_t* cnt) -> double {
     double m4[4] = {0.0, 0.0, 0.0, 0.0};
-    uint32_t c = 0;
-    if (!compacted) {
+    uint32_t wc = 0;  // uniform in the wavefront
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const bool ge = key[e] >= K;
-        if (with_mass) m4[e & 3] = fma(ge ? 1.0 : 0.0, pr[e], m4[e & 3]);
-        c += ge ? 1u : 0u;
-      }
-    } else {
-#pragma unroll
-      for (int r = 0; r < kCand; ++r) {
-        const bool ge = ck[r] >= K;
-        if (with_mass) m4[r & 3] = fma(ge ? 1.0 : 0.0, cp[r], m4[r & 3]);
-        c += ge ? 1u : 0u;
-      }
+    for (int e = 0; e < E; ++e) {
+      const bool ge = key[e] >= K;
+      if (with_mass) m4[e & 3] = fma(ge ? 1.0 : 0.0, pr[e], m4[e & 3]);
+      wc += (uint32_t)__popcll(__ballot(ge));
     }
-    const uint32_t wc = wave_reduce(c, AddOp());
     if (with_mass) return gr.reduce_sum_count((m4[0] + m4[1]) + (m4[2] + m4[3]), wc, cnt);
     *cnt = gr.reduce_count(wc);
     return 0.0;
   };
   // the only key in [lo, hi) (callers know there is exactly one)
-  auto only_key_in = [&](uint64_t lo, uint64_t hi, bool compacted) -> uint64_t {
+  auto only_key_in = [&](uint64_t lo, uint64_t hi) -> uint64_t {
     uint64_t k = 0;
-    if (!compacted) {
 #pragma unroll
-      for (int e = 0; e < E; ++e)
-        if (key[e] >= lo && key[e] < hi) k = key[e];
-    } else {
-#pragma unroll
-      for (int r = 0; r < kCand; ++r)
-        if (ck[r] >= lo && ck[r] < hi) k = ck[r];
-    }
+    for (int e = 0; e < E; ++e)
+      if (key[e] >= lo && key[e] < hi) k = key[e];
     return gr.reduce(k, MaxOp());
   };
-  // Bisection of the key range for the largest K with pred(K): pred holds at
-  // lo and fails at hi, with the counts of keys >= lo and >= hi (and, for the
-  // mass search, the mass at hi) at hand.  The pivot halves the scores
+  // the probability of the blocks with key K (every tied block has the same
+  // probability; any holder reports it)
+  auto tie_pr = [&](uint64_t K) -> double {
+    double t = 0.0;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (key[e] == K) t = pr[e];
+    return gr.reduce(t, MaxOp());
+  };
+  // Bisection of the key range for the largest K with pred(K): pred holds
+  // at lo and fails at hi, with the counts of keys >= lo and >= hi (and, for
+  // the mass search, the mass at hi) at hand.  The pivot halves the scores
   // between the bracket's ends (keys that order doubles leave long runs of
-  // unused codes between the exponents of the scores present); it falls back
-  // to the middle key when that is not strictly inside.  Once the bracket
-  // holds at most kCand blocks per lane they are compacted and later passes
-  // touch only them.  Once a single key lies in [lo, hi), that key is the
-  // answer and the search stops (otherwise it runs until hi = lo + 1).  At
-  // the end no key lies in (lo, hi), so "keys > lo" are exactly "keys >= hi".
+  // unused codes between the exponents of the scores present) for the first
+  // kValueSteps passes (two distinct scores close to zero could take a
+  // thousand value halvings to part), then the key codes, which end within
+  // 64 more; it falls back to the middle key when the value midpoint is not
+  // strictly inside.  Passes go over all blocks until the bracket holds at
+  // most kCand blocks per lane; those are compacted and wavefront 0
+  // finishes alone over them (no workgroup barrier per pass), adding what
+  // lies at or above the bracket's top.  Once a single key lies in [lo, hi),
+  // that key is the answer and the search stops (otherwise it runs until
+  // hi = lo + 1).  At the end lo is a key present, no key lies in (lo, hi),
+  // so "keys > lo" are exactly "keys >= hi", and for the mass search *ptie
+  // is the probability of key lo.
   auto search = [&](bool with_mass, double target, uint64_t& lo, uint64_t& hi, uint32_t& c_lo, uint32_t& c_hi,
-                    double& m_hi) {
-    // the value midpoint for the first kValueSteps passes (two distinct
-    // scores close to zero could take a thousand value halvings to part),
-    // then the key midpoint, which ends within 64 more
+                    double& m_hi, double* ptie) {
     int steps = 0;
     auto pivot = [&]() -> uint64_t {
       if (steps++ < kValueSteps) {
@@ -734,33 +737,81 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
     while (hi - lo > 1 && c_lo - c_hi > (uint32_t)(kCand * threads)) {
       const uint64_t mid = pivot();
       uint32_t c_mid;
-      const double m = mass_count_ge(mid, false, with_mass, &c_mid);
+      const double m = mass_count_ge(mid, with_mass, &c_mid);
       step(mid, m, c_mid);
     }
-    if (hi - lo <= 1) return;
-    if (c_lo - c_hi == 1) {
-      lo = only_key_in(lo, hi, false);
+    lo = uniform(lo);
+    hi = uniform(hi);
+    c_lo = uniform(c_lo);
+    c_hi = uniform(c_hi);
+    if (hi - lo <= 1 || c_lo - c_hi == 1) {
+      if (hi - lo > 1) lo = only_key_in(lo, hi);
+      if (with_mass) *ptie = tie_pr(lo);
       return;
     }
-    // then over the compacted candidates, adding what lies at or above the top
-    compact(lo, hi, c_lo - c_hi);
-    const double m_above = m_hi;
-    const uint32_t c_above = c_hi;
-    while (hi - lo > 1) {
-      if (c_lo - c_hi == 1) {
-        lo = only_key_in(lo, hi, true);
-        return;
+    // then wavefront 0 over the compacted candidates, kSlots per lane; sums
+    // over its lanes by the fixed tree of wave_reduce
+    compact(lo, hi, with_mass);
+    if (wave == 0) {
+      const uint32_t n_cand = c_lo - c_hi;
+      uint64_t ck[kSlots];
+      double cp[kSlots];
+#pragma unroll
+      for (int r = 0; r < kSlots; ++r) {
+        const uint32_t idx = (uint32_t)(lane + 64 * r);
+        ck[r] = idx < n_cand ? cand_key[idx] : 0ull;
+        cp[r] = with_mass && idx < n_cand ? cand_pr[idx] : 0.0;
       }
-      const uint64_t mid = pivot();
-      uint32_t c_mid;
-      const double m = m_above + mass_count_ge(mid, true, with_mass, &c_mid);
-      step(mid, m, c_mid + c_above);
+      const double m_above = m_hi;
+      const uint32_t c_above = c_hi;
+      while (hi - lo > 1 && c_lo - c_hi > 1) {
+        const uint64_t mid = pivot();
+        double acc = 0.0;
+        uint32_t c = 0;  // uniform in the wavefront
+#pragma unroll
+        for (int r = 0; r < kSlots; ++r) {
+          const bool ge = ck[r] >= mid;
+          if (with_mass) acc = fma(ge ? 1.0 : 0.0, cp[r], acc);
+          c += (uint32_t)__popcll(__ballot(ge));
+        }
+        step(mid, with_mass ? m_above + wave_reduce(acc, AddOp()) : 0.0, c_above + c);
+      }
+      if (hi - lo > 1) {  // the only candidate in [lo, hi)
+        uint64_t k = 0;
+#pragma unroll
+        for (int r = 0; r < kSlots; ++r)
+          if (ck[r] >= lo && ck[r] < hi) k = ck[r];
+        lo = wave_reduce(k, MaxOp());
+      }
+      double t = 0.0;
+      if (with_mass) {
+#pragma unroll
+        for (int r = 0; r < kSlots; ++r)
+          if (ck[r] == lo) t = cp[r];
+        t = wave_reduce(t, MaxOp());
+      }
+      if (lane == 0) {
+        res_key[0] = lo;
+        res_key[1] = hi;
+        res_f64[0] = m_hi;
+        res_f64[1] = t;
+        res_cnt[0] = c_lo;
+        res_cnt[1] = c_hi;
+      }
     }
+    __syncthreads();
+    lo = uniform(res_key[0]);
+    hi = uniform(res_key[1]);
+    m_hi = uniform(res_f64[0]);
+    c_lo = uniform(res_cnt[0]);
+    c_hi = uniform(res_cnt[1]);
+    if (with_mass) *ptie = uniform(res_f64[1]);
+    __syncthreads();  // the results and candidates are rewritten by the next search
   };
 
   const double p = (double)top_p;
   uint32_t n_real = 0;
-  const double total = mass_count_ge(kmin, false, true, &n_real);
+  const double total = mass_count_ge(kmin, true, &n_real);
   int nstar;
   uint64_t cut = 0;        // crossing key of the Top-p search
   uint32_t cut_above = 0;  // blocks with key > cut
@@ -776,26 +827,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
     // largest K with mass(key >= K) >= p: the key of the crossing block
     uint64_t lo = kmin, hi = kmax;
     uint32_t c_lo = n_real, c_hi = 0;
-    double m_hi = mass_count_ge(hi, false, true, &c_hi);
-    double above;
+    double m_hi = mass_count_ge(hi, true, &c_hi);
+    double above, ptie;
     uint32_t n_above;
     if (m_hi >= p) {
       lo = hi;
       c_lo = c_hi;
       above = 0.0;  // nothing above the largest key
       n_above = 0;
+      ptie = tie_pr(lo);
     } else {
-      search(true, p, lo, hi, c_lo, c_hi, m_hi);
+      search(true, p, lo, hi, c_lo, c_hi, m_hi, &ptie);
       above = m_hi;
       n_above = c_hi;
     }
     // blocks above the crossing key, then as many tied blocks as needed
-    double ptie = 0.0;
-#pragma unroll
-    for (int e = 0; e < E; ++e)
-      if (key[e] == lo) ptie = pr[e];
-    // every tied block has the same probability; any holder reports it
-    ptie = gr.reduce(ptie, MaxOp());
     int need = 1;
     double c = above + ptie;
     const int n_tie = (int)(c_lo - n_above);
@@ -832,7 +878,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
         hi = cut;
         c_hi = cut_at;
       } else {
-        mass_count_ge(hi, false, false, &c_hi);
+        mass_count_ge(hi, false, &c_hi);
         if (c_hi >= (uint32_t)keep) {
           lo = hi;
           n_above = 0;
@@ -840,7 +886,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
         }
       }
       if (!done) {
-        search(false, (double)keep, lo, hi, c_lo, c_hi, m_unused);
+        search(false, (double)keep, lo, hi, c_lo, c_hi, m_unused, nullptr);
         n_above = c_hi;
       }
     }
