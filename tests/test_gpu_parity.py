@@ -577,6 +577,26 @@ def test_select_exact_scores_far_below_the_range(top_p, k_floor, block):
     assert np.array_equal(mg, mo)
 
 
+@pytest.mark.parametrize("wl", [
+    # 2100 blocks: 66 mask words, two wavefronts, the second holding 2 lanes of blocks
+    _custom("select_n2100", 1, 64, (14, 20, 60), (2, 2, 2), 0.8, 5),
+    # 3200 blocks: two wavefronts, the second holding 36 lanes of blocks
+    _custom("select_n3200", 2, 64, (16, 40, 40), (2, 2, 2), 0.9, 4),
+    _custom("select_n3200_topk", 1, 64, (16, 40, 40), (2, 2, 2), 0.0, 40),
+    # 4160 blocks: three wavefronts, the third holding 2 lanes of blocks
+    _custom("select_n4160", 1, 128, (16, 40, 52), (2, 2, 2), 0.85, 8),
+], ids=lambda w: w.name)
+def test_route_select_partial_wavefronts(wl):
+    """The selection router on two and three wavefronts per row with the last
+    wavefront partly empty (lanes past the mask words hold no blocks), at the
+    Top-p and fixed top-k settings: masks and counts against the oracle."""
+    N = oracle.num_blocks(wl.grid, wl.block)
+    words = (N + 31) // 32
+    assert 64 < words and words % 64 != 0
+    (q, k, v), (qd, kd, vd) = _inputs(wl)
+    _check_route(wl, q, k, qd, kd)
+
+
 @pytest.mark.parametrize("name", ["tiny", "wan14b", "long"])
 def test_plan_exec_equals_sparse_attn(name):
     """fva_attn_plan + fva_attn_exec is fva_sparse_attn split in two: bitwise equal O."""
