@@ -440,7 +440,9 @@ def dense_attn_ref(q, k, v, scale=None, out=None, ws=None, stream=None):
 
 def xcd_speed(trace_host: np.ndarray, xcd_load) -> np.ndarray:
     """Relative XCD speeds (per mille) from a host copy of a per-XCD-schedule
-    trace and the cost sasa() placed on each XCD (fva_trace_xcd_speed)."""
+    trace and the cost sasa() placed on each XCD (fva_trace_xcd_speed).  The
+    traces of several launches may be stacked (any leading shape): their item
+    times add up per XCD."""
     t = np.ascontiguousarray(trace_host).view(np.uint64).reshape(-1)
     ld = np.ascontiguousarray(np.asarray(xcd_load)[:8], dtype=np.int64)
     out = np.zeros(8, dtype=np.int32)

@@ -333,6 +333,9 @@ fva_status fva_sasa(const fva_desc* desc, const fva_grid* grid, const uint32_t* 
  * placed as fva_sasa placed the heads) and the cost fva_sasa assigned each
  * XCD (xcd_load[0..7]): speed_x = xcd_load[x] / (summed item time of the
  * workgroups on XCD x), weight_x = round(1000 * speed_x / mean speed).
+ * The traces of several launches of one plan may be passed back to back
+ * (n_wg = launches * workgroups): their item times add up per XCD, which
+ * averages out launch-to-launch variation.
  * Returns INVALID_ARG for null pointers, n_wg < 1 or an XCD with no work. */
 fva_status fva_trace_xcd_speed(const uint64_t* host_trace, int32_t n_wg, const int64_t* xcd_load,
                                int32_t* xcd_weight);
