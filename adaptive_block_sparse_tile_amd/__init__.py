@@ -66,7 +66,7 @@ _P = ctypes.c_void_p
 
 
 def load():
-    """Load libfva.so (built in-tree by __graft_entry__.build() or build.py)."""
+    """Load libfva.so (built in-tree by build.py)."""
     global _lib
     if _lib is not None:
         return _lib
