@@ -49,6 +49,9 @@ def main():
                          "against the eager loop)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only copy 2 GiB device-to-device three times (reference for rocprofv3 FETCH/WRITE_SIZE)")
+    ap.add_argument("--calibrate-gemm", action="store_true",
+                    help="only time torch's bf16 GEMM (n = 8192 and 16384), a reference for what the bf16 MFMA "
+                         "peak yields to a library kernel on this part")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -66,6 +69,25 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes_per_launch": n}))
+        return
+    if args.calibrate_gemm:
+        for n, reps in ((8192, 20), (16384, 5)):
+            a = torch.randn(n, n, dtype=torch.bfloat16, device="cuda")
+            b = torch.randn(n, n, dtype=torch.bfloat16, device="cuda")
+            for _ in range(3):
+                c = a @ b
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                c = a @ b
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+            print(json.dumps({"calibrate_gemm_n": n, "dtype": "bf16", "ms": round(ms, 3), "tflops": round(tf, 1),
+                              "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 3)}), flush=True)
+            del a, b, c
         return
 
     import adaptive_block_sparse_tile_amd as fva
