@@ -168,40 +168,54 @@ __global__ __launch_bounds__(1024) void sasa_lpt_kernel(const int64_t* __restric
   // The assignment on wavefront 0: lane x (mod 8) holds XCD x's load, head
   // count and weight; the XCD of the earliest finish comes from three
   // register exchanges inside each group of 8 lanes (lane i with i ^ 1, then
-  // i ^ 2, then 7 - i), every group computing the same thing.
+  // i ^ 2, then 7 - i), every group computing the same thing.  The ranked
+  // heads and costs are read 64 at a time into the lanes and taken from
+  // there one by one.  Loads stay below 2^43 and weights below 2^20 (the
+  // host's limits), so load x weight is exact in 64 bits.
   const int xl = lane & (SASA_NXCD - 1);
-  int64_t wx = w.w[0];
+  uint32_t wx = (uint32_t)w.w[0];
 #pragma unroll
   for (int x = 1; x < SASA_NXCD; ++x)
-    if (xl == x) wx = w.w[x];
+    if (xl == x) wx = (uint32_t)w.w[x];
+  auto mul = [](uint64_t a, uint32_t b) -> uint64_t {  // a < 2^43, b < 2^20
+    return (uint64_t)(uint32_t)a * b + ((uint64_t)((uint32_t)(a >> 32) * b) << 32);
+  };
   int64_t ld = 0;
   int cnt = 0;
-  for (int r = 0; r < BH; ++r) {
-    const int hd = horder[r];
-    const int64_t c = rcost[r];
-    // earliest finish (ld + c) / w, ties to the lower XCD
-    int64_t a = ld + c, aw = wx;
-    int bx = xl;
-    auto take = [&](int64_t pa, int64_t pw, int px) {
-      const int64_t lhs = pa * aw, rhs = a * pw;  // pa / pw vs a / aw
-      if (lhs < rhs || (lhs == rhs && px < bx)) {
-        a = pa;
-        aw = pw;
-        bx = px;
+  for (int r0 = 0; r0 < BH; r0 += 64) {
+    const int rr = r0 + lane;
+    const int my_hd = rr < BH ? horder[rr] : 0;
+    const int64_t my_c = rr < BH ? rcost[rr] : 0;
+    const int n = min(64, BH - r0);
+    for (int i = 0; i < n; ++i) {
+      const int hd = __builtin_amdgcn_readlane(my_hd, i);
+      const int64_t c = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(my_c >> 32), i) << 32) |
+                                  (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)my_c, i));
+      // earliest finish (ld + c) / w, ties to the lower XCD
+      int64_t a = ld + c;
+      uint32_t aw = wx;
+      int bx = xl;
+      auto take = [&](int64_t pa, uint32_t pw, int px) {
+        const uint64_t lhs = mul((uint64_t)pa, aw), rhs = mul((uint64_t)a, pw);  // pa / pw vs a / aw
+        if (lhs < rhs || (lhs == rhs && px < bx)) {
+          a = pa;
+          aw = pw;
+          bx = px;
+        }
+      };
+      take(sasa_dpp<0xB1>(a), (uint32_t)sasa_dpp<0xB1>((int)aw), sasa_dpp<0xB1>(bx));     // lane ^ 1
+      take(sasa_dpp<0x4E>(a), (uint32_t)sasa_dpp<0x4E>((int)aw), sasa_dpp<0x4E>(bx));     // lane ^ 2
+      take(sasa_dpp<0x141>(a), (uint32_t)sasa_dpp<0x141>((int)aw), sasa_dpp<0x141>(bx));  // 7 - lane, within 8
+      const int best = __builtin_amdgcn_readfirstlane(bx);
+      const int slot = __builtin_amdgcn_readlane(cnt, best);
+      if (lane == 0) {
+        slot_head[best * BH + slot] = hd;
+        head_xcd[hd] = best;
       }
-    };
-    take(sasa_dpp<0xB1>(a), sasa_dpp<0xB1>(aw), sasa_dpp<0xB1>(bx));     // lane ^ 1
-    take(sasa_dpp<0x4E>(a), sasa_dpp<0x4E>(aw), sasa_dpp<0x4E>(bx));     // lane ^ 2
-    take(sasa_dpp<0x141>(a), sasa_dpp<0x141>(aw), sasa_dpp<0x141>(bx));  // 7 - lane, within 8
-    const int best = __builtin_amdgcn_readfirstlane(bx);
-    const int slot = __builtin_amdgcn_readlane(cnt, best);
-    if (lane == 0) {
-      slot_head[best * BH + slot] = hd;
-      head_xcd[hd] = best;
-    }
-    if (xl == best) {
-      ld += c;
-      ++cnt;
+      if (xl == best) {
+        ld += c;
+        ++cnt;
+      }
     }
   }
   if (lane < SASA_NXCD) {
