@@ -553,10 +553,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
   const int nwaves = blockDim.x >> 6;
   GroupRed gr{red_slot, nwaves, 0};
   const int tid = threadIdx.x;
-  const SlabRow sr = slab_row(blockIdx.x, t0, nIT, N, hd);
+  // rows in reverse slab order: the scores kernel wrote the last rows last,
+  // so the first rows read here are the ones still in the memory-side cache
+  const int64_t slab_r = (int64_t)gridDim.x - 1 - blockIdx.x;
+  const SlabRow sr = slab_row(slab_r, t0, nIT, N, hd);
   if (sr.i >= N) return;  // padding row of a head's last tile (uniform over the workgroup)
   const int64_t row = sr.out;
-  const double* s = S + (int64_t)blockIdx.x * N;
+  const double* s = S + slab_r * N;
   const int j0 = tid * E;
 
   double pr[E];
