@@ -174,8 +174,8 @@ def test_route_parity(name):
 
 # (workload, random items per head, heads checked in full, more heads in full); None: every item
 ATTN_COVERAGE = [("tiny", None), ("wan5b", None), ("wan14b", None),
-                 ("720p", (8, 3, (36,))),      # plus every item of global head 36 (near-dense)
-                 ("long", (64, 1, ()))]
+                 ("720p", (12, 3, (36, 39))),  # plus every item of global heads 36 and 39 (near-dense)
+                 ("long", (96, 1, ()))]
 
 
 @pytest.mark.parametrize("name,cover", ATTN_COVERAGE, ids=[c[0] for c in ATTN_COVERAGE])
