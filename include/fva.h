@@ -24,7 +24,9 @@
  *     ((b*L + l)*heads + h)*D + d.  Token l = (t*H + y)*W + x.
  *   - Every tensor, mask and workspace pointer is a DEVICE pointer owned by
  *     the caller.  The library never allocates, frees or caches device memory
- *     and keeps no state between calls.
+ *     at run time and keeps no state between calls; the one exception is the
+ *     static per-GPU scratch array of fva_route_noalloc, part of the loaded
+ *     module, whose contents the last such call leaves behind.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Calls enqueue their kernels on it and return without synchronising.
  *   - Arguments are validated on the host before anything is enqueued; on a
