@@ -597,6 +597,35 @@ def test_route_select_partial_wavefronts(wl):
     _check_route(wl, q, k, qd, kd)
 
 
+@pytest.mark.parametrize("grid,block", [((12, 16, 24), (2, 4, 4)), ((12, 16, 24), (2, 2, 4)),
+                                        ((12, 16, 24), (2, 2, 2)), ((16, 40, 40), (2, 2, 2))],
+                         ids=["n144", "n288", "n576", "n3200"])
+@pytest.mark.parametrize("top_p,k_floor", [(0.3141, 3), (0.0013, 7), (0.0, None)])
+def test_route_identical_keys_keep_lowest_indices(grid, block, top_p, k_floor):
+    """Every key token the same bf16 vector: all key blocks pool to it, every
+    score of a row ties, P = 1/N, and each router kernel (the row sort for
+    N = 144, the selection on one wavefront for 288, on one and two
+    wavefronts of 32 blocks per lane for 576 and 3200) must keep the
+    max(k_floor, ceil(p N)) lowest block indices (k_floor with Top-p off), as
+    the oracle does; p N is at least 0.16 from an integer, so no row is near a
+    step of the cumulative mass."""
+    N = oracle.num_blocks(grid, block)
+    if k_floor is None:
+        k_floor = N // 3 + 1
+    wl = _custom("identical_keys", 2, 64, grid, block, top_p, k_floor)
+    L = int(np.prod(grid))
+    rng = np.random.default_rng(11)
+    q = fvgen.f64_to_bf16(rng.normal(scale=2.0, size=(1, L, 2, 64)))
+    k = np.ascontiguousarray(np.broadcast_to(fvgen.f64_to_bf16(rng.normal(size=64)), (1, L, 2, 64)))
+    (mg, cg, sg), (mo, co, flags, so) = _route_both(wl, q, k, _dev(q), _dev(k))
+    expect = max(k_floor, math.ceil(float(np.float32(top_p)) * N)) if top_p > 0 else k_floor
+    assert sg == so == 0 and (flags == 0).all()
+    assert (co == expect).all()
+    assert np.array_equal(cg, co) and np.array_equal(mg, mo)
+    kept = oracle.mask_to_bool(mg, N).reshape(-1, N)
+    assert kept[:, :expect].all() and not kept[:, expect:].any()
+
+
 @pytest.mark.parametrize("name", ["tiny", "wan14b", "long"])
 def test_plan_exec_equals_sparse_attn(name):
     """fva_attn_plan + fva_attn_exec is fva_sparse_attn split in two: bitwise equal O."""
