@@ -334,14 +334,16 @@ def test_nonfinite_rows_repaired_dense():
 
 
 
-@pytest.mark.parametrize("block,n_expect", [((2, 2, 2), 576), ((2, 2, 4), 288)])
-def test_select_router_nonfinite_and_all_kept(block, n_expect):
-    # N = 576 (32 blocks per lane) and N = 288 (one wavefront, 8 blocks per
-    # lane): the selection router.  A NaN in one query token of head 1
-    # makes that query block's row non-finite; a +inf in one key token of
-    # head 0 makes every row of head 0 non-finite.  Both are repaired to all
-    # blocks with status bit 0 set; top_p = 1 keeps every block of every row.
-    wl = _custom("select_nonfinite", 2, 64, (12, 16, 24), block, 0.7, 3)
+@pytest.mark.parametrize("grid,block,n_expect", [((12, 16, 24), (2, 2, 2), 576), ((12, 16, 24), (2, 2, 4), 288),
+                                                  ((16, 40, 40), (2, 2, 2), 3200)])
+def test_select_router_nonfinite_and_all_kept(grid, block, n_expect):
+    # N = 576 (32 blocks per lane, one wavefront), N = 288 (one wavefront, 8
+    # blocks per lane) and N = 3200 (32 per lane, two wavefronts): the
+    # selection router.  A NaN in one query token of head 1 makes that query
+    # block's row non-finite; a +inf in one key token of head 0 makes every
+    # row of head 0 non-finite.  Both are repaired to all blocks with status
+    # bit 0 set; top_p = 1 keeps every block of every row.
+    wl = _custom("select_nonfinite", 2, 64, grid, block, 0.7, 3)
     N = oracle.num_blocks(wl.grid, wl.block)
     assert N == n_expect
     q0, k0, _ = fvgen.generate_qkv(wl)
