@@ -121,7 +121,10 @@ __global__ __launch_bounds__(256) void pool_kernel(const bf16_bits* __restrict__
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 typedef double f64x2 __attribute__((ext_vector_type(2)));
 
-__global__ __launch_bounds__(256) void scores_kernel(const double* __restrict__ qbar, const double* __restrict__ kbar,
+// Four wavefronts per SIMD: 112 registers hold a wavefront's accumulators,
+// operands and next-slice loads without spilling, and four 33.8 KB staging
+// buffers fit a CU's LDS (long-video route 2.39 -> 2.33 ms against three).
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) void scores_kernel(const double* __restrict__ qbar, const double* __restrict__ kbar,
                                                      int N, int D, int t0, int nIT, double* __restrict__ S) {
   __shared__ double As[64][33];
   __shared__ double Bs[64][33];
